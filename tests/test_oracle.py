@@ -1,0 +1,379 @@
+"""Pins for the fp64 oracle: closed forms, the pages' printed examples,
+invariants, a library special case and brute force on tiny inputs.
+
+Each test checks the oracle against something other than itself, chosen so
+that a plausible slip (a dropped term, a wrong sign, a transposed operand, an
+off-by-one causal boundary, a wrong GQA head map) fails at least one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import cascade_ref as ref
+
+
+def _paged_single(keys, values, page_size, perm_seed=0, extra_pages=3):
+    """Scatter one request's [L, Hkv, d] K/V into a shuffled paged cache."""
+    L, hkv, d = keys.shape
+    n_pages = -(-L // page_size)
+    total = n_pages + extra_pages
+    rng = np.random.default_rng(perm_seed)
+    ids = rng.permutation(total)[:n_pages]
+    kc = np.full((total, page_size, hkv, d), np.nan)
+    vc = np.full((total, page_size, hkv, d), np.nan)
+    for t in range(L):
+        kc[ids[t // page_size], t % page_size] = keys[t]
+        vc[ids[t // page_size], t % page_size] = values[t]
+    bt = np.concatenate([ids, rng.integers(0, total, 2)])[None, :]
+    return kc, vc, bt
+
+
+# ----------------------------------------------------------------- closed forms
+
+def test_hand_softmax():
+    # d=1, scale=1, q=1, k=(0, ln2, ln3): weights 1/6, 2/6, 3/6.
+    # v=(6, 12, 18) -> o = (6 + 24 + 54) / 6 = 14, lse = ln(1 + 2 + 3) = ln 6.
+    q = np.array([[1.0]])
+    k = np.array([[0.0], [math.log(2.0)], [math.log(3.0)]])
+    v = np.array([[6.0], [12.0], [18.0]])
+    o, lse = oracle.attend(q, k, v, 1.0)
+    assert abs(o[0, 0] - 14.0) < 1e-12
+    assert abs(lse[0] - math.log(6.0)) < 1e-12
+
+
+def test_hand_softmax_through_paged_path():
+    # Same numbers through block tables, shuffled pages and the causal rule:
+    # one request, seq_len 3, one query at position 2 sees all three keys.
+    keys = np.array([[0.0], [math.log(2.0)], [math.log(3.0)]])[:, None, :]
+    vals = np.array([[6.0], [12.0], [18.0]])[:, None, :]
+    kc, vc, bt = _paged_single(keys, vals, page_size=2)
+    q = np.ones((1, 1, 1))
+    out, lse = oracle.attention_full(q, kc, vc, bt, [0, 1], [3], 2, scale=1.0)
+    assert abs(out[0, 0, 0] - 14.0) < 1e-12
+    assert abs(lse[0, 0] - math.log(6.0)) < 1e-12
+
+
+def test_causal_boundary():
+    # num_computed = 0, three queries: query i sees keys 0..i only.
+    rng = np.random.default_rng(1)
+    L, d = 3, 4
+    keys = rng.standard_normal((L, 1, d))
+    vals = rng.standard_normal((L, 1, d))
+    q = rng.standard_normal((L, 1, d))
+    kc, vc, bt = _paged_single(keys, vals, page_size=2)
+    scale = 0.7
+    out, lse = oracle.attention_full(q, kc, vc, bt, [0, L], [L], 2, scale=scale)
+    # query 0: exactly one visible key
+    assert np.allclose(out[0, 0], vals[0, 0], atol=1e-14, rtol=0)
+    assert abs(lse[0, 0] - scale * float(q[0, 0] @ keys[0, 0])) < 1e-13
+    # query 1: two keys, written out by hand
+    s = np.array([scale * q[1, 0] @ keys[t, 0] for t in range(2)])
+    w = np.exp(s - s.max())
+    exp_o = (w[0] * vals[0, 0] + w[1] * vals[1, 0]) / w.sum()
+    assert np.allclose(out[1, 0], exp_o, atol=1e-13, rtol=0)
+    assert abs(lse[1, 0] - (s.max() + math.log(w.sum()))) < 1e-13
+
+
+def test_constant_values_give_that_value():
+    rng = np.random.default_rng(2)
+    L, hkv, d = 37, 2, 8
+    keys = rng.standard_normal((L, hkv, d)) * 3
+    vals = np.broadcast_to(rng.standard_normal((1, hkv, d)), (L, hkv, d)).copy()
+    kc, vc, bt = _paged_single(keys, vals, page_size=16)
+    q = rng.standard_normal((5, 4, d))
+    out, _ = oracle.attention_full(q, kc, vc, bt, [0, 5], [L], 16)
+    for h in range(4):
+        assert np.allclose(out[:, h], vals[0, h // 2][None, :], atol=1e-13, rtol=0)
+
+
+def test_zero_query_is_mean_of_visible_values():
+    rng = np.random.default_rng(3)
+    L, d = 21, 8
+    keys = rng.standard_normal((L, 1, d))
+    vals = rng.standard_normal((L, 1, d))
+    kc, vc, bt = _paged_single(keys, vals, page_size=4)
+    qn = 4
+    q = np.zeros((qn, 1, d))
+    out, lse = oracle.attention_full(q, kc, vc, bt, [0, qn], [L], 4)
+    for i in range(qn):
+        pos = L - qn + i
+        assert np.allclose(out[i, 0], vals[:pos + 1, 0].mean(axis=0), atol=1e-13, rtol=0)
+        assert abs(lse[i, 0] - math.log(pos + 1)) < 1e-13
+
+
+def test_gqa_head_mapping():
+    # Hq=4, Hkv=2: heads 0,1 read KV head 0 and heads 2,3 read KV head 1.
+    # KV head 0 has constant V = +1, KV head 1 has constant V = -1.
+    rng = np.random.default_rng(4)
+    L, d = 9, 4
+    keys = rng.standard_normal((L, 2, d))
+    vals = np.zeros((L, 2, d))
+    vals[:, 0] = 1.0
+    vals[:, 1] = -1.0
+    kc, vc, bt = _paged_single(keys, vals, page_size=4)
+    q = rng.standard_normal((1, 4, d))
+    out, _ = oracle.attention_full(q, kc, vc, bt, [0, 1], [L], 4)
+    assert np.allclose(out[0, 0:2], 1.0) and np.allclose(out[0, 2:4], -1.0)
+
+
+# ------------------------------------------------------------ library routine
+
+def _dense_kv(batch, r):
+    """Independent gather of a request's dense K/V [L, Hkv, d] (page loop)."""
+    ps = batch.workload.page_size
+    L = int(batch.seq_lens[r])
+    k = torch.empty(L, batch.k_cache.shape[2], batch.k_cache.shape[3], dtype=torch.float64)
+    v = torch.empty_like(k)
+    for p in range(-(-L // ps)):
+        page = int(batch.block_table[r, p])
+        n = min(ps, L - p * ps)
+        k[p * ps:p * ps + n] = batch.k_cache[page, :n].to(torch.float64)
+        v[p * ps:p * ps + n] = batch.v_cache[page, :n].to(torch.float64)
+    return k, v
+
+
+def _small_batch(seed=7, n=5, prefix=40, suffix=(3, 30), q=(1, 6), hq=4, hkv=2, d=16, ps=8):
+    w = workloads.Workload("small", n, prefix, suffix, q, hq, hkv, d, page_size=ps, seed=seed)
+    return workloads.make_batch(w)
+
+
+@pytest.mark.parametrize("seed", [7, 8])
+def test_matches_torch_sdpa_fp64(seed):
+    b = _small_batch(seed)
+    w = b.workload
+    G = w.num_q_heads // w.num_kv_heads
+    out, lse = oracle.attention_full(
+        b.q.float().numpy(), b.k_cache.float().numpy(), b.v_cache.float().numpy(),
+        b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy(), w.page_size)
+    for r in range(w.num_reqs):
+        q0, q1 = int(b.query_start_loc[r]), int(b.query_start_loc[r + 1])
+        k, v = _dense_kv(b, r)
+        L = k.shape[0]
+        qq = b.q[q0:q1].to(torch.float64).transpose(0, 1)          # [Hq, q, d]
+        kk = k.repeat_interleave(G, dim=1).transpose(0, 1)          # [Hq, L, d]
+        vv = v.repeat_interleave(G, dim=1).transpose(0, 1)
+        ql = q1 - q0
+        mask = torch.ones(ql, L, dtype=torch.bool).tril(diagonal=L - ql)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk, vv, attn_mask=mask, scale=w.softmax_scale)
+        s = (qq @ kk.transpose(1, 2)) * w.softmax_scale
+        l = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)
+        assert np.abs(out[q0:q1] - o.transpose(0, 1).numpy()).max() < 1e-12
+        assert np.abs(lse[q0:q1] - l.transpose(0, 1).numpy()).max() < 1e-12
+
+
+# ------------------------------------------------------------------- merging
+
+@pytest.mark.parametrize("parts", [2, 3, 5])
+def test_merge_of_partition_equals_union(parts):
+    rng = np.random.default_rng(10 + parts)
+    m, n, d = 6, 50, 8
+    q = rng.standard_normal((m, d)) * 2
+    k = rng.standard_normal((n, d)) * 2
+    v = rng.standard_normal((n, d))
+    o_all, l_all = oracle.attend(q, k, v, 0.5)
+    label = rng.integers(0, parts, n)
+    label[:parts] = np.arange(parts)                       # no part empty
+    outs, lses = [], []
+    for p in range(parts):
+        sel = label == p
+        o_p, l_p = oracle.attend(q, k[sel], v[sel], 0.5)
+        outs.append(o_p)
+        lses.append(l_p)
+    o_m, l_m = oracle.merge_states(outs, lses)
+    assert np.abs(o_m - o_all).max() < 1e-12
+    assert np.abs(l_m - l_all).max() < 1e-12
+
+
+def test_merge_with_empty_partial_and_all_empty():
+    rng = np.random.default_rng(20)
+    q = rng.standard_normal((3, 4))
+    k = rng.standard_normal((7, 4))
+    v = rng.standard_normal((7, 4))
+    o_all, l_all = oracle.attend(q, k, v, 1.0)
+    o_e, l_e = oracle.attend(q, k[:0], v[:0], 1.0)
+    assert np.all(np.isneginf(l_e)) and np.all(o_e == 0)
+    o_m, l_m = oracle.merge_states([o_e, o_all], [l_e, l_all])
+    assert np.abs(o_m - o_all).max() < 1e-14 and np.abs(l_m - l_all).max() < 1e-14
+    o_z, l_z = oracle.merge_states([o_e, o_e], [l_e, l_e])
+    assert np.all(o_z == 0) and np.all(np.isneginf(l_z))
+
+
+def test_cascade_split_equals_full_attention():
+    """The decomposition the pages describe, done with the oracle's own
+    pieces: non-causal attention of every query over the capped shared
+    prefix, causal attention over each request's suffix, LSE merge. Checked
+    against full attention (a different computation of the same values)."""
+    b = _small_batch(seed=11, n=6, prefix=48, suffix=(5, 25), q=(1, 5), ps=8)
+    w = b.workload
+    G = w.num_q_heads // w.num_kv_heads
+    kc, vc = b.k_cache.float().numpy(), b.v_cache.float().numpy()
+    bt, qsl, sl = b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy()
+    full_o, full_l = oracle.attention_full(b.q.float().numpy(), kc, vc, bt, qsl, sl, w.page_size)
+    blocks = oracle.common_prefix_blocks(bt, sl, w.page_size)
+    pc = oracle.cascade_prefix_len(blocks, w.page_size, b.num_computed.numpy())
+    assert pc == 48
+    for r in range(w.num_reqs):
+        q0, q1 = int(qsl[r]), int(qsl[r + 1])
+        k, v = _dense_kv(b, r)
+        nc = int(b.num_computed[r])
+        for h in range(w.num_q_heads):
+            g = h // G
+            rows = b.q[q0:q1, h].double().numpy()
+            o_p, l_p = oracle.attend(rows, k[:pc, g].numpy(), v[:pc, g].numpy(), w.softmax_scale)
+            t = np.arange(pc, k.shape[0])
+            vis = t[None, :] <= (nc + np.arange(q1 - q0))[:, None]
+            o_s, l_s = oracle.attend(rows, k[pc:, g].numpy(), v[pc:, g].numpy(), w.softmax_scale, vis)
+            o_m, l_m = oracle.merge_states([o_p, o_s], [l_p, l_s])
+            assert np.abs(o_m - full_o[q0:q1, h]).max() < 1e-12
+            assert np.abs(l_m - full_l[q0:q1, h]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- invariances
+
+def _run(b, requests=None):
+    return oracle.attention_full(
+        b.q.float().numpy(), b.k_cache.float().numpy(), b.v_cache.float().numpy(),
+        b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy(),
+        b.workload.page_size, requests=requests)
+
+
+def _reorder(b, order):
+    qsl = b.query_start_loc
+    qs = [b.q[int(qsl[r]):int(qsl[r + 1])] for r in order]
+    lens = torch.tensor([int(qsl[r + 1] - qsl[r]) for r in order])
+    new_qsl = torch.zeros(len(order) + 1, dtype=torch.int32)
+    new_qsl[1:] = torch.cumsum(lens, 0)
+    return workloads.Batch(b.workload, torch.cat(qs), b.k_cache, b.v_cache,
+                           b.block_table[order], new_qsl, b.seq_lens[order], b.num_computed[order])
+
+
+def test_request_permutation_and_subset_are_bitwise_invariant():
+    b = _small_batch(seed=12)
+    out, lse = _run(b)
+    qsl = b.query_start_loc
+    order = [3, 0, 4, 1, 2]
+    out_p, lse_p = _run(_reorder(b, order))
+    qslp = _reorder(b, order).query_start_loc
+    for new_r, r in enumerate(order):
+        a = slice(int(qsl[r]), int(qsl[r + 1]))
+        c = slice(int(qslp[new_r]), int(qslp[new_r + 1]))
+        assert np.array_equal(out[a], out_p[c]) and np.array_equal(lse[a], lse_p[c])
+    alone_o, alone_l = _run(_reorder(b, [2]))
+    a = slice(int(qsl[2]), int(qsl[3]))
+    assert np.array_equal(out[a], alone_o) and np.array_equal(lse[a], alone_l)
+
+
+def test_page_relabel_is_bitwise_invariant():
+    b = _small_batch(seed=13)
+    out, lse = _run(b)
+    n = b.num_pages
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(5))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(n)
+    b2 = workloads.Batch(b.workload, b.q, b.k_cache[inv], b.v_cache[inv],
+                         perm[b.block_table.long()].to(torch.int32),
+                         b.query_start_loc, b.seq_lens, b.num_computed)
+    out2, lse2 = _run(b2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_oracle_never_reads_poison():
+    b = _small_batch(seed=14)
+    out, lse = _run(b)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+# ------------------------------------------------------------- host decisions
+
+def test_r1_r2_example(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "r1r2_example.json")))
+    tok = ex["tokens"]
+    bt = [[tok[x] for x in row] for row in ex["block_table"]]
+    blocks = oracle.common_prefix_blocks(bt, ex["seq_lens"], ex["page_size"])
+    assert blocks == ex["expected_common_blocks"]
+    pc = oracle.cascade_prefix_len(blocks, ex["page_size"], ex["num_computed_tokens"])
+    assert pc == ex["expected_prefix_len"]
+    assert bt[0][:pc] == [tok[x] for x in ex["expected_prefix"]]
+    for r in range(2):
+        assert bt[r][pc:ex["seq_lens"][r]] == [tok[x] for x in ex["expected_suffix"][r]]
+
+
+def test_cap_and_floor(golden_dir):
+    cases = json.load(open(os.path.join(golden_dir, "cap_floor.json")))["cases"]
+    for c in cases:
+        assert oracle.cascade_prefix_len(c["blocks"], c["page_size"], c["num_computed"]) == c["prefix_len"], c
+
+
+def test_gates(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "gates.json")))
+    assert oracle.MIN_PREFIX_TOKENS == g["min_prefix_tokens"]
+    assert oracle.MIN_NUM_REQS == g["min_num_reqs"]
+    for c in g["cases"]:
+        assert oracle.passes_cascade_gates(c["prefix_len"], c["num_reqs"]) == c["pass"], c
+
+
+def test_worked_example_kv_tokens(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    n, p, s = ex["num_reqs"], ex["prefix"], ex["suffix"]
+    lens = [p + s] * n
+    assert oracle.kv_tokens_standard(lens) == ex["kv_tokens_standard"]
+    assert oracle.kv_tokens_cascade(p, lens) == ex["kv_tokens_cascade"]
+    assert oracle.kv_tokens_cascade(p, lens) - p == ex["kv_tokens_cascade_suffix"]
+    assert round(ex["kv_tokens_standard"] / ex["kv_tokens_cascade"]) == ex["reduction"]
+
+
+def test_common_blocks_hand_cases():
+    ps = 4
+    # identical leading pages, then divergence at column 2
+    assert oracle.common_prefix_blocks([[5, 6, 7, 9], [5, 6, 8, 9]], [16, 16], ps) == 2
+    # divergence at column 0
+    assert oracle.common_prefix_blocks([[1, 6], [5, 6]], [8, 8], ps) == 0
+    # a short request: its padding column equals the other's real page, but
+    # padding never counts (limit = ceil(5/4) = 2 columns)
+    assert oracle.common_prefix_blocks([[5, 6, 7], [5, 6, 7]], [12, 5], ps) == 2
+    # a single request shares all of its pages with itself
+    assert oracle.common_prefix_blocks([[3, 4, 2]], [9], ps) == 3
+    # match resumes after a mismatch: still only the contiguous run counts
+    assert oracle.common_prefix_blocks([[1, 2, 3], [1, 9, 3]], [12, 12], ps) == 1
+
+
+def test_common_blocks_brute_force_tiny():
+    """Exhaustive check on tiny tables against a differently written rule:
+    the largest C such that the first C columns, restricted to real pages,
+    form one identical row."""
+    rng = np.random.default_rng(30)
+    for _ in range(2000):
+        n = int(rng.integers(1, 4))
+        cols = int(rng.integers(1, 5))
+        ps = int(rng.integers(1, 4))
+        bt = rng.integers(0, 3, (n, cols)).tolist()
+        lens = rng.integers(1, cols * ps + 1, n).tolist()
+        limit = min(-(-x // ps) for x in lens)
+        best = 0
+        for c in range(limit + 1):
+            if len({tuple(row[:c]) for row in bt}) == 1:
+                best = c
+        assert oracle.common_prefix_blocks(bt, lens, ps) == best
+
+
+# --------------------------------------------------------------- input recipe
+
+def test_workload_structure_matches_recipe():
+    b = workloads.make_batch(workloads.get("tiny_decode"))
+    w = b.workload
+    assert b.q.shape == (8, 4, 64) and b.q.dtype == torch.bfloat16
+    assert b.seq_lens.tolist() == [272] * 8
+    assert b.num_computed.tolist() == [271] * 8
+    shared = w.prefix // w.page_size
+    assert (b.block_table[:, :shared] == b.block_table[0, :shared]).all()
+    assert len(set(b.block_table[:, shared].tolist())) == 8
+    out, lse = _run(b)
+    assert np.isfinite(out).all()
