@@ -1,0 +1,203 @@
+/*
+ * cascade_attn.h -- C ABI of the MI355X (gfx950) shared-prefix ("cascade")
+ * attention library.
+ *
+ * The method ("vLLM Cascade Attention：用法、场景与原理解析", beaiera.top,
+ * section 1 and section 8 Step 5): for a batch of requests whose paged KV
+ * caches begin with the same physical pages,
+ *   (1) all requests' query tokens, packed as one sequence, attend
+ *       non-causally and once to the shared-prefix KV pages;
+ *   (2) each request attends causally to its own remaining ("suffix") pages;
+ *   (3) the two partial results are merged by log-sum-exp rescaling.
+ * The result equals ordinary causal attention of every request over its
+ * whole KV sequence; the saving is that the shared pages are read once
+ * instead of once per request (same page, section 5).
+ *
+ * Host side (same page, section 8 Steps 1-3): count the leading KV pages
+ * common to every request of the batch, cap that prefix at the smallest
+ * num_computed_tokens and floor it to a page, decide whether cascade pays,
+ * and derive the per-phase metadata. That is cascade_attn_plan(); it touches
+ * no device memory and may run while the GPU is busy with the previous step.
+ * cascade_attn_run() launches the kernels on the caller's stream.
+ *
+ * Conventions for every entry point:
+ *   - Plain C, no allocation visible to the caller other than the plan
+ *     handle; the caller owns every tensor (device memory from any allocator).
+ *   - Dtypes: Q, K/V cache and output are bf16; LSE and workspace fp32;
+ *     metadata int32.
+ *   - seq_lens[r] counts all KV positions of request r including this
+ *     step's q_len_r query tokens, which are its last q_len_r positions;
+ *     num_computed_tokens[r] = seq_lens[r] - q_len_r.
+ *   - Causal rule: query i (0-based within request r) sees KV positions
+ *     t <= num_computed_tokens[r] + i.
+ *   - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - LSE values are natural logs of the softmax normaliser of the scaled
+ *     scores.
+ *   - Every function returns a ca_status_t; on a non-OK status,
+ *     cascade_attn_last_error() returns a message for the calling thread.
+ *     No function aborts the process on bad input.
+ */
+#ifndef CASCADE_ATTN_H_
+#define CASCADE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CA_OK = 0,
+  CA_EINVAL = 1,        /* null pointer, bad handle, bad size argument */
+  CA_EUNSUPPORTED = 2,  /* head_dim not 64/128, page_size not 16, Hq % Hkv != 0 */
+  CA_EMETA = 3,         /* inconsistent batch metadata (lengths, page ids, strides) */
+  CA_EWORKSPACE = 4,    /* workspace smaller than the plan requires */
+  CA_EHIP = 5           /* a HIP runtime call or kernel launch failed */
+} ca_status_t;
+
+/* User switch over the planner's decision ([p1] "Diary - vLLM's cascade
+ * attention": the disable_cascade_attn option; [p2] section 3: cascade is
+ * only used when the heuristic says it pays). */
+typedef enum {
+  CA_MODE_AUTO = 0,       /* gates + cost model decide */
+  CA_MODE_FORCE_ON = 1,   /* cascade whenever the capped shared prefix is > 0 */
+  CA_MODE_FORCE_OFF = 2   /* always the non-cascade path */
+} ca_mode_t;
+
+typedef struct {
+  int32_t num_reqs;            /* N >= 1 */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
+  int32_t head_dim;            /* d: 64 or 128 */
+  int32_t page_size;           /* tokens per KV page: 16 */
+  int32_t block_table_stride;  /* int32 entries per block-table row */
+  int32_t num_pages;           /* pages in the KV pool (bounds check of page ids) */
+  int32_t reserved0;
+  /* K/V cache element strides (bf16 elements). The cache is indexed
+   * [page][slot][kv_head][d] with d contiguous; NHD layout
+   * [num_pages, page_size, Hkv, d] has (page_size*Hkv*d, Hkv*d, d), HND
+   * layout [num_pages, Hkv, page_size, d] has (Hkv*page_size*d, d, page_size*d).
+   * All three must be multiples of 8 (16-byte aligned rows). */
+  int64_t kv_stride_page;
+  int64_t kv_stride_token;
+  int64_t kv_stride_head;
+  float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t mode;                /* ca_mode_t */
+  int32_t num_cus;             /* compute units to plan for; 0 = query the current device */
+  int32_t reserved1;
+} ca_params_t;
+
+typedef struct {
+  int32_t use_cascade;                 /* 1 if run() takes the three-phase path */
+  int32_t num_common_prefix_blocks;    /* pages shared by every request */
+  int32_t common_prefix_len;           /* capped, page-floored shared prefix (tokens) */
+  int32_t gates_pass;                  /* prefix >= 256 tokens and >= 8 requests */
+  int32_t prefix_splits;               /* KV splits of the prefix phase */
+  int32_t prefix_row_tile;             /* packed query rows per prefix work-group */
+  int32_t suffix_chunks;               /* KV chunks per request of the suffix (or only) phase */
+  int32_t suffix_chunk_tokens;         /* tokens per chunk */
+  int32_t suffix_kernel;               /* 0 = tiled kernel, 1 = decode kernel */
+  int32_t num_partial_slots;           /* fp32 partial states per (token, head) */
+  int64_t total_q;                     /* T = query_start_loc[N] */
+  int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
+  int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */
+  int64_t kv_tokens_noncascade;        /* sum of seq_lens (positions read without cascade) */
+  float est_us_cascade;                /* cost-model estimates used by AUTO */
+  float est_us_noncascade;
+} ca_plan_info_t;
+
+typedef struct ca_plan* ca_plan_t;
+
+/*
+ * Number of leading KV pages shared by every request of the batch
+ * ([p2] section 8 Step 1: count the physical blocks shared by all running
+ * requests, matching contiguously from block 0; [p3] "resolve async KV
+ * transfer bug in cascade attention #23485": only the running requests --
+ * here, the rows passed in -- are counted).
+ *
+ * block_table_h: host int32 [num_reqs][stride]; seq_lens_h: host int32
+ * [num_reqs]. Column j is compared only if j < ceil(seq_lens[r]/page_size)
+ * for every r, so block-table padding never counts. Result in *out_blocks.
+ * Errors: CA_EINVAL for null pointers or non-positive sizes, CA_EMETA if a
+ * request needs more pages than stride.
+ */
+ca_status_t cascade_attn_num_common_prefix_blocks(const int32_t* block_table_h, int32_t num_reqs,
+                                                  int32_t stride, const int32_t* seq_lens_h,
+                                                  int32_t page_size, int32_t* out_blocks);
+
+/*
+ * Host-only planner ([p2] section 8 Steps 1-3; the decision of section 3).
+ * Reads host copies of the batch metadata:
+ *   block_table_h        int32 [num_reqs][block_table_stride]
+ *   query_start_loc_h    int32 [num_reqs + 1], [0] == 0, q_len_r >= 1
+ *   seq_lens_h           int32 [num_reqs]
+ *   num_computed_tokens_h int32 [num_reqs] (may be NULL: derived as
+ *                        seq_lens - q_len; if given it must equal that)
+ * and computes: the shared-page count, the capped/floored prefix length,
+ * the gates (prefix >= 256 tokens, >= 8 requests; [p2] section 3), the
+ * cascade/non-cascade decision (mode, then a cost model of this library's
+ * kernels on params->num_cus compute units), the work partition of each
+ * phase and the workspace size. Copies nothing but derived scalars; the
+ * plan is valid for every layer of the step (same metadata, any Q/KV).
+ * Device is touched only when params->num_cus == 0 (to read the CU count).
+ * Errors: CA_EINVAL (null pointers), CA_EUNSUPPORTED (head_dim, page_size,
+ * head ratio, strides), CA_EMETA (inconsistent lengths, a request needing
+ * more than stride pages, a referenced page id outside [0, num_pages)).
+ */
+ca_status_t cascade_attn_plan(const ca_params_t* params, const int32_t* block_table_h,
+                              const int32_t* query_start_loc_h, const int32_t* seq_lens_h,
+                              const int32_t* num_computed_tokens_h, ca_plan_t* out_plan);
+
+/* Copies the plan's decisions and sizes into *out. */
+ca_status_t cascade_attn_plan_info(ca_plan_t plan, ca_plan_info_t* out);
+
+/*
+ * Runs one attention step of the plan on `stream` (a hipStream_t; NULL =
+ * the null stream). Asynchronous: no host synchronisation, no allocation,
+ * no host-to-device copy; inputs must stay alive until the stream passes
+ * this call.
+ *   q                [T][num_q_heads][head_dim] bf16, contiguous
+ *   k_cache, v_cache paged bf16 caches with the plan's strides
+ *   block_table_d, query_start_loc_d, seq_lens_d: device copies of the
+ *                    same metadata given to cascade_attn_plan
+ *   out              [T][num_q_heads][head_dim] bf16 (written)
+ *   lse_out          [T][num_q_heads] fp32, natural log (written; may be NULL)
+ *   workspace        device scratch of >= info.workspace_bytes bytes (may be
+ *                    NULL when that is 0); 256-byte aligned. Its contents
+ *                    need no initialisation and are meaningless afterwards;
+ *                    two runs that overlap in time must not share it.
+ * Cascade path: prefix kernel + suffix kernel + merge kernel ([p2] section 8
+ * Step 5). Non-cascade path: one attention over each request's full block
+ * table (Step 4), plus a merge when the plan splits the KV range.
+ * Errors: CA_EINVAL (null pointers/handle), CA_EWORKSPACE (too small),
+ * CA_EHIP (launch failure).
+ */
+ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table_d, const int32_t* query_start_loc_d,
+                             const int32_t* seq_lens_d, void* out, float* lse_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Frees a plan (NULL is accepted). */
+void cascade_attn_plan_destroy(ca_plan_t plan);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* cascade_attn_last_error(void);
+
+/*
+ * Kernel timing for measurement. While enabled, run() records a HIP event
+ * pair around every kernel it launches, on the launch stream.
+ * cascade_attn_profile_read() waits for the recorded events, writes the
+ * summed milliseconds and launch counts per kernel kind
+ * (0 = prefix, 1 = suffix / non-cascade attention, 2 = merge,
+ * 3 = decode attention) into ms[4] and counts[4], and clears the record.
+ * Errors: CA_EHIP if an event call fails, CA_EINVAL for null outputs.
+ */
+ca_status_t cascade_attn_profile_enable(int32_t enable);
+ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CASCADE_ATTN_H_ */

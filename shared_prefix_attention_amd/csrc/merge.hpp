@@ -1,0 +1,53 @@
+// LSE merge of partial attention states ("vLLM Cascade Attention：用法、场景与
+// 原理解析", beaiera.top, section 1 step 3 and section 8 Step 5: the partial
+// outputs are combined by log-sum-exp rescaling; section 5: an element-wise
+// weighted sum). n-way: it combines the prefix splits and the suffix chunks
+// of every (token, head) row in one pass:
+//   M = max_s lse_s, w_s = exp(lse_s - M), out = sum_s w_s o_s / sum_s w_s,
+//   lse = M + log(sum_s w_s).
+// Partials with lse = -inf have weight 0 and their o is not read.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace ca {
+
+struct MergeArgs {
+  const float* part_o;     // [slots][rows][D]
+  const float* part_lse;   // [slots][rows]
+  int32_t slots;
+  int64_t rows;            // T * hq
+  int64_t slot_elems;      // rows * D
+  uint16_t* out;           // [rows][D] bf16
+  float* lse_out;          // [rows] (may be null)
+};
+
+// D/4 threads per row, each owning 4 consecutive d values.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  if (row >= a.rows) return;
+  float big = -INFINITY;
+  for (int s = 0; s < a.slots; ++s) big = fmaxf(big, a.part_lse[(int64_t)s * a.rows + row]);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (big != -INFINITY) {
+    for (int s = 0; s < a.slots; ++s) {
+      const float l = a.part_lse[(int64_t)s * a.rows + row];
+      if (l == -INFINITY) continue;
+      const float w = exp2f((l - big) * kLog2e);
+      wsum += w;
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.part_o + (int64_t)s * a.slot_elems + row * D + part * 4);
+      acc += w * x;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  acc *= inv;
+  *reinterpret_cast<u32x2_t*>(a.out + row * D + part * 4) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  if (part == 0 && a.lse_out) a.lse_out[row] = wsum > 0.f ? big + logf(wsum) : -INFINITY;
+}
+
+}  // namespace ca

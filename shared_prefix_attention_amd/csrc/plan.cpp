@@ -1,0 +1,334 @@
+// Host planner: common-prefix detection, prefix-length cap, cascade decision
+// and the work partition of each kernel. Pure host C++ (no HIP calls except
+// the optional CU-count query in cascade_attn_plan, kept in run.hip).
+//
+// Method references: "vLLM Cascade Attention：用法、场景与原理解析"
+// (beaiera.top), section 8 Steps 1-3 (detector, cap/floor, metadata) and
+// section 3 (trigger thresholds); "resolve async KV transfer bug in cascade
+// attention #23485" (the detector counts running requests only).
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "plan.h"
+
+namespace ca {
+
+static thread_local std::string g_err;
+
+void set_error(const std::string& msg) { g_err = msg; }
+
+static ca_status_t fail(ca_status_t code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// [p2] section 8 Step 1 / [p3]: leading block-table columns whose physical
+// page id is the same in every row, stopping at the first column that
+// differs; only columns inside every request's own pages are compared.
+static int32_t count_common_blocks(const int32_t* bt, int32_t n, int32_t stride, const int32_t* seq_lens,
+                                   int32_t ps) {
+  int64_t limit = stride;
+  for (int32_t r = 0; r < n; ++r) limit = std::min<int64_t>(limit, cdiv(seq_lens[r], ps));
+  int32_t count = 0;
+  for (int64_t j = 0; j < limit; ++j) {
+    const int32_t first = bt[j];
+    bool same = true;
+    for (int32_t r = 1; r < n && same; ++r) same = (bt[(int64_t)r * stride + j] == first);
+    if (!same) break;
+    ++count;
+  }
+  return count;
+}
+
+// Cost model of this library's own kernels on `cus` compute units. The pages
+// give only the shape of such a model (section 9 of [p2]: count the work
+// tiles of each path and the waves of them the SMs must run; cascade only
+// when it beats the plain path) and ask that it be re-derived per kernel
+// family ([p4] "Update Cascade Attention Heuristics for FA3"). Constants are
+// effective rates of these kernels on MI355X, not spec-sheet peaks.
+struct CostModel {
+  double hbm_bw = 4.5e12;         // bytes/s streamed from HBM by the attention kernels
+  double mall_bw = 11.0e12;       // bytes/s for re-reads that hit L2 / Infinity Cache
+  double cu_mfma = 4.0e12;        // flop/s of one CU in the tiled MFMA kernel
+  double launch_us = 2.5;         // per kernel launch on one stream
+  double mall_bytes = 256.0e6;    // Infinity Cache capacity
+};
+
+struct TileChoice {
+  int32_t row_blocks, mtiles, splits, split_tokens;
+  double est_us;
+};
+
+// Prefix phase: rows = T*G packed (token, head-in-group) rows per KV head,
+// keys = the capped shared prefix.
+static TileChoice choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& cm) {
+  const int64_t rows = pl.total_q * pl.group;
+  const int32_t rb = rows >= 512 ? 2 : 1;
+  const int64_t bm = 64 * rb;
+  const int64_t mtiles = cdiv(rows, bm);
+  const int64_t ntiles = cdiv(pl.prefix_len, kTileKeys);
+  const double bpt = 4.0 * pl.hkv * pl.d;                       // K+V bytes per token
+  const double part_per_split = (double)pl.total_q * pl.hq * (pl.d + 1) * 4.0;
+  TileChoice best{rb, (int32_t)mtiles, 1, (int32_t)round_up(pl.prefix_len, kTileKeys), 1e30};
+  for (int64_t s = 1; s <= ntiles; s *= 2) {
+    const int64_t tiles_per = cdiv(ntiles, s);
+    const int64_t splits = cdiv(ntiles, tiles_per);
+    const int64_t items = mtiles * pl.hkv * splits;
+    const double item_flops = 4.0 * bm * pl.d * (double)tiles_per * kTileKeys;
+    const double rounds = std::ceil((double)items / cus);
+    const double t_mfma = rounds * item_flops / cm.cu_mfma;
+    const double bytes = bpt * pl.prefix_len + part_per_split * splits +
+                         (double)pl.total_q * pl.hq * pl.d * 2.0;
+    const double t_bytes = bytes / cm.hbm_bw;
+    const double t = std::max(t_mfma, t_bytes) * 1e6 + (part_per_split * splits / cm.mall_bw) * 1e6;
+    if (t < best.est_us) best = {rb, (int32_t)mtiles, (int32_t)splits, (int32_t)(tiles_per * kTileKeys), t};
+    if (splits == ntiles) break;
+  }
+  return best;
+}
+
+// Suffix (or only) phase: per request r the rows are q_len_r*G and the keys
+// [key_start, seq_len_r); chunks split the keys so the grid fills the chip.
+static TileChoice choose_suffix(const ca_plan& pl, int32_t cus, bool has_merge_anyway, const CostModel& cm) {
+  const int32_t rb = 1;
+  const int64_t mt = cdiv((int64_t)pl.max_q_len * pl.group, 64 * rb);
+  const int64_t base = (int64_t)pl.num_reqs * mt * pl.hkv;
+  const int64_t ntiles = std::max<int64_t>(1, cdiv(pl.max_suffix_len, kTileKeys));
+  const int64_t want = std::max<int64_t>(1, cdiv(2 * (int64_t)cus, base));
+  int64_t chunks = std::min(ntiles, want);
+  const int64_t tiles_per = cdiv(ntiles, chunks);
+  chunks = cdiv(ntiles, tiles_per);
+  (void)has_merge_anyway;
+  (void)cm;
+  return {rb, (int32_t)mt, (int32_t)chunks, (int32_t)(tiles_per * kTileKeys), 0.0};
+}
+
+// Per-request phase over KV positions [key_start, seq_len): HBM bytes for the
+// KV actually streamed, plus the MFMA work of 16-row padded query blocks.
+static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_flops, int32_t chunks, bool merge,
+                            int32_t cus, const CostModel& cm, double extra_mall_bytes) {
+  const double bpt = 4.0 * pl.hkv * pl.d;
+  const double io = (double)pl.total_q * pl.hq * pl.d * 2.0 * 2.0;
+  const double t_bytes = (bpt * kv_tokens + io) / cm.hbm_bw + extra_mall_bytes / cm.mall_bw;
+  const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma);
+  double us = std::max(t_bytes, t_mfma) * 1e6 + cm.launch_us;
+  if (merge) {
+    const double part = (double)chunks * pl.total_q * pl.hq * (pl.d + 1) * 4.0;
+    us += 2.0 * part / cm.mall_bw * 1e6 + cm.launch_us;
+  }
+  return us;
+}
+
+// MFMA work of the per-request phase: every KV head of request r runs
+// ceil(q_len*G / 16) blocks of 16 rows over its keys (causal rows stop early,
+// counted here as the mean of the first and last row's key count).
+static double suffix_padded_flops(const ca_plan& pl, const int32_t* qsl, const int32_t* seq_lens, int32_t key_start) {
+  double f = 0.0;
+  for (int32_t r = 0; r < pl.num_reqs; ++r) {
+    const int64_t ql = (int64_t)qsl[r + 1] - qsl[r];
+    const int64_t keys_last = seq_lens[r] - key_start;
+    const int64_t keys_first = keys_last - (ql - 1);
+    const double blocks = (double)cdiv(ql * pl.group, 16);
+    f += blocks * 16.0 * 0.5 * (double)(keys_first + keys_last);
+  }
+  return f * 4.0 * pl.d * pl.hkv;
+}
+
+}  // namespace ca
+
+using namespace ca;
+
+extern "C" const char* cascade_attn_last_error(void) { return g_err.c_str(); }
+
+extern "C" ca_status_t cascade_attn_num_common_prefix_blocks(const int32_t* block_table_h, int32_t num_reqs,
+                                                             int32_t stride, const int32_t* seq_lens_h,
+                                                             int32_t page_size, int32_t* out_blocks) {
+  if (!block_table_h || !seq_lens_h || !out_blocks) return fail(CA_EINVAL, "null pointer argument");
+  if (num_reqs <= 0 || stride <= 0 || page_size <= 0) return fail(CA_EINVAL, "num_reqs, stride and page_size must be > 0");
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (seq_lens_h[r] < 0) return fail(CA_EMETA, "negative seq_len for request " + std::to_string(r));
+    if (cdiv(seq_lens_h[r], page_size) > stride)
+      return fail(CA_EMETA, "request " + std::to_string(r) + " needs more pages than block_table_stride");
+  }
+  *out_blocks = count_common_blocks(block_table_h, num_reqs, stride, seq_lens_h, page_size);
+  return CA_OK;
+}
+
+// Defined in run.hip: CU count of the current device (host HIP call).
+extern "C" int ca_query_num_cus(int32_t* out);
+
+extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* bt, const int32_t* qsl,
+                                         const int32_t* seq_lens, const int32_t* num_computed,
+                                         ca_plan_t* out_plan) {
+  if (!prm || !bt || !qsl || !seq_lens || !out_plan) return fail(CA_EINVAL, "null pointer argument");
+  *out_plan = nullptr;
+  const ca_params_t& p = *prm;
+  if (p.num_reqs <= 0) return fail(CA_EINVAL, "num_reqs must be >= 1");
+  if (p.num_q_heads <= 0 || p.num_kv_heads <= 0) return fail(CA_EINVAL, "head counts must be >= 1");
+  if (p.num_q_heads % p.num_kv_heads != 0) return fail(CA_EUNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
+  if (p.head_dim != 64 && p.head_dim != 128) return fail(CA_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (p.page_size != 16) return fail(CA_EUNSUPPORTED, "page_size must be 16");
+  if (p.block_table_stride <= 0) return fail(CA_EINVAL, "block_table_stride must be >= 1");
+  if (p.num_pages <= 0) return fail(CA_EINVAL, "num_pages must be >= 1");
+  if (p.kv_stride_page <= 0 || p.kv_stride_token <= 0 || p.kv_stride_head <= 0 || p.kv_stride_page % 8 ||
+      p.kv_stride_token % 8 || p.kv_stride_head % 8)
+    return fail(CA_EUNSUPPORTED, "KV strides must be positive multiples of 8 elements");
+  if (p.mode < CA_MODE_AUTO || p.mode > CA_MODE_FORCE_OFF) return fail(CA_EINVAL, "unknown mode");
+
+  const int32_t n = p.num_reqs, ps = p.page_size, stride = p.block_table_stride;
+  if (qsl[0] != 0) return fail(CA_EMETA, "query_start_loc[0] must be 0");
+  int32_t max_q = 0, max_seq = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    const int64_t ql = (int64_t)qsl[r + 1] - qsl[r];
+    if (ql < 1) return fail(CA_EMETA, "request " + std::to_string(r) + " has no query token");
+    if (seq_lens[r] < ql) return fail(CA_EMETA, "seq_len smaller than query length for request " + std::to_string(r));
+    if (num_computed && num_computed[r] != seq_lens[r] - ql)
+      return fail(CA_EMETA, "num_computed_tokens != seq_len - q_len for request " + std::to_string(r));
+    const int64_t pages = cdiv(seq_lens[r], ps);
+    if (pages > stride) return fail(CA_EMETA, "request " + std::to_string(r) + " needs more pages than block_table_stride");
+    for (int64_t j = 0; j < pages; ++j) {
+      const int32_t id = bt[(int64_t)r * stride + j];
+      if (id < 0 || id >= p.num_pages)
+        return fail(CA_EMETA, "page id out of range in request " + std::to_string(r));
+    }
+    max_q = std::max<int32_t>(max_q, (int32_t)ql);
+    max_seq = std::max(max_seq, seq_lens[r]);
+  }
+  const int64_t total_q = qsl[n];
+
+  int32_t cus = p.num_cus;
+  if (cus <= 0) {
+    if (ca_query_num_cus(&cus) != 0 || cus <= 0) return fail(CA_EHIP, "could not query the device CU count");
+  }
+
+  ca_plan* pl = new (std::nothrow) ca_plan();
+  if (!pl) return fail(CA_EINVAL, "out of host memory");
+  pl->p = p;
+  pl->num_reqs = n;
+  pl->hq = p.num_q_heads;
+  pl->hkv = p.num_kv_heads;
+  pl->group = p.num_q_heads / p.num_kv_heads;
+  pl->d = p.head_dim;
+  pl->ps = ps;
+  pl->total_q = total_q;
+  pl->max_q_len = max_q;
+  pl->max_seq_len = max_seq;
+  pl->scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)p.head_dim);
+
+  // Step 1: shared pages. Step 2: cap at min num_computed, floor to a page.
+  pl->common_blocks = count_common_blocks(bt, n, stride, seq_lens, ps);
+  int64_t min_computed = INT64_MAX;
+  for (int32_t r = 0; r < n; ++r) min_computed = std::min<int64_t>(min_computed, seq_lens[r] - (qsl[r + 1] - qsl[r]));
+  int64_t plen = (int64_t)pl->common_blocks * ps;
+  plen = std::min(plen, min_computed);
+  plen = (plen / ps) * ps;
+  pl->prefix_len = (int32_t)plen;
+  // [p2] section 3: shared prefix >= 256 tokens and >= 8 requests.
+  pl->gates_pass = (plen >= 256 && n >= 8) ? 1 : 0;
+
+  int64_t sum_seq = 0;
+  for (int32_t r = 0; r < n; ++r) sum_seq += seq_lens[r];
+  pl->kv_tokens_noncascade = sum_seq;
+  pl->kv_tokens_cascade = plen + (sum_seq - plen * n);
+
+  const CostModel cm;
+  const double bpt = 4.0 * pl->hkv * pl->d;
+
+  // Non-cascade estimate: every request streams its whole sequence; the
+  // shared pages are fetched from HBM once and re-read from cache by the
+  // other requests when they fit in it.
+  pl->key_start = 0;
+  pl->max_suffix_len = max_seq;
+  TileChoice nc = choose_suffix(*pl, cus, false, cm);
+  {
+    const double shared_bytes = bpt * plen;
+    const double reread = shared_bytes * (n - 1);
+    int64_t hbm_tokens = pl->kv_tokens_cascade;
+    double extra = 0.0;
+    if (shared_bytes <= cm.mall_bytes) extra = reread;
+    else hbm_tokens = sum_seq;
+    pl->est_us_noncascade = (float)est_suffix_us(*pl, hbm_tokens, suffix_padded_flops(*pl, qsl, seq_lens, 0),
+                                                 nc.splits, nc.splits > 1, cus, cm, extra);
+  }
+
+  // Cascade estimate (only meaningful when something is shared).
+  TileChoice pre{1, 0, 1, 0, 0.0}, suf{1, 0, 1, 0, 0.0};
+  if (plen > 0) {
+    pl->prefix_len = (int32_t)plen;
+    pre = choose_prefix(*pl, cus, cm);
+    pl->key_start = (int32_t)plen;
+    pl->max_suffix_len = max_seq - (int32_t)plen;
+    suf = choose_suffix(*pl, cus, true, cm);
+    const double t_suf = est_suffix_us(*pl, pl->kv_tokens_cascade - plen,
+                                       suffix_padded_flops(*pl, qsl, seq_lens, (int32_t)plen), suf.splits, false,
+                                       cus, cm, 0.0);
+    const double merge_bytes = (double)(pre.splits + suf.splits) * total_q * pl->hq * (pl->d + 1) * 4.0 +
+                               (double)total_q * pl->hq * pl->d * 2.0;
+    pl->est_us_cascade = (float)(pre.est_us + cm.launch_us + t_suf +
+                                 (merge_bytes / cm.mall_bw) * 1e6 + cm.launch_us);
+  }
+
+  bool cascade = false;
+  if (p.mode == CA_MODE_FORCE_ON) cascade = plen > 0;
+  else if (p.mode == CA_MODE_AUTO) cascade = pl->gates_pass && pl->est_us_cascade < pl->est_us_noncascade;
+  pl->use_cascade = cascade ? 1 : 0;
+
+  if (cascade) {
+    pl->key_start = (int32_t)plen;
+    pl->max_suffix_len = max_seq - (int32_t)plen;
+    pl->prefix = {pre.row_blocks, pre.mtiles, pre.splits, pre.split_tokens, 0};
+    pl->suffix = {suf.row_blocks, suf.mtiles, suf.splits, suf.split_tokens, 0};
+    pl->num_slots = pre.splits + suf.splits;
+    pl->direct_out = false;
+  } else {
+    pl->key_start = 0;
+    pl->max_suffix_len = max_seq;
+    pl->prefix = {};
+    pl->suffix = {nc.row_blocks, nc.mtiles, nc.splits, nc.split_tokens, 0};
+    pl->num_slots = nc.splits > 1 ? nc.splits : 0;
+    pl->direct_out = nc.splits == 1;
+  }
+  pl->slot_elems = total_q * pl->hq * pl->d;
+  if (pl->num_slots > 0) {
+    const int64_t o_bytes = round_up((int64_t)pl->num_slots * pl->slot_elems * 4, 256);
+    const int64_t l_bytes = round_up((int64_t)pl->num_slots * total_q * pl->hq * 4, 256);
+    pl->ws_lse_offset = o_bytes;
+    pl->workspace_bytes = o_bytes + l_bytes;
+  } else {
+    pl->ws_lse_offset = 0;
+    pl->workspace_bytes = 0;
+  }
+  *out_plan = pl;
+  return CA_OK;
+}
+
+extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out) {
+  if (!pl || !out) return fail(CA_EINVAL, "null plan or output");
+  std::memset(out, 0, sizeof(*out));
+  out->use_cascade = pl->use_cascade;
+  out->num_common_prefix_blocks = pl->common_blocks;
+  out->common_prefix_len = pl->prefix_len;
+  out->gates_pass = pl->gates_pass;
+  out->prefix_splits = pl->use_cascade ? pl->prefix.splits : 0;
+  out->prefix_row_tile = pl->use_cascade ? 64 * pl->prefix.row_blocks : 0;
+  out->suffix_chunks = pl->suffix.splits;
+  out->suffix_chunk_tokens = pl->suffix.split_tokens;
+  out->suffix_kernel = pl->suffix.kernel;
+  out->num_partial_slots = pl->num_slots;
+  out->total_q = pl->total_q;
+  out->workspace_bytes = pl->workspace_bytes;
+  out->kv_tokens_cascade = pl->kv_tokens_cascade;
+  out->kv_tokens_noncascade = pl->kv_tokens_noncascade;
+  out->est_us_cascade = pl->est_us_cascade;
+  out->est_us_noncascade = pl->est_us_noncascade;
+  return CA_OK;
+}
+
+extern "C" void cascade_attn_plan_destroy(ca_plan_t pl) { delete pl; }

@@ -1,0 +1,57 @@
+// Internal plan record shared by the host planner (plan.cpp) and the launcher
+// (run.hip). Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "cascade_attn.h"
+
+namespace ca {
+
+// Keys staged per LDS tile by the tiled kernel (4 pages of 16 tokens).
+constexpr int kTileKeys = 64;
+// Threads per work-group of every attention kernel (4 wave64s).
+constexpr int kThreads = 256;
+
+struct PhaseTile {
+  int32_t row_blocks = 1;      // 16-row MFMA blocks per wave (rows per WG = 64 * row_blocks)
+  int32_t mtiles = 0;          // row tiles (prefix: of the packed rows; suffix: max per request)
+  int32_t splits = 1;          // KV splits (prefix) or chunks per request (suffix)
+  int32_t split_tokens = 0;    // tokens per split / chunk (multiple of kTileKeys)
+  int32_t kernel = 0;          // suffix only: 0 = tiled, 1 = decode
+};
+
+}  // namespace ca
+
+struct ca_plan {
+  ca_params_t p;
+  int32_t num_reqs = 0, hq = 0, hkv = 0, group = 0, d = 0, ps = 0;
+  int64_t total_q = 0;
+  int32_t max_q_len = 0;
+  int32_t max_seq_len = 0;
+  float scale = 0.f;
+
+  int32_t common_blocks = 0;
+  int32_t prefix_len = 0;
+  int32_t gates_pass = 0;
+  int32_t use_cascade = 0;
+
+  ca::PhaseTile prefix;       // used when use_cascade
+  ca::PhaseTile suffix;       // suffix phase (cascade) or the only phase
+  int32_t key_start = 0;      // first KV position of the suffix phase (prefix_len or 0)
+  int32_t max_suffix_len = 0; // max over requests of seq_len - key_start
+  int32_t num_slots = 0;      // fp32 partial states per (token, head)
+  bool direct_out = false;    // single-phase single-chunk run writes bf16 output directly
+  int64_t slot_elems = 0;     // T * Hq * d
+  int64_t ws_lse_offset = 0;  // byte offset of the partial LSE array
+  int64_t workspace_bytes = 0;
+
+  int64_t kv_tokens_cascade = 0;
+  int64_t kv_tokens_noncascade = 0;
+  float est_us_cascade = 0.f, est_us_noncascade = 0.f;
+};
+
+namespace ca {
+void set_error(const std::string& msg);
+}

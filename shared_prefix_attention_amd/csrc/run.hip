@@ -1,0 +1,229 @@
+// Launcher: cascade_attn_run() and the kernel-timing hooks.
+//
+// Cascade path ("vLLM Cascade Attention：用法、场景与原理解析", beaiera.top,
+// section 8 Step 5): prefix phase (all queries, shared pages, non-causal) ->
+// suffix phase (per request, own pages, causal) -> LSE merge. Non-cascade
+// path (Step 4): one attention over each request's whole block table, plus
+// a merge when the plan splits the KV range. All launches go to the
+// caller's stream in order; nothing here allocates or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attn_tile.hpp"
+#include "merge.hpp"
+#include "plan.h"
+
+using namespace ca;
+
+namespace {
+
+enum KernelKind { K_PREFIX = 0, K_SUFFIX = 1, K_MERGE = 2, K_DECODE = 3, K_KINDS = 4 };
+
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+};
+Profiler g_prof;
+
+struct LaunchTimer {
+  hipEvent_t a = nullptr, b = nullptr;
+  int kind;
+  hipStream_t s;
+  bool on;
+  LaunchTimer(int k, hipStream_t st) : kind(k), s(st) {
+    on = g_prof.enabled;
+    if (on) {
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+        on = false;
+        return;
+      }
+      (void)hipEventRecord(a, s);
+    }
+  }
+  void done() {
+    if (!on) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> g(g_prof.mu);
+    g_prof.recs.push_back({kind, a, b});
+  }
+};
+
+ca_status_t fail(ca_status_t c, const std::string& m) {
+  set_error(m);
+  return c;
+}
+
+ca_status_t check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CA_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+  return CA_OK;
+}
+
+template <int D, int RB>
+void launch_tile(const TileArgs& args, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_tile_kernel<D, RB>), dim3(grid), dim3(kThreads), 0, s, args);
+}
+
+template <int D>
+ca_status_t run_tile(const TileArgs& args, int rb, int64_t grid, hipStream_t s, int kind) {
+  if (grid <= 0) return CA_OK;
+  if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
+  LaunchTimer tm(kind, s);
+  if (rb == 2) launch_tile<D, 2>(args, (int)grid, s);
+  else launch_tile<D, 1>(args, (int)grid, s);
+  tm.done();
+  return check_launch("attention kernel launch");
+}
+
+template <int D>
+ca_status_t run_merge(const MergeArgs& args, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 4);
+  const int64_t grid = (args.rows + RPB - 1) / RPB;
+  if (grid <= 0) return CA_OK;
+  LaunchTimer tm(K_MERGE, s);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, args);
+  tm.done();
+  return check_launch("merge kernel launch");
+}
+
+template <int D>
+ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void* v, const int32_t* bt,
+                     const int32_t* qsl, const int32_t* sl, void* out, float* lse, void* ws, hipStream_t s) {
+  TileArgs base{};
+  base.q = static_cast<const uint16_t*>(q);
+  base.k = static_cast<const uint16_t*>(k);
+  base.v = static_cast<const uint16_t*>(v);
+  base.sp = pl->p.kv_stride_page;
+  base.st = pl->p.kv_stride_token;
+  base.sh = pl->p.kv_stride_head;
+  base.bt = bt;
+  base.qsl = qsl;
+  base.seq_lens = sl;
+  base.bt_stride = pl->p.block_table_stride;
+  base.hq = pl->hq;
+  base.hkv = pl->hkv;
+  base.group = pl->group;
+  base.scale_log2 = pl->scale * kLog2e;
+  base.num_reqs = pl->num_reqs;
+  base.slot_elems = pl->slot_elems;
+  base.slot_rows = pl->total_q * pl->hq;
+  base.out = static_cast<uint16_t*>(out);
+  base.lse_out = lse;
+  float* part_o = static_cast<float*>(ws);
+  float* part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl->ws_lse_offset) : nullptr;
+  base.part_o = part_o;
+  base.part_lse = part_lse;
+
+  ca_status_t st;
+  if (pl->use_cascade) {
+    TileArgs pa = base;
+    pa.prefix_mode = 1;
+    pa.total_rows = (int32_t)(pl->total_q * pl->group);
+    pa.prefix_len = pl->prefix_len;
+    pa.mtiles = pl->prefix.mtiles;
+    pa.splits = pl->prefix.splits;
+    pa.split_tokens = pl->prefix.split_tokens;
+    pa.slot_base = 0;
+    pa.direct = 0;
+    st = run_tile<D>(pa, pl->prefix.row_blocks, (int64_t)pa.mtiles * pl->hkv * pa.splits, s, K_PREFIX);
+    if (st != CA_OK) return st;
+  }
+  TileArgs sa = base;
+  sa.prefix_mode = 0;
+  sa.key_start = pl->key_start;
+  sa.mtiles = pl->suffix.mtiles;
+  sa.splits = pl->suffix.splits;
+  sa.split_tokens = pl->suffix.split_tokens;
+  sa.slot_base = pl->use_cascade ? pl->prefix.splits : 0;
+  sa.direct = pl->direct_out ? 1 : 0;
+  st = run_tile<D>(sa, pl->suffix.row_blocks, (int64_t)pl->num_reqs * sa.mtiles * pl->hkv * sa.splits, s, K_SUFFIX);
+  if (st != CA_OK) return st;
+  if (!pl->direct_out) {
+    MergeArgs ma{};
+    ma.part_o = part_o;
+    ma.part_lse = part_lse;
+    ma.slots = pl->num_slots;
+    ma.rows = pl->total_q * pl->hq;
+    ma.slot_elems = pl->slot_elems;
+    ma.out = static_cast<uint16_t*>(out);
+    ma.lse_out = lse;
+    st = run_merge<D>(ma, s);
+    if (st != CA_OK) return st;
+  }
+  return CA_OK;
+}
+
+}  // namespace
+
+extern "C" int ca_query_num_cus(int32_t* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 1;
+  *out = n;
+  return 0;
+}
+
+extern "C" ca_status_t cascade_attn_run(ca_plan_t pl, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table_d, const int32_t* query_start_loc_d,
+                                        const int32_t* seq_lens_d, void* out, float* lse_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!pl) return fail(CA_EINVAL, "null plan");
+  if (!q || !k_cache || !v_cache || !block_table_d || !query_start_loc_d || !seq_lens_d || !out)
+    return fail(CA_EINVAL, "null tensor argument");
+  if ((int64_t)workspace_bytes < pl->workspace_bytes || (pl->workspace_bytes > 0 && !workspace))
+    return fail(CA_EWORKSPACE, "workspace smaller than the plan requires (" + std::to_string(pl->workspace_bytes) +
+                                   " bytes)");
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(CA_EINVAL, "workspace must be 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+       reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(CA_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pl->d == 128)
+    return run_impl<128>(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse_out,
+                         workspace, s);
+  return run_impl<64>(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse_out, workspace,
+                      s);
+}
+
+extern "C" ca_status_t cascade_attn_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> g(g_prof.mu);
+  g_prof.enabled = enable != 0;
+  return CA_OK;
+}
+
+extern "C" ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts) {
+  if (!ms || !counts) return fail(CA_EINVAL, "null output");
+  std::vector<Profiler::Rec> recs;
+  {
+    std::lock_guard<std::mutex> g(g_prof.mu);
+    recs.swap(g_prof.recs);
+  }
+  for (int i = 0; i < K_KINDS; ++i) {
+    ms[i] = 0.0;
+    counts[i] = 0;
+  }
+  ca_status_t st = CA_OK;
+  for (auto& r : recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      st = fail(CA_EHIP, "event timing failed");
+    } else {
+      ms[r.kind] += t;
+      counts[r.kind] += 1;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  return st;
+}

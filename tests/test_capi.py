@@ -1,0 +1,191 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and its host planner agrees with the oracle's definitions (no kernel runs)."""
+
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import shared_prefix_attention_amd as spa
+from shared_prefix_attention_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+
+def test_library_exports_every_header_symbol():
+    lib = spa.load()
+    names = _lib.header_symbols()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        ctypes.cast(getattr(lib, n), ctypes.c_void_p)
+
+
+def _plan(b, mode="auto", **kw):
+    w = b.workload
+    return spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                          k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
+                          seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode,
+                          num_cus=256, **kw)
+
+
+def test_detector_matches_oracle_on_random_tables():
+    rng = np.random.default_rng(40)
+    for _ in range(3000):
+        n = int(rng.integers(1, 5))
+        cols = int(rng.integers(1, 6))
+        ps = int(rng.integers(1, 5))
+        base = rng.integers(0, 3, cols)
+        bt = np.tile(base, (n, 1))
+        # perturb a few entries so rows diverge at random columns
+        for _ in range(int(rng.integers(0, 4))):
+            bt[rng.integers(0, n), rng.integers(0, cols)] = rng.integers(0, 3)
+        lens = rng.integers(1, cols * ps + 1, n)
+        got = spa.cascade_attn_num_common_prefix_blocks(bt, lens, ps)
+        assert got == oracle.common_prefix_blocks(bt.tolist(), lens.tolist(), ps)
+
+
+def test_detector_r1_r2_example(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "r1r2_example.json")))
+    tok = ex["tokens"]
+    bt = [[tok[x] for x in row] for row in ex["block_table"]]
+    assert spa.cascade_attn_num_common_prefix_blocks(bt, ex["seq_lens"], ex["page_size"]) == \
+        ex["expected_common_blocks"]
+
+
+def test_plan_r1_r2_example_scaled_to_pages(golden_dir):
+    """The section-4 example with every token of it scaled to one 16-token page:
+    shared pages A..E, R1 computed 3 pages, R2 computed 4 -> prefix 3 pages."""
+    ex = json.load(open(os.path.join(golden_dir, "r1r2_example.json")))
+    tok = ex["tokens"]
+    bt = np.array([[tok[x] for x in row] for row in ex["block_table"]], dtype=np.int32)
+    ps = 16
+    seq = np.array(ex["seq_lens"]) * ps
+    nc = np.array(ex["num_computed_tokens"]) * ps
+    qsl = np.concatenate([[0], np.cumsum(seq - nc)])
+    pl = spa.cascade_attn_plan(num_q_heads=2, num_kv_heads=1, head_dim=64, page_size=ps, num_pages=7,
+                               kv_strides=(ps * 64, 64, 64), block_table=bt, query_start_loc=qsl,
+                               seq_lens=seq, num_computed_tokens=nc, mode="on", num_cus=256)
+    assert pl.info["num_common_prefix_blocks"] == ex["expected_common_blocks"]
+    assert pl.info["common_prefix_len"] == ex["expected_prefix_len"] * ps
+    assert pl.info["use_cascade"] == 1
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_plan_matches_oracle_on_workloads(name):
+    b = workloads.make_batch(workloads.get(name))
+    pl = _plan(b)
+    info = pl.info
+    ps = b.workload.page_size
+    blocks = oracle.common_prefix_blocks(b.block_table.tolist(), b.seq_lens.tolist(), ps)
+    plen = oracle.cascade_prefix_len(blocks, ps, b.num_computed.tolist())
+    assert info["num_common_prefix_blocks"] == blocks
+    assert info["common_prefix_len"] == plen
+    assert info["gates_pass"] == int(oracle.passes_cascade_gates(plen, b.workload.num_reqs))
+    assert info["kv_tokens_noncascade"] == oracle.kv_tokens_standard(b.seq_lens.tolist())
+    assert info["kv_tokens_cascade"] == oracle.kv_tokens_cascade(plen, b.seq_lens.tolist())
+    assert info["total_q"] == b.total_q
+    if not info["gates_pass"]:
+        assert info["use_cascade"] == 0
+    on = _plan(b, mode="on").info
+    off = _plan(b, mode="off").info
+    assert on["use_cascade"] == int(plen > 0)
+    assert off["use_cascade"] == 0
+
+
+def test_expected_prefix_lengths_of_the_workloads():
+    expect = {"tiny_decode": 256, "worked_decode": 4096, "mixed_prefill": 2048,
+              "mixed_prefill_capped": 2032, "self_consistency": 8192, "long_doc": 32768,
+              "long_doc_n8": 32768, "long_doc_p255": 240}
+    for name, plen in expect.items():
+        b = workloads.make_batch(workloads.get(name))
+        assert _plan(b).info["common_prefix_len"] == plen, name
+
+
+def test_auto_decisions_at_the_gates():
+    # P=255 -> 240 shared tokens: below 256, AUTO must fall back
+    assert _plan(workloads.make_batch(workloads.get("long_doc_p255"))).info["use_cascade"] == 0
+    # N = 8 with a 32768-token document: at the threshold, gates pass
+    info = _plan(workloads.make_batch(workloads.get("long_doc_n8"))).info
+    assert info["gates_pass"] == 1
+    # the pages' worked example: cascade
+    assert _plan(workloads.make_batch(workloads.get("worked_decode"))).info["use_cascade"] == 1
+
+
+def test_worked_example_accounting_through_the_planner(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    b = workloads.make_batch(workloads.get("worked_decode"))
+    info = _plan(b).info
+    assert info["kv_tokens_noncascade"] == ex["kv_tokens_standard"]
+    assert info["kv_tokens_cascade"] == ex["kv_tokens_cascade"]
+
+
+def test_seven_requests_fail_the_gate():
+    w = workloads.Workload("seven", 7, 1024, (32, 32), (1, 1), 8, 2, 64, seed=5)
+    b = workloads.make_batch(w)
+    info = _plan(b).info
+    assert info["common_prefix_len"] == 1024 and info["gates_pass"] == 0 and info["use_cascade"] == 0
+
+
+def _meta(n=3, seq=40, q=2, stride=4):
+    bt = np.arange(n * stride, dtype=np.int32).reshape(n, stride)
+    qsl = np.arange(n + 1, dtype=np.int32) * q
+    sl = np.full(n, seq, dtype=np.int32)
+    return bt, qsl, sl
+
+
+def _try(**kw):
+    bt, qsl, sl = _meta()
+    args = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, num_pages=64,
+                kv_strides=(16 * 2 * 64, 2 * 64, 64), block_table=bt, query_start_loc=qsl, seq_lens=sl,
+                num_cus=256)
+    args.update(kw)
+    return spa.cascade_attn_plan(**args)
+
+
+def test_error_codes():
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(head_dim=96)
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(page_size=8)
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(num_q_heads=6, num_kv_heads=4)
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    bt, qsl, sl = _meta()
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(num_computed_tokens=sl - 1)          # q_len is 2, not 1
+    assert e.value.status == _lib.CA_EMETA
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(num_pages=5)                          # page ids up to 11 referenced
+    assert e.value.status == _lib.CA_EMETA
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(seq_lens=np.full(3, 80, dtype=np.int32))   # needs 5 pages, stride 4
+    assert e.value.status == _lib.CA_EMETA
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(query_start_loc=np.array([0, 2, 2, 4], dtype=np.int32))   # empty request
+    assert e.value.status == _lib.CA_EMETA
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(kv_strides=(16 * 2 * 64, 2 * 64, 60))
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    assert "stride" in _lib.load().cascade_attn_last_error().decode()
+
+
+def test_plan_partition_is_consistent():
+    for name in workloads.WORKLOADS:
+        b = workloads.make_batch(workloads.get(name))
+        for mode in ("on", "off"):
+            info = _plan(b, mode=mode).info
+            T, hq, d = b.q.shape
+            slots = info["num_partial_slots"]
+            assert info["workspace_bytes"] >= slots * T * hq * (d + 1) * 4
+            if info["use_cascade"]:
+                assert slots == info["prefix_splits"] + info["suffix_chunks"]
+                assert info["prefix_splits"] >= 1
+            assert info["suffix_chunk_tokens"] % 64 == 0

@@ -1,0 +1,95 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small batches are compared element by element over every output; the full
+workloads are compared on sampled requests (the oracle evaluates those rows
+only). Tolerances: |out - ref| <= 2e-2 + 1e-2 |ref| elementwise, |lse - ref|
+<= 1e-3. Inputs carry NaN in unused pages and in the tail slots of each
+request's last page, so any out-of-range read shows up as a non-finite output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import Workload
+from parity_util import DeviceBatch, assert_close, log, oracle_ref, rows_of, run
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    w.name: w for w in [
+        workloads.get("tiny_decode"),
+        Workload("decode_ragged", 16, 512, (33, 47), (1, 1), 32, 8, 128, seed=2001),
+        Workload("prefill_mix", 8, 256, (20, 100), (1, 20), 8, 2, 128, seed=2002),
+        # request 0 computed only 238 tokens: the cap binds (256 -> 224)
+        Workload("prefill_capped", 8, 256, (20, 100), (1, 20), 8, 2, 128, seed=2003, override=((0, 250, 12),)),
+        Workload("gqa8_outliers", 24, 1024, (1, 100), (1, 1), 16, 2, 128, seed=2004,
+                 outlier_frac=0.01, outlier_scale=8.0),
+        Workload("long_prefix_split", 8, 4096, (64, 64), (1, 1), 8, 2, 128, seed=2005),
+        Workload("many_rows", 16, 768, (24, 40), (8, 16), 16, 4, 128, seed=2006),
+        Workload("d64_gqa", 10, 320, (5, 60), (1, 4), 8, 2, 64, seed=2007),
+        Workload("single_request", 1, 0, (70, 70), (3, 3), 8, 2, 128, seed=2008),
+        Workload("fresh_prefill", 4, 0, (30, 50), (30, 50), 4, 1, 64, seed=2009),
+        Workload("partial_page_prefix", 9, 250, (10, 30), (1, 2), 4, 2, 128, seed=2010),
+        Workload("one_page_suffix", 12, 512, (1, 1), (1, 1), 8, 8, 128, seed=2011),
+    ]
+}
+
+
+def setup_module():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("mode", ["auto", "on", "off"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(name, mode):
+    log(f"[parity] {name} mode={mode}")
+    b = workloads.make_batch(SMALL[name])
+    ref_o, ref_l = oracle_ref(b)
+    out, lse, info = run(DeviceBatch(b), mode=mode)
+    log(f"  plan: cascade={info['use_cascade']} P_c={info['common_prefix_len']} "
+        f"psplit={info['prefix_splits']} schunks={info['suffix_chunks']}")
+    assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}")
+
+
+@pytest.mark.parametrize("name", ["decode_ragged", "prefill_mix", "d64_gqa"])
+def test_small_hnd_layout(name):
+    log(f"[parity] {name} HND")
+    b = workloads.make_batch(SMALL[name])
+    ref_o, ref_l = oracle_ref(b)
+    for mode in ("on", "off"):
+        out, lse, _ = run(DeviceBatch(b, layout="HND"), mode=mode)
+        assert_close(out, lse, ref_o, ref_l, what=f"{name}/HND/{mode}")
+
+
+def _sample_requests(n, seed):
+    rng = np.random.default_rng(seed)
+    pick = {0, n - 1, n // 2}
+    pick.update(int(x) for x in rng.integers(0, n, 3))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_full_size_sampled_parity(name):
+    w = workloads.get(name)
+    log(f"[parity-full] {name}")
+    b = workloads.make_batch(w)
+    reqs = _sample_requests(w.num_reqs, w.seed)
+    rows = rows_of(b, reqs)
+    ref_o, ref_l = oracle_ref(b, requests=reqs)
+    db = DeviceBatch(b)
+    outs = {}
+    for mode in ("auto", "on", "off"):
+        out, lse, info = run(db, mode=mode)
+        log(f"  {mode}: cascade={info['use_cascade']} P_c={info['common_prefix_len']} "
+            f"psplit={info['prefix_splits']} schunks={info['suffix_chunks']}")
+        assert np.isfinite(out).all() and np.isfinite(lse).all()
+        assert_close(out, lse, ref_o, ref_l, rows=rows, what=f"{name}/{mode}")
+        outs[mode] = (out, lse)
+    # cascade against the GPU non-cascade baseline, every row
+    o_on, l_on = outs["on"]
+    o_off, l_off = outs["off"]
+    assert np.all(np.abs(o_on - o_off) <= 2e-2 + 1e-2 * np.abs(o_off))
+    assert np.abs(l_on - l_off).max() <= 1e-3
