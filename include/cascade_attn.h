@@ -99,6 +99,10 @@ typedef struct {
   int32_t suffix_chunk_tokens;         /* tokens per chunk */
   int32_t suffix_kernel;               /* 0 = tiled kernel, 1 = decode kernel */
   int32_t num_partial_slots;           /* fp32 partial states per (token, head) */
+  int32_t prefix_stages;               /* LDS pipeline depth of the prefix kernel */
+  int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
+  int32_t merge_in_suffix;             /* 1: the suffix kernel merges and writes the output */
+  int32_t reserved0;
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
   int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */

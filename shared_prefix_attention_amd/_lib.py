@@ -60,6 +60,10 @@ class ca_plan_info_t(ctypes.Structure):
         ("suffix_chunk_tokens", ctypes.c_int32),
         ("suffix_kernel", ctypes.c_int32),
         ("num_partial_slots", ctypes.c_int32),
+        ("prefix_stages", ctypes.c_int32),
+        ("suffix_stages", ctypes.c_int32),
+        ("merge_in_suffix", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("kv_tokens_cascade", ctypes.c_int64),

@@ -4,24 +4,37 @@
 //     packed as one sequence, times the query heads of one KV head) attends
 //     non-causally to the shared-prefix pages (block-table row 0);
 //   * the suffix phase: each request's rows attend causally to its own KV
-//     range [key_start, seq_len) through its block-table row;
+//     range [key_start, seq_len) through its block-table row, and -- when the
+//     request's suffix is one work item -- merges the prefix phase's partial
+//     states into its own and writes the final output;
 //   * the non-cascade path: the suffix phase with key_start = 0.
 // ("vLLM Cascade Attention：用法、场景与原理解析", beaiera.top, section 8
-// Step 5, phases 1 and 2; section 4 for which keys each query sees.)
+// Step 5: prefix phase, suffix phase, LSE merge; section 4 for which keys
+// each query sees.)
 //
-// Work-group: 4 wave64s. A work-group owns one (KV head, row tile, KV split)
-// item; its K/V range is staged through LDS 64 keys (4 pages) at a time,
-// double buffered, and every wave computes 16*RB rows against each tile:
-//   S^T[key][row] = K Q^T   (v_mfma_f32_16x16x32_bf16, A = K from LDS,
-//                            B = Q^T held in registers)
+// Work-group: RW * KG wave64s owning one (KV head, row tile, KV range) item.
+// K/V are streamed 64 keys (4 pages) per stage straight from HBM into LDS
+// with global_load_lds_dwordx4 (no register staging), NS stages in flight.
+// Each LDS row (one key, d contiguous) has its 16-byte chunks XOR-swizzled
+// by the key index so the MFMA operand reads are bank-conflict free.
+// Wave (rw, kg) owns query rows [rw*16*RB, +16*RB) of the tile and keys
+// [kg*64/KG, +64/KG) of every stage, with its own online-softmax state; the
+// KG states of a row block are merged through LDS at the end. Per wave and
+// stage:
+//   S^T[key][row] = K Q^T   (v_mfma_f32_16x16x32_bf16: A = K from LDS,
+//                            B = Q^T kept in registers)
 //   online softmax on S^T (exp2 domain, fp32), P^T rounded to bf16
-//   O^T[d][row] += V^T P^T (v_mfma_f32_16x16x32_bf16, A = V^T from a
-//                            transposed LDS tile, B = P^T straight from the
-//                            S^T accumulators)
-// Computing the transposed products keeps P in the lane layout the second
-// product needs, so no cross-lane shuffle of P is required. K/V positions
-// outside the item's range are never read: their LDS slots are zero-filled
-// and their scores masked, so NaN in unused pages or tail slots cannot leak.
+//   O^T[d][row] += V^T P^T (A = V^T read with the LDS transpose load
+//                            ds_read_b64_tr_b16, B = P^T taken straight from
+//                            the S^T accumulators; 16x16x32 MFMA for 32-key
+//                            groups, 16x16x16 for 16-key groups)
+// Computing the transposed products leaves P in the lane layout the second
+// product needs, so P never moves between lanes.
+//
+// Masking: positions past the item's range are loaded from the item's last
+// valid position (so no unused page or NaN tail slot is ever read) and their
+// scores are set to -inf; causally hidden positions likewise. Stages that
+// need no mask skip it.
 #pragma once
 
 #include "device_common.hpp"
@@ -46,46 +59,134 @@ struct TileArgs {
   int32_t num_reqs;
   int32_t mtiles;               // row tiles (prefix) / max row tiles per request
   int32_t splits;               // KV splits (prefix) / chunks per request
-  int32_t split_tokens;         // multiple of 64
+  int32_t split_tokens;         // multiple of 64, <= kMaxItemPages * 16
   float* part_o;                // [slots][T][hq][D] fp32 (partial mode)
   float* part_lse;              // [slots][T][hq] fp32, natural log
   int32_t slot_base;
   int64_t slot_elems;           // T * hq * D
   int64_t slot_rows;            // T * hq
-  uint16_t* out;                // [T][hq][D] bf16 (direct mode)
-  float* lse_out;               // [T][hq] (direct mode, may be null)
-  int32_t direct;
+  uint16_t* out;                // [T][hq][D] bf16 (direct / merge mode)
+  float* lse_out;               // [T][hq] (may be null)
+  int32_t direct;               // write the final output (no partial)
+  int32_t merge_slots;          // direct mode: prefix partial slots [0, merge_slots) to fold in
 };
 
-template <int D>
+constexpr int kMaxItemPages = 512;
+// Prefix partial slots the suffix kernel loads per batch when it merges.
+constexpr int kMergeBatch = 2;
+
+template <int D, int NS>
 struct TileSmem {
-  static constexpr int KS = D + 8;        // K row stride (elements): 16-byte rows, spread banks
-  static constexpr int VS = 64 + 8;       // V^T row stride (elements)
-  static constexpr int K_ELEMS = 64 * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * BUF * 2;
+  static constexpr int TILE_BYTES = 64 * D * 2;            // one of K or V, one stage
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int BYTES = NS * STAGE_BYTES + kMaxItemPages * 4;
 };
 
-template <int D, int RB>
-__global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
+// 16-byte chunk swizzle of key row `key`: conflict-free 16-lane reads of one
+// chunk column across 16 consecutive keys (rows are D*2 bytes apart). It
+// depends on key mod 16 only, so it is the same in every 16-key block.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+}
+
+// Waits until at most N vector-memory ops of this wave are outstanding
+// (expcnt / lgkmcnt left unconstrained). gfx9 s_waitcnt encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+__device__ __forceinline__ u32x4_t lds_load16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)addr;
+}
+
+// ds_read_b64_tr_b16 through inline asm: the builtin form makes the compiler
+// wait for every in-flight LDS DMA before it (vmcnt 0). The compiler does not
+// track this read, so its result must pass through lds_wait_regs() before use.
+// Within each 16-lane group, lane 4*j + c supplies the address of row j,
+// columns [4c, 4c+4) of a 4 x 16 block of 16-bit values; lane i receives
+// column i of the four rows.
+__device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// Waits for this wave's LDS reads and makes the registers that received them
+// outputs of the wait, so no consumer can be scheduled above it.
+template <int N>
+__device__ __forceinline__ void lds_wait_regs(u32x4_t (&r)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8, "register batch");
+  if constexpr (N == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1])::"memory");
+  } else if constexpr (N == 4) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])::"memory");
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+                 :: "memory");
+  }
+}
+__device__ __forceinline__ void lds_wait_regs(u32x2_t (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])::"memory");
+}
+
+// Work-group barrier without the memory fences of __syncthreads() (which
+// would wait for every in-flight LDS DMA): this wave's LDS reads are retired
+// first (lgkmcnt 0); DMA completion is waited for explicitly by the caller.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
+}
+
+template <int D, int RB, int RW, int KG, int NS>
+__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a) {
+  constexpr int W = RW * KG;              // waves per work-group
+  constexpr int NT = 64 * W;              // threads
+  constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
   constexpr int KC = D / 32;              // 32-wide d chunks per QK^T MFMA chain
   constexpr int DB = D / 16;              // 16-wide d blocks of the output
-  constexpr int KCH = D / 8;              // 16-byte chunks per K/V row
-  constexpr int K_LOADS = 64 * KCH / 256; // per thread per tile
-  constexpr int V_ITEMS = 16 * KCH;       // (key quad, d chunk) pairs per tile
-  constexpr int V_LOADS = (V_ITEMS + 255) / 256;
-  using SM = TileSmem<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::BUF];
+  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  constexpr int KPB = 64 / CPR;           // keys per 1 KB DMA block
+  constexpr int BLK = 64 / KPB;           // 1 KB DMA blocks per tile (K or V)
+  static_assert(BLK % W == 0, "DMA blocks must divide among the waves");
+  constexpr int BLK_PER_WAVE = BLK / W;
+  constexpr int OPS = 2 * BLK_PER_WAVE;   // vector-memory ops per wave per stage
+  constexpr int NKB = 4 / KG;             // 16-key blocks per wave per stage
+  constexpr int ROWB = D * 2;             // LDS bytes per key row
+  constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
+  using SM = TileSmem<D, NS>;
+  static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= NS * SM::STAGE_BYTES, "merge scratch");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SM::BYTES];
+  int32_t* s_pages = reinterpret_cast<int32_t*>(smem + NS * SM::STAGE_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int rw = wave % RW;
+  const int kg = wave / RW;
   const int lr = lane & 15;
   const int lq = lane >> 4;
 
   // ---------------------------------------------------------- item decode
-  int g, row_begin, row_end, key_begin, key_end, slot, req = 0;
+  int g, row_begin, row_end, key_begin, key_end, slot;
   int tok_base = 0, q_pos_base = 0;      // token of row 0, causal position of row 0's token
   bool causal;
   const int32_t* bt_row;
@@ -97,8 +198,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
       const int kvi = bid - mt * kv_items;
       g = kvi / a.splits;
       const int s = kvi - g * a.splits;
-      row_begin = mt * 64 * RB;
-      row_end = min(row_begin + 64 * RB, a.total_rows);
+      row_begin = mt * ROWS;
+      row_end = min(row_begin + ROWS, a.total_rows);
       key_begin = s * a.split_tokens;
       key_end = min(key_begin + a.split_tokens, a.prefix_len);
       slot = a.slot_base + s;
@@ -110,12 +211,12 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
       const int mt = rest % a.mtiles;
       rest /= a.mtiles;
       g = rest % a.hkv;
-      req = rest / a.hkv;
+      const int req = rest / a.hkv;
       const int q0 = a.qsl[req];
       const int q_len = a.qsl[req + 1] - q0;
       const int seq_len = a.seq_lens[req];
-      row_begin = mt * 64 * RB;
-      row_end = min(row_begin + 64 * RB, q_len * a.group);
+      row_begin = mt * ROWS;
+      row_end = min(row_begin + ROWS, q_len * a.group);
       if (row_begin >= row_end) return;   // uniform across the work-group
       key_begin = a.key_start + c * a.split_tokens;
       key_end = min(key_begin + a.split_tokens, seq_len);
@@ -128,9 +229,12 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
     }
   }
   const int n_tiles = (key_end - key_begin + 63) >> 6;
+  const int first_page = key_begin >> 4;
+  // keys at or below this position are visible to every row of the item
+  const int all_visible_to = causal ? q_pos_base + row_begin / a.group : 0x7fffffff;
 
   // ------------------------------------------------- per-lane query rows
-  const int wrow0 = row_begin + wave * 16 * RB;
+  const int wrow0 = row_begin + rw * 16 * RB;
   const bool wave_active = wrow0 < row_end;
   u32x4_t qf[RB][KC];
   int row_tok[RB], row_head[RB], row_qpos[RB];
@@ -139,9 +243,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
   for (int rb = 0; rb < RB; ++rb) {
     const int m = wrow0 + rb * 16 + lr;
     row_ok[rb] = m < row_end;
-    const int mt = a.prefix_mode ? m : m;            // packed row index within the item space
-    const int t_in = mt / a.group;
-    const int j = mt - t_in * a.group;
+    const int t_in = m / a.group;
+    const int j = m - t_in * a.group;
     row_tok[rb] = tok_base + t_in;
     row_head[rb] = g * a.group + j;
     row_qpos[rb] = q_pos_base + t_in;
@@ -154,6 +257,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
       }
     }
   }
+  // the item's page ids, once, into LDS
+  const int n_pages = n_tiles > 0 ? ((key_end + 15) >> 4) - first_page : 0;
+  for (int i = tid; i < n_pages; i += NT) s_pages[i] = bt_row[first_page + i];
+  __syncthreads();   // also retires the Q loads before the DMA pipeline starts
 
   f32x4_t o[DB][RB];
 #pragma unroll
@@ -167,152 +274,205 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
     l_run[rb] = 0.f;
   }
 
-  // ------------------------------------------------ global -> register stage
-  u32x4_t kreg[K_LOADS];
-  u32x4_t vreg[V_LOADS][4];
+  // Lane-constant parts of the LDS operand addresses (the XOR swizzle
+  // depends on key mod 16 only, so 16-key blocks differ by a constant).
+  const uint32_t smem_base = lds_addr(smem);
+  uint32_t k_off[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * ROWB + (((kc * 4 + lq) ^ chunk_swz<D>(lr)) * 16);
+  const int tr_row = 4 * lq + (lr >> 2);   // key within a 16-key block for the transpose read
+  uint32_t v_off[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int d0 = db * 16 + 4 * (lr & 3);
+    v_off[db] = tr_row * ROWB + (((d0 >> 3) ^ chunk_swz<D>(tr_row)) * 16) + (d0 & 7) * 2;
+  }
+
   const int64_t head_off = (int64_t)g * a.sh;
-
-  auto load_tile = [&](int t) {
+  // DMA one stage: this wave moves BLK_PER_WAVE 1 KB blocks of K and of V.
+  // Lane l of a block writes LDS bytes [16 l, 16 l + 16) = (key, chunk
+  // column) of the swizzled layout; it loads the matching source chunk.
+  auto issue_stage = [&](int t) {
+    uint8_t* sK = smem + (t % NS) * SM::STAGE_BYTES;
+    uint8_t* sV = sK + SM::TILE_BYTES;
     const int kt0 = key_begin + t * 64;
-    int pg[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) pg[kb] = (kt0 + kb * 16 < key_end) ? bt_row[(kt0 >> 4) + kb] : 0;
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / KCH;
-      const int dc = c - key * KCH;
-      const int pos = kt0 + key;
-      if (pos < key_end) {
-        kreg[i] = load16(a.k + (int64_t)pg[key >> 4] * a.sp + (int64_t)(pos & 15) * a.st + head_off + dc * 8);
-      } else {
-        kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int kq = c / KCH;
-      const int dc = c - kq * KCH;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = kq * 4 + kk;
-        const int pos = kt0 + key;
-        if (c < V_ITEMS && pos < key_end) {
-          vreg[i][kk] = load16(a.v + (int64_t)pg[key >> 4] * a.sp + (int64_t)(pos & 15) * a.st + head_off + dc * 8);
-        } else {
-          vreg[i][kk] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
+    for (int i = 0; i < BLK_PER_WAVE; ++i) {
+      const int blk = wave * BLK_PER_WAVE + i;
+      const int key = blk * KPB + lane / CPR;
+      const int col = lane % CPR;
+      const int dc = col ^ chunk_swz<D>(key);
+      const int pos = min(kt0 + key, key_end - 1);
+      const int page = s_pages[(pos >> 4) - first_page];
+      const int64_t off = (int64_t)page * a.sp + (int64_t)(pos & 15) * a.st + head_off + dc * 8;
+      lds_dma16(a.k + off, sK + blk * 1024);
+      lds_dma16(a.v + off, sV + blk * 1024);
     }
   };
-
-  auto store_tile = [&](int buf) {
-    uint16_t* sK = smem + buf * SM::BUF;
-    uint16_t* sV = sK + SM::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / KCH;
-      const int dc = c - key * KCH;
-      *reinterpret_cast<u32x4_t*>(sK + key * SM::KS + dc * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int c = tid + 256 * i;
-      if (c < V_ITEMS) {
-        const int kq = c / KCH;
-        const int dc = c - kq * KCH;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const int sh = (e & 1) * 16;
-          const uint32_t x0 = (vreg[i][0][w] >> sh) & 0xffffu;
-          const uint32_t x1 = (vreg[i][1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (vreg[i][2][w] >> sh) & 0xffffu;
-          const uint32_t x3 = (vreg[i][3][w] >> sh) & 0xffffu;
-          *reinterpret_cast<u32x2_t*>(sV + (dc * 8 + e) * SM::VS + kq * 4) = u32x2_t{x0 | (x1 << 16), x2 | (x3 << 16)};
-        }
-      }
-    }
+  auto wait_stage = [&](int after) {   // `after` stages were issued after the one needed
+    if (NS >= 4 && after >= 2) wait_vmcnt<2 * OPS>();
+    else if (NS >= 3 && after >= 1) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
   };
 
-  if (n_tiles > 0) load_tile(0);
+  const int pro = min(NS - 1, n_tiles);
+  for (int t = 0; t < pro; ++t) issue_stage(t);
+
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    wait_stage(min(NS - 2, n_tiles - 1 - t));
+    block_barrier();
+    if (t + NS - 1 < n_tiles) issue_stage(t + NS - 1);
     if (wave_active) {
-      const uint16_t* sK = smem + buf * SM::BUF;
-      const uint16_t* sV = sK + SM::K_ELEMS;
-      const int kt0 = key_begin + t * 64;
-      // S^T = K Q^T for 4 blocks of 16 keys
-      f32x4_t s[4][RB];
+      const uint32_t stage = smem_base + (t % NS) * SM::STAGE_BYTES;
+      const uint32_t sK = stage + kg * NKB * 16 * ROWB;
+      const uint32_t sV = stage + SM::TILE_BYTES + kg * NKB * 16 * ROWB;
+      const int kt0 = key_begin + t * 64 + kg * NKB * 16;   // first key of this wave's group
+      // S^T = K Q^T for NKB blocks of 16 keys
+      f32x4_t s[NKB][RB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sK + (kb * 16 + lr) * SM::KS + kc * 32 + lq * 8);
+          const u32x4_t kf = lds_load16(sK + kb * 16 * ROWB + k_off[kc]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) s[kb][rb] = mfma16x16x32(kf, qf[rb][kc], s[kb][rb]);
         }
       }
-      // online softmax over this tile's 64 keys, per row (lane lr)
-      u32x4_t pb[RB][2];
+      // online softmax over this wave's keys of the stage, per row (lane lr)
+      const bool need_mask = (kt0 + NKB * 16 > key_end) || (kt0 + NKB * 16 - 1 > all_visible_to);
+      u32x2_t pb[RB][NKB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float x[4][4];
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kpos = kt0 + kb * 16 + lq * 4 + i;
+              const bool vis = kpos < key_end && (!causal || kpos <= row_qpos[rb]);
+              s[kb][rb][i] = vis ? s[kb][rb][i] : -INFINITY;
+            }
+        }
         float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kpos = kt0 + kb * 16 + lq * 4 + i;
-            const bool vis = kpos < key_end && (!causal || kpos <= row_qpos[rb]);
-            x[kb][i] = vis ? s[kb][rb][i] * a.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, x[kb][i]);
-          }
-        tmax = wave_max_across_quads(tmax);
+        for (int kb = 0; kb < NKB; ++kb)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb][rb][0], s[kb][rb][1]), fmaxf(s[kb][rb][2], s[kb][rb][3])));
+        tmax = wave_max_across_quads(tmax) * a.scale_log2;
         const float m_new = fmaxf(m_run[rb], tmax);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run[rb] - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
         float psum = 0.f;
-        float p[4][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+          float p[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[kb][i] = exp2f(x[kb][i] - m_use);
-            psum += p[kb][i];
+            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][rb][i], a.scale_log2, -m_use));
+            psum += p[i];
           }
+          pb[rb][kb] = u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        }
         l_run[rb] = l_run[rb] * alpha + psum;
         m_run[rb] = m_new;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
+      }
+      // O^T += V^T P^T. The transpose load gives lane lr of group lq, for
+      // keys kb*16 + 4*lq + (0..3), the values at d = db*16 + lr.
+      if constexpr (NKB == 1) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          pb[rb][kk] = u32x4_t{pack_bf16x2(p[2 * kk][0], p[2 * kk][1]), pack_bf16x2(p[2 * kk][2], p[2 * kk][3]),
-                               pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]),
-                               pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3])};
+        for (int dh = 0; dh < DB / 4; ++dh) {
+          u32x2_t vr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vr[i] = lds_read_tr16(sV + v_off[dh * 4 + i]);
+          lds_wait_regs(vr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) o[dh * 4 + i][rb] = mfma16x16x16(vr[i], pb[rb][0], o[dh * 4 + i][rb]);
+        }
+      } else {
+        // 32 keys per MFMA: k-slot (lq, j) <-> key kk*32 + (j < 4 ? 4*lq + j
+        // : 16 + 4*lq + j - 4), the map the S^T accumulators give P^T.
+        constexpr int NKK = NKB / 2;
+        constexpr int DBH = DB / 2;
+#pragma unroll
+        for (int dh = 0; dh < 2; ++dh) {
+          u32x4_t vf[DBH * NKK];
+#pragma unroll
+          for (int dbi = 0; dbi < DBH; ++dbi) {
+            const uint32_t va = sV + v_off[dh * DBH + dbi];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+              const u32x2_t h0 = lds_read_tr16(va + kk * 32 * ROWB);
+              const u32x2_t h1 = lds_read_tr16(va + (kk * 32 + 16) * ROWB);
+              vf[dbi * NKK + kk] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+            }
+          }
+          lds_wait_regs(vf);
+#pragma unroll
+          for (int dbi = 0; dbi < DBH; ++dbi)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) {
+                const u32x4_t pk = u32x4_t{pb[rb][2 * kk][0], pb[rb][2 * kk][1], pb[rb][2 * kk + 1][0],
+                                           pb[rb][2 * kk + 1][1]};
+                o[dh * DBH + dbi][rb] = mfma16x16x32(vf[dbi * NKK + kk], pk, o[dh * DBH + dbi][rb]);
+              }
         }
       }
-      // O^T += V^T P^T, 32 keys per MFMA: k-slot (lq, j) <-> key
-      // kk*32 + (j < 4 ? 4*lq + j : 16 + 4*lq + j - 4), the same map the
-      // S^T accumulators give P^T.
+    }
+  }
+
+  // ------------------------------------------- combine the key groups
+  // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). Waves
+  // kg > 0 publish theirs in LDS; wave kg = 0 of each row block folds them in.
+  // The stage buffers are free once every wave is past the loop.
+  if constexpr (KG > 1) {
+    constexpr int SLOT_F = 16 * RB * XS_ROW;   // floats per published wave state
+    float* xs = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    if (kg > 0 && wave_active) {
+      float* my = xs + ((kg - 1) * RW + rw) * SLOT_F;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int rb = 0; rb < RB; ++rb) {
+        float* r = my + (rb * 16 + lr) * XS_ROW;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const uint16_t* vrow = sV + (db * 16 + lr) * SM::VS + kk * 32 + lq * 4;
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-          const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16x16x32(vf, pb[rb][kk], o[db][rb]);
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(r + db * 16 + lq * 4) = o[db][rb];
+        const float l_tot = wave_sum_across_quads(l_run[rb]);
+        if (lq == 0) {
+          r[D] = m_run[rb];
+          r[D + 1] = l_tot;
         }
+      }
+    }
+    __syncthreads();
+    if (kg > 0) return;
+    if (wave_active) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float l_tot = wave_sum_across_quads(l_run[rb]);
+        float m = m_run[rb];
+#pragma unroll
+        for (int k2 = 1; k2 < KG; ++k2) {
+          const float* r = xs + ((k2 - 1) * RW + rw) * SLOT_F + (rb * 16 + lr) * XS_ROW;
+          const float m2 = r[D], l2 = r[D + 1];
+          const float mn = fmaxf(m, m2);
+          const float mu = (mn == -INFINITY) ? 0.f : mn;
+          const float a1 = __builtin_amdgcn_exp2f(m - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            o[db][rb] = o[db][rb] * a1 + *reinterpret_cast<const f32x4_t*>(r + db * 16 + lq * 4) * a2;
+          l_tot = l_tot * a1 + l2 * a2;
+          m = mn;
+        }
+        m_run[rb] = m;
+        // the combined sum sits in lane group 0 so the epilogue's quad sum
+        // reproduces it
+        l_run[rb] = (lq == 0) ? l_tot : 0.f;
       }
     }
   }
@@ -324,16 +484,41 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const TileArgs a) {
     const float l_tot = wave_sum_across_quads(l_run[rb]);
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
-    const float lse = live ? (m_run[rb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (!row_ok[rb]) continue;
     const int64_t row = (int64_t)row_tok[rb] * a.hq + row_head[rb];
     if (a.direct) {
+      f32x4_t acc[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4_t v = o[db][rb] * inv;
-        *reinterpret_cast<u32x2_t*>(a.out + row * D + db * 16 + lq * 4) =
-            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int db = 0; db < DB; ++db) acc[db] = o[db][rb] * inv;
+      if (a.merge_slots > 0) {
+        // LSE merge of this state with the prefix phase's partial states of
+        // the same row (online form). The loads of a batch of slots are all
+        // issued before the first use: one memory round trip per batch.
+        float m = lse, wsum = live ? 1.f : 0.f;
+        for (int s0 = 0; s0 < a.merge_slots; s0 += kMergeBatch) {
+          float ls[kMergeBatch];
+          f32x4_t po[kMergeBatch][DB];
+#pragma unroll
+          for (int k = 0; k < kMergeBatch; ++k) {
+            const int sl = min(s0 + k, a.merge_slots - 1);
+            ls[k] = (s0 + k < a.merge_slots) ? a.part_lse[(int64_t)sl * a.slot_rows + row] : -INFINITY;
+            const float* src = a.part_o + (int64_t)sl * a.slot_elems + row * D + lq * 4;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) po[k][db] = *reinterpret_cast<const f32x4_t*>(src + db * 16);
+          }
+#pragma unroll
+          for (int k = 0; k < kMergeBatch; ++k) merge_step(m, wsum, acc, ls[k], po[k]);
+        }
+        const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= winv;
+        lse = wsum > 0.f ? m + logf(wsum) : -INFINITY;
       }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<u32x2_t*>(a.out + row * D + db * 16 + lq * 4) =
+            u32x2_t{pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
       if (lq == 0 && a.lse_out) a.lse_out[row] = lse;
     } else {
       float* dst = a.part_o + (int64_t)slot * a.slot_elems + row * D;

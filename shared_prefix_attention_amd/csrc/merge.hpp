@@ -30,24 +30,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   if (row >= a.rows) return;
-  float big = -INFINITY;
-  for (int s = 0; s < a.slots; ++s) big = fmaxf(big, a.part_lse[(int64_t)s * a.rows + row]);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (big != -INFINITY) {
-    for (int s = 0; s < a.slots; ++s) {
-      const float l = a.part_lse[(int64_t)s * a.rows + row];
-      if (l == -INFINITY) continue;
-      const float w = exp2f((l - big) * kLog2e);
-      wsum += w;
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.part_o + (int64_t)s * a.slot_elems + row * D + part * 4);
-      acc += w * x;
+  // Online merge over slots in batches whose loads (LSE and o, the latter
+  // unconditionally: every slot is in bounds) are all issued before the first
+  // use, so a row costs one memory round trip per batch.
+  constexpr int B = 8;
+  float m = -INFINITY, wsum = 0.f;
+  f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < a.slots; s0 += B) {
+    float l[B];
+    f32x4_t x[B][1];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int sl = min(s0 + k, a.slots - 1);
+      l[k] = (s0 + k < a.slots) ? a.part_lse[(int64_t)sl * a.rows + row] : -INFINITY;
+      x[k][0] = *reinterpret_cast<const f32x4_t*>(a.part_o + (int64_t)sl * a.slot_elems + row * D + part * 4);
     }
+#pragma unroll
+    for (int k = 0; k < B; ++k) merge_step(m, wsum, acc, l[k], x[k]);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  acc *= inv;
-  *reinterpret_cast<u32x2_t*>(a.out + row * D + part * 4) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-  if (part == 0 && a.lse_out) a.lse_out[row] = wsum > 0.f ? big + logf(wsum) : -INFINITY;
+  const f32x4_t r = acc[0] * inv;
+  *reinterpret_cast<u32x2_t*>(a.out + row * D + part * 4) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  if (part == 0 && a.lse_out) a.lse_out[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
 }  // namespace ca

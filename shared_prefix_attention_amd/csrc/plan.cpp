@@ -54,60 +54,96 @@ static int32_t count_common_blocks(const int32_t* bt, int32_t n, int32_t stride,
 // family ([p4] "Update Cascade Attention Heuristics for FA3"). Constants are
 // effective rates of these kernels on MI355X, not spec-sheet peaks.
 struct CostModel {
-  double hbm_bw = 4.5e12;         // bytes/s streamed from HBM by the attention kernels
+  double hbm_bw = 5.5e12;         // bytes/s streamed from HBM by the attention kernels
+  double cu_bw = 40.0e9;          // bytes/s one CU's work-groups pull when few CUs are busy
+  double item_latency_us = 4.0;   // fixed start / drain latency of one work item
   double mall_bw = 11.0e12;       // bytes/s for re-reads that hit L2 / Infinity Cache
   double cu_mfma = 4.0e12;        // flop/s of one CU in the tiled MFMA kernel
   double launch_us = 2.5;         // per kernel launch on one stream
   double mall_bytes = 256.0e6;    // Infinity Cache capacity
 };
 
-struct TileChoice {
-  int32_t row_blocks, mtiles, splits, split_tokens;
-  double est_us;
-};
+// Work-group shapes of the tiled kernel (all 64-key stages):
+//   kRowsConfig   64 rows (4 waves x 16), each stage split over 2 key groups
+//                 -> 8 waves; for packed prefix rows and prefill suffixes;
+//   kMfmaConfig   128 rows (4 waves x 32), one key group; when the prefix
+//                 is large enough to be bound by the MFMA rate;
+//   kDecodeConfig 16 rows (1 wave), each stage split over 4 key groups;
+//                 for suffixes whose rows (q_len * G) fit one MFMA block.
+static PhaseTile rows_config() { PhaseTile t; t.row_blocks = 1; t.row_waves = 4; t.key_groups = 2; return t; }
+static PhaseTile mfma_config() { PhaseTile t; t.row_blocks = 2; t.row_waves = 4; t.key_groups = 1; return t; }
+static PhaseTile decode_config() {
+  PhaseTile t;
+  t.row_blocks = 1;
+  t.row_waves = 1;
+  t.key_groups = 4;
+  t.kernel = 1;
+  return t;
+}
+
+// Pipeline depth: 4 stages when the grid leaves CUs with a single
+// work-group (more bytes in flight per work-group), else 2 (two work-groups
+// per CU fit in LDS).
+static int32_t pick_stages(int64_t items, int32_t cus) { return items >= 2 * (int64_t)cus ? 2 : 4; }
 
 // Prefix phase: rows = T*G packed (token, head-in-group) rows per KV head,
-// keys = the capped shared prefix.
-static TileChoice choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& cm) {
+// keys = the capped shared prefix. Chooses the KV split count.
+static PhaseTile choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& cm, double* est_us) {
   const int64_t rows = pl.total_q * pl.group;
-  const int32_t rb = rows >= 512 ? 2 : 1;
-  const int64_t bm = 64 * rb;
+  PhaseTile t = rows >= 2048 ? mfma_config() : rows_config();
+  const int64_t bm = t.rows_per_wg();
   const int64_t mtiles = cdiv(rows, bm);
   const int64_t ntiles = cdiv(pl.prefix_len, kTileKeys);
+  const int64_t max_tiles = kMaxItemTokens / kTileKeys;
   const double bpt = 4.0 * pl.hkv * pl.d;                       // K+V bytes per token
   const double part_per_split = (double)pl.total_q * pl.hq * (pl.d + 1) * 4.0;
-  TileChoice best{rb, (int32_t)mtiles, 1, (int32_t)round_up(pl.prefix_len, kTileKeys), 1e30};
+  double best = 1e30;
+  t.mtiles = (int32_t)mtiles;
+  t.splits = 1;
+  t.split_tokens = (int32_t)(ntiles * kTileKeys);
   for (int64_t s = 1; s <= ntiles; s *= 2) {
     const int64_t tiles_per = cdiv(ntiles, s);
+    if (tiles_per > max_tiles) continue;
     const int64_t splits = cdiv(ntiles, tiles_per);
     const int64_t items = mtiles * pl.hkv * splits;
+    const double active = (double)std::min<int64_t>(items, cus);
     const double item_flops = 4.0 * bm * pl.d * (double)tiles_per * kTileKeys;
-    const double rounds = std::ceil((double)items / cus);
-    const double t_mfma = rounds * item_flops / cm.cu_mfma;
-    const double bytes = bpt * pl.prefix_len + part_per_split * splits +
-                         (double)pl.total_q * pl.hq * pl.d * 2.0;
-    const double t_bytes = bytes / cm.hbm_bw;
-    const double t = std::max(t_mfma, t_bytes) * 1e6 + (part_per_split * splits / cm.mall_bw) * 1e6;
-    if (t < best.est_us) best = {rb, (int32_t)mtiles, (int32_t)splits, (int32_t)(tiles_per * kTileKeys), t};
+    const double waves_of_items = std::ceil((double)items / cus);
+    const double t_mfma = waves_of_items * item_flops / cm.cu_mfma;
+    const double hbm = bpt * pl.prefix_len + part_per_split * splits + (double)pl.total_q * pl.hq * pl.d * 2.0;
+    const double t_hbm = hbm / std::min(cm.hbm_bw, active * cm.cu_bw);
+    const double est = (std::max(t_mfma, t_hbm) + part_per_split * splits / cm.mall_bw) * 1e6 + cm.item_latency_us;
+    if (est < best) {
+      best = est;
+      t.splits = (int32_t)splits;
+      t.split_tokens = (int32_t)(tiles_per * kTileKeys);
+      t.stages = pick_stages(items, cus);
+    }
     if (splits == ntiles) break;
   }
-  return best;
+  *est_us = best;
+  return t;
 }
 
 // Suffix (or only) phase: per request r the rows are q_len_r*G and the keys
-// [key_start, seq_len_r); chunks split the keys so the grid fills the chip.
-static TileChoice choose_suffix(const ca_plan& pl, int32_t cus, bool has_merge_anyway, const CostModel& cm) {
-  const int32_t rb = 1;
-  const int64_t mt = cdiv((int64_t)pl.max_q_len * pl.group, 64 * rb);
+// [key_start, seq_len_r). `fill` asks for enough chunks per request to give
+// the grid ~2 work-groups per CU; otherwise the fewest chunks the per-item
+// token cap allows (one chunk lets the cascade suffix kernel do the merge).
+static PhaseTile choose_suffix(const ca_plan& pl, int32_t cus, bool fill) {
+  PhaseTile t = ((int64_t)pl.max_q_len * pl.group <= 16) ? decode_config() : rows_config();
+  const int64_t mt = cdiv((int64_t)pl.max_q_len * pl.group, t.rows_per_wg());
   const int64_t base = (int64_t)pl.num_reqs * mt * pl.hkv;
   const int64_t ntiles = std::max<int64_t>(1, cdiv(pl.max_suffix_len, kTileKeys));
-  const int64_t want = std::max<int64_t>(1, cdiv(2 * (int64_t)cus, base));
-  int64_t chunks = std::min(ntiles, want);
+  const int64_t max_tiles = kMaxItemTokens / kTileKeys;
+  int64_t chunks = cdiv(ntiles, max_tiles);
+  if (fill) chunks = std::max(chunks, std::min(ntiles, std::max<int64_t>(1, cdiv(2 * (int64_t)cus, base))));
   const int64_t tiles_per = cdiv(ntiles, chunks);
   chunks = cdiv(ntiles, tiles_per);
-  (void)has_merge_anyway;
-  (void)cm;
-  return {rb, (int32_t)mt, (int32_t)chunks, (int32_t)(tiles_per * kTileKeys), 0.0};
+  t.mtiles = (int32_t)mt;
+  t.splits = (int32_t)chunks;
+  t.split_tokens = (int32_t)(tiles_per * kTileKeys);
+  t.stages = pick_stages(base * chunks, cus);
+  return t;
 }
 
 // Per-request phase over KV positions [key_start, seq_len): HBM bytes for the
@@ -246,7 +282,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   // other requests when they fit in it.
   pl->key_start = 0;
   pl->max_suffix_len = max_seq;
-  TileChoice nc = choose_suffix(*pl, cus, false, cm);
+  PhaseTile nc = choose_suffix(*pl, cus, true);
   {
     const double shared_bytes = bpt * plen;
     const double reread = shared_bytes * (n - 1);
@@ -259,19 +295,20 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   }
 
   // Cascade estimate (only meaningful when something is shared).
-  TileChoice pre{1, 0, 1, 0, 0.0}, suf{1, 0, 1, 0, 0.0};
+  PhaseTile pre, suf;
+  double pre_us = 0.0;
   if (plen > 0) {
     pl->prefix_len = (int32_t)plen;
-    pre = choose_prefix(*pl, cus, cm);
+    pre = choose_prefix(*pl, cus, cm, &pre_us);
     pl->key_start = (int32_t)plen;
     pl->max_suffix_len = max_seq - (int32_t)plen;
-    suf = choose_suffix(*pl, cus, true, cm);
+    suf = choose_suffix(*pl, cus, false);
     const double t_suf = est_suffix_us(*pl, pl->kv_tokens_cascade - plen,
                                        suffix_padded_flops(*pl, qsl, seq_lens, (int32_t)plen), suf.splits, false,
                                        cus, cm, 0.0);
     const double merge_bytes = (double)(pre.splits + suf.splits) * total_q * pl->hq * (pl->d + 1) * 4.0 +
                                (double)total_q * pl->hq * pl->d * 2.0;
-    pl->est_us_cascade = (float)(pre.est_us + cm.launch_us + t_suf +
+    pl->est_us_cascade = (float)(pre_us + cm.launch_us + t_suf +
                                  (merge_bytes / cm.mall_bw) * 1e6 + cm.launch_us);
   }
 
@@ -283,15 +320,17 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (cascade) {
     pl->key_start = (int32_t)plen;
     pl->max_suffix_len = max_seq - (int32_t)plen;
-    pl->prefix = {pre.row_blocks, pre.mtiles, pre.splits, pre.split_tokens, 0};
-    pl->suffix = {suf.row_blocks, suf.mtiles, suf.splits, suf.split_tokens, 0};
-    pl->num_slots = pre.splits + suf.splits;
-    pl->direct_out = false;
+    pl->prefix = pre;
+    pl->suffix = suf;
+    pl->merge_in_suffix = suf.splits == 1 ? 1 : 0;
+    pl->num_slots = pre.splits + (pl->merge_in_suffix ? 0 : suf.splits);
+    pl->direct_out = pl->merge_in_suffix != 0;
   } else {
     pl->key_start = 0;
     pl->max_suffix_len = max_seq;
-    pl->prefix = {};
-    pl->suffix = {nc.row_blocks, nc.mtiles, nc.splits, nc.split_tokens, 0};
+    pl->prefix = PhaseTile{};
+    pl->suffix = nc;
+    pl->merge_in_suffix = 0;
     pl->num_slots = nc.splits > 1 ? nc.splits : 0;
     pl->direct_out = nc.splits == 1;
   }
@@ -317,11 +356,14 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->common_prefix_len = pl->prefix_len;
   out->gates_pass = pl->gates_pass;
   out->prefix_splits = pl->use_cascade ? pl->prefix.splits : 0;
-  out->prefix_row_tile = pl->use_cascade ? 64 * pl->prefix.row_blocks : 0;
+  out->prefix_row_tile = pl->use_cascade ? pl->prefix.rows_per_wg() : 0;
   out->suffix_chunks = pl->suffix.splits;
   out->suffix_chunk_tokens = pl->suffix.split_tokens;
   out->suffix_kernel = pl->suffix.kernel;
   out->num_partial_slots = pl->num_slots;
+  out->prefix_stages = pl->use_cascade ? pl->prefix.stages : 0;
+  out->suffix_stages = pl->suffix.stages;
+  out->merge_in_suffix = pl->merge_in_suffix;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

@@ -15,12 +15,19 @@ constexpr int kTileKeys = 64;
 constexpr int kThreads = 256;
 
 struct PhaseTile {
-  int32_t row_blocks = 1;      // 16-row MFMA blocks per wave (rows per WG = 64 * row_blocks)
+  int32_t row_blocks = 1;      // 16-row MFMA blocks per wave
+  int32_t row_waves = 4;       // waves splitting the rows (rows per WG = 16 * row_blocks * row_waves)
+  int32_t key_groups = 1;      // waves splitting each 64-key stage
   int32_t mtiles = 0;          // row tiles (prefix: of the packed rows; suffix: max per request)
   int32_t splits = 1;          // KV splits (prefix) or chunks per request (suffix)
   int32_t split_tokens = 0;    // tokens per split / chunk (multiple of kTileKeys)
-  int32_t kernel = 0;          // suffix only: 0 = tiled, 1 = decode
+  int32_t kernel = 0;          // 0 = tiled rows, 1 = decode (rows <= 16, waves split the keys)
+  int32_t stages = 2;          // LDS pipeline depth of the tiled kernel (2 or 4)
+  int32_t rows_per_wg() const { return 16 * row_blocks * row_waves; }
 };
+
+// Longest KV range one work item may cover (its page ids are held in LDS).
+constexpr int kMaxItemTokens = 512 * 16;
 
 }  // namespace ca
 
@@ -42,7 +49,8 @@ struct ca_plan {
   int32_t key_start = 0;      // first KV position of the suffix phase (prefix_len or 0)
   int32_t max_suffix_len = 0; // max over requests of seq_len - key_start
   int32_t num_slots = 0;      // fp32 partial states per (token, head)
-  bool direct_out = false;    // single-phase single-chunk run writes bf16 output directly
+  bool direct_out = false;    // the last attention launch writes the bf16 output directly
+  int32_t merge_in_suffix = 0;// cascade: the suffix kernel folds in the prefix partials
   int64_t slot_elems = 0;     // T * Hq * d
   int64_t ws_lse_offset = 0;  // byte offset of the partial LSE array
   int64_t workspace_bytes = 0;

@@ -68,18 +68,28 @@ ca_status_t check_launch(const char* what) {
   return CA_OK;
 }
 
-template <int D, int RB>
+template <int D, int RB, int RW, int KG, int NS>
 void launch_tile(const TileArgs& args, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_tile_kernel<D, RB>), dim3(grid), dim3(kThreads), 0, s, args);
+  hipLaunchKernelGGL((attn_tile_kernel<D, RB, RW, KG, NS>), dim3(grid), dim3(64 * RW * KG), 0, s, args);
+}
+
+template <int D, int RB, int RW, int KG>
+void launch_tile_ns(const TileArgs& args, int ns, int grid, hipStream_t s) {
+  if (ns == 4) launch_tile<D, RB, RW, KG, 4>(args, grid, s);
+  else launch_tile<D, RB, RW, KG, 2>(args, grid, s);
 }
 
 template <int D>
-ca_status_t run_tile(const TileArgs& args, int rb, int64_t grid, hipStream_t s, int kind) {
+ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hipStream_t s, int kind) {
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
+  if (ph.split_tokens > kMaxItemTokens || ph.split_tokens % kTileKeys)
+    return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   LaunchTimer tm(kind, s);
-  if (rb == 2) launch_tile<D, 2>(args, (int)grid, s);
-  else launch_tile<D, 1>(args, (int)grid, s);
+  if (ph.row_blocks == 1 && ph.row_waves == 4 && ph.key_groups == 2) launch_tile_ns<D, 1, 4, 2>(args, ph.stages, (int)grid, s);
+  else if (ph.row_blocks == 2 && ph.row_waves == 4 && ph.key_groups == 1) launch_tile_ns<D, 2, 4, 1>(args, ph.stages, (int)grid, s);
+  else if (ph.row_blocks == 1 && ph.row_waves == 1 && ph.key_groups == 4) launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s);
+  else return fail(CA_EINVAL, "unsupported work-group shape in plan");
   tm.done();
   return check_launch("attention kernel launch");
 }
@@ -134,7 +144,7 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     pa.split_tokens = pl->prefix.split_tokens;
     pa.slot_base = 0;
     pa.direct = 0;
-    st = run_tile<D>(pa, pl->prefix.row_blocks, (int64_t)pa.mtiles * pl->hkv * pa.splits, s, K_PREFIX);
+    st = run_tile<D>(pa, pl->prefix, (int64_t)pa.mtiles * pl->hkv * pa.splits, s, K_PREFIX);
     if (st != CA_OK) return st;
   }
   TileArgs sa = base;
@@ -145,7 +155,9 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   sa.split_tokens = pl->suffix.split_tokens;
   sa.slot_base = pl->use_cascade ? pl->prefix.splits : 0;
   sa.direct = pl->direct_out ? 1 : 0;
-  st = run_tile<D>(sa, pl->suffix.row_blocks, (int64_t)pl->num_reqs * sa.mtiles * pl->hkv * sa.splits, s, K_SUFFIX);
+  sa.merge_slots = pl->merge_in_suffix ? pl->prefix.splits : 0;
+  st = run_tile<D>(sa, pl->suffix, (int64_t)pl->num_reqs * sa.mtiles * pl->hkv * sa.splits, s,
+                   pl->suffix.kernel == 1 ? K_DECODE : K_SUFFIX);
   if (st != CA_OK) return st;
   if (!pl->direct_out) {
     MergeArgs ma{};
