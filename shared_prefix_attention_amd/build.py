@@ -27,6 +27,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR <-> VGPR copies around the softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -4,10 +4,11 @@
 //     packed as one sequence, times the query heads of one KV head) attends
 //     non-causally to the shared-prefix pages (block-table row 0);
 //   * the suffix phase: each request's rows attend causally to its own KV
-//     range [key_start, seq_len) through its block-table row, and -- when the
-//     request's suffix is one work item -- merges the prefix phase's partial
-//     states into its own and writes the final output;
-//   * the non-cascade path: the suffix phase with key_start = 0.
+//     range [key_start, seq_len) through its block-table row;
+//   * the non-cascade path: the suffix phase with key_start = 0, writing the
+//     final bf16 output directly when its KV range is one work item.
+// Both cascade phases run in one launch (cascade_phases_kernel); their
+// partial states are combined by the merge kernel.
 // ("vLLM Cascade Attention：用法、场景与原理解析", beaiera.top, section 8
 // Step 5: prefix phase, suffix phase, LSE merge; section 4 for which keys
 // each query sees.)
@@ -68,12 +69,9 @@ struct TileArgs {
   uint16_t* out;                // [T][hq][D] bf16 (direct / merge mode)
   float* lse_out;               // [T][hq] (may be null)
   int32_t direct;               // write the final output (no partial)
-  int32_t merge_slots;          // direct mode: prefix partial slots [0, merge_slots) to fold in
 };
 
 constexpr int kMaxItemPages = 512;
-// Prefix partial slots the suffix kernel loads per batch when it merges.
-constexpr int kMergeBatch = 2;
 
 template <int D, int NS>
 struct TileSmem {
@@ -82,12 +80,18 @@ struct TileSmem {
   static constexpr int BYTES = NS * STAGE_BYTES + kMaxItemPages * 4;
 };
 
-// 16-byte chunk swizzle of key row `key`: conflict-free 16-lane reads of one
-// chunk column across 16 consecutive keys (rows are D*2 bytes apart). It
-// depends on key mod 16 only, so it is the same in every 16-key block.
+// 16-byte chunk swizzles of a key row (rows are D*2 bytes apart), chosen
+// from LDS bank-conflict counts measured on gfx950. K rows are read one
+// 16-byte chunk column across 16 consecutive keys (MFMA A operand); V rows
+// by the transpose load, 8 bytes from each of 4 consecutive keys per group of
+// 4 lanes. Both depend on key mod 16 only, so they repeat every 16 keys.
 template <int D>
 __device__ __forceinline__ int chunk_swz(int key) {
   return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int chunk_swz_v(int key) {
+  return D == 128 ? ((2 * key) & 15) : ((key >> 1) & 7);
 }
 
 __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_block) {
@@ -116,9 +120,11 @@ __device__ __forceinline__ u32x4_t lds_load16(uint32_t addr) {
 // Within each 16-lane group, lane 4*j + c supplies the address of row j,
 // columns [4c, 4c+4) of a 4 x 16 block of 16-bit values; lane i receives
 // column i of the four rows.
+template <int OFF = 0>
 __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   u32x2_t r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
 
@@ -157,7 +163,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
 }
 
 template <int D, int RB, int RW, int KG, int NS>
-__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a) {
+__device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
   constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
@@ -174,7 +180,6 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
   using SM = TileSmem<D, NS>;
   static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= NS * SM::STAGE_BYTES, "merge scratch");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[SM::BYTES];
   int32_t* s_pages = reinterpret_cast<int32_t*>(smem + NS * SM::STAGE_BYTES);
 
   const int tid = threadIdx.x;
@@ -186,54 +191,72 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
   const int lq = lane >> 4;
 
   // ---------------------------------------------------------- item decode
+  // Everything that needs no memory comes from the block index. The page ids
+  // of the item's KV range are fetched speculatively (the block-table row is
+  // known before the lengths are) in the same round trip as the per-request
+  // lengths; entries past the request's pages are read but never used.
   int g, row_begin, row_end, key_begin, key_end, slot;
   int tok_base = 0, q_pos_base = 0;      // token of row 0, causal position of row 0's token
   bool causal;
   const int32_t* bt_row;
-  {
-    const int bid = blockIdx.x;
-    if (a.prefix_mode) {
-      const int kv_items = a.hkv * a.splits;
-      const int mt = bid / kv_items;
-      const int kvi = bid - mt * kv_items;
-      g = kvi / a.splits;
-      const int s = kvi - g * a.splits;
-      row_begin = mt * ROWS;
-      row_end = min(row_begin + ROWS, a.total_rows);
-      key_begin = s * a.split_tokens;
-      key_end = min(key_begin + a.split_tokens, a.prefix_len);
-      slot = a.slot_base + s;
-      causal = false;
-      bt_row = a.bt;
-    } else {
-      const int c = bid % a.splits;
-      int rest = bid / a.splits;
-      const int mt = rest % a.mtiles;
-      rest /= a.mtiles;
-      g = rest % a.hkv;
-      const int req = rest / a.hkv;
-      const int q0 = a.qsl[req];
-      const int q_len = a.qsl[req + 1] - q0;
-      const int seq_len = a.seq_lens[req];
-      row_begin = mt * ROWS;
-      row_end = min(row_begin + ROWS, q_len * a.group);
-      if (row_begin >= row_end) return;   // uniform across the work-group
-      key_begin = a.key_start + c * a.split_tokens;
-      key_end = min(key_begin + a.split_tokens, seq_len);
-      if (key_end < key_begin) key_end = key_begin;
-      slot = a.slot_base + c;
-      causal = true;
-      tok_base = q0;
-      q_pos_base = seq_len - q_len;          // num_computed_tokens
-      bt_row = a.bt + (int64_t)req * a.bt_stride;
-    }
+  int req = 0, c = 0, mt = 0;
+  if (a.prefix_mode) {
+    const int kv_items = a.hkv * a.splits;
+    mt = bid / kv_items;
+    const int kvi = bid - mt * kv_items;
+    g = kvi / a.splits;
+    c = kvi - g * a.splits;
+    key_begin = c * a.split_tokens;
+    causal = false;
+    bt_row = a.bt;
+  } else {
+    c = bid % a.splits;
+    int rest = bid / a.splits;
+    mt = rest % a.mtiles;
+    rest /= a.mtiles;
+    g = rest % a.hkv;
+    req = rest / a.hkv;
+    key_begin = a.key_start + c * a.split_tokens;
+    causal = true;
+    bt_row = a.bt + (int64_t)req * a.bt_stride;
+  }
+  const int first_page = key_begin >> 4;
+  constexpr int PG_PER_THREAD = (kMaxItemPages + NT - 1) / NT;
+  int pg_reg[PG_PER_THREAD];
+  const int item_pages = a.split_tokens >> 4;
+#pragma unroll
+  for (int k = 0; k < PG_PER_THREAD; ++k) {
+    const int i = tid + k * NT;
+    pg_reg[k] = i < item_pages ? bt_row[min(first_page + i, a.bt_stride - 1)] : 0;
+  }
+  row_begin = mt * ROWS;
+  slot = a.slot_base + c;
+  if (a.prefix_mode) {
+    row_end = min(row_begin + ROWS, a.total_rows);
+    key_end = min(key_begin + a.split_tokens, a.prefix_len);
+  } else {
+    const int q0 = a.qsl[req];
+    const int q_len = a.qsl[req + 1] - q0;
+    const int seq_len = a.seq_lens[req];
+    row_end = min(row_begin + ROWS, q_len * a.group);
+    if (row_begin >= row_end) return;   // uniform across the work-group
+    key_end = max(key_begin, min(key_begin + a.split_tokens, seq_len));
+    tok_base = q0;
+    q_pos_base = seq_len - q_len;        // num_computed_tokens
   }
   const int n_tiles = (key_end - key_begin + 63) >> 6;
-  const int first_page = key_begin >> 4;
   // keys at or below this position are visible to every row of the item
   const int all_visible_to = causal ? q_pos_base + row_begin / a.group : 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < PG_PER_THREAD; ++k) {
+    const int i = tid + k * NT;
+    if (i < item_pages) s_pages[i] = pg_reg[k];
+  }
+  __syncthreads();
 
   // ------------------------------------------------- per-lane query rows
+  // Loaded before the K/V stages are issued, so waiting for the first stage
+  // also waits for Q.
   const int wrow0 = row_begin + rw * 16 * RB;
   const bool wave_active = wrow0 < row_end;
   u32x4_t qf[RB][KC];
@@ -257,10 +280,6 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
       }
     }
   }
-  // the item's page ids, once, into LDS
-  const int n_pages = n_tiles > 0 ? ((key_end + 15) >> 4) - first_page : 0;
-  for (int i = tid; i < n_pages; i += NT) s_pages[i] = bt_row[first_page + i];
-  __syncthreads();   // also retires the Q loads before the DMA pipeline starts
 
   f32x4_t o[DB][RB];
 #pragma unroll
@@ -285,13 +304,25 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int d0 = db * 16 + 4 * (lr & 3);
-    v_off[db] = tr_row * ROWB + (((d0 >> 3) ^ chunk_swz<D>(tr_row)) * 16) + (d0 & 7) * 2;
+    v_off[db] = tr_row * ROWB + (((d0 >> 3) ^ chunk_swz_v<D>(tr_row)) * 16) + (d0 & 7) * 2;
   }
 
   const int64_t head_off = (int64_t)g * a.sh;
   // DMA one stage: this wave moves BLK_PER_WAVE 1 KB blocks of K and of V.
   // Lane l of a block writes LDS bytes [16 l, 16 l + 16) = (key, chunk
-  // column) of the swizzled layout; it loads the matching source chunk.
+  // column) of the swizzled layout; it loads the matching source chunk. The
+  // key-slot / chunk part of each source offset is the same every stage.
+  int dma_key[BLK_PER_WAVE];
+  int64_t dma_koff[BLK_PER_WAVE], dma_voff[BLK_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < BLK_PER_WAVE; ++i) {
+    const int blk = wave * BLK_PER_WAVE + i;
+    const int key = blk * KPB + lane / CPR;
+    const int col = lane % CPR;
+    dma_key[i] = key;
+    dma_koff[i] = (int64_t)(key & 15) * a.st + head_off + (col ^ chunk_swz<D>(key)) * 8;
+    dma_voff[i] = (int64_t)(key & 15) * a.st + head_off + (col ^ chunk_swz_v<D>(key)) * 8;
+  }
   auto issue_stage = [&](int t) {
     uint8_t* sK = smem + (t % NS) * SM::STAGE_BYTES;
     uint8_t* sV = sK + SM::TILE_BYTES;
@@ -299,29 +330,38 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
 #pragma unroll
     for (int i = 0; i < BLK_PER_WAVE; ++i) {
       const int blk = wave * BLK_PER_WAVE + i;
-      const int key = blk * KPB + lane / CPR;
-      const int col = lane % CPR;
-      const int dc = col ^ chunk_swz<D>(key);
-      const int pos = min(kt0 + key, key_end - 1);
-      const int page = s_pages[(pos >> 4) - first_page];
-      const int64_t off = (int64_t)page * a.sp + (int64_t)(pos & 15) * a.st + head_off + dc * 8;
-      lds_dma16(a.k + off, sK + blk * 1024);
-      lds_dma16(a.v + off, sV + blk * 1024);
+      const int key = dma_key[i];
+      int pos = kt0 + key;
+      int64_t koff = dma_koff[i], voff = dma_voff[i];
+      if (pos >= key_end) {   // past the item: re-read its last position
+        pos = key_end - 1;
+        const int col = lane % CPR;
+        koff = (int64_t)(pos & 15) * a.st + head_off + (col ^ chunk_swz<D>(key)) * 8;
+        voff = (int64_t)(pos & 15) * a.st + head_off + (col ^ chunk_swz_v<D>(key)) * 8;
+      }
+      const int64_t pg = (int64_t)s_pages[(pos >> 4) - first_page] * a.sp;
+      lds_dma16(a.k + pg + koff, sK + blk * 1024);
+      lds_dma16(a.v + pg + voff, sV + blk * 1024);
     }
   };
   auto wait_stage = [&](int after) {   // `after` stages were issued after the one needed
-    if (NS >= 4 && after >= 2) wait_vmcnt<2 * OPS>();
-    else if (NS >= 3 && after >= 1) wait_vmcnt<OPS>();
+    if (NS >= 4 && after >= 3) wait_vmcnt<3 * OPS>();
+    else if (NS >= 3 && after >= 2) wait_vmcnt<2 * OPS>();
+    else if (after >= 1) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
   };
 
-  const int pro = min(NS - 1, n_tiles);
+  // All NS buffers are filled up front; afterwards stage t + NS - 1 goes into
+  // the buffer that stage t - 1 used, once every wave is past stage t's barrier.
+  const int pro = min(NS, n_tiles);
   for (int t = 0; t < pro; ++t) issue_stage(t);
 
   for (int t = 0; t < n_tiles; ++t) {
-    wait_stage(min(NS - 2, n_tiles - 1 - t));
+    // stages issued after stage t so far: the prologue filled NS buffers,
+    // and iteration i >= 1 issued stage i + NS - 1
+    wait_stage(t == 0 ? min(NS - 1, n_tiles - 1) : min(NS - 2, n_tiles - 1 - t));
     block_barrier();
-    if (t + NS - 1 < n_tiles) issue_stage(t + NS - 1);
+    if (t >= 1 && t + NS - 1 < n_tiles) issue_stage(t + NS - 1);
     if (wave_active) {
       const uint32_t stage = smem_base + (t % NS) * SM::STAGE_BYTES;
       const uint32_t sK = stage + kg * NKB * 16 * ROWB;
@@ -376,8 +416,11 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
         }
         l_run[rb] = l_run[rb] * alpha + psum;
         m_run[rb] = m_new;
+        // the running max of most rows stops moving after a few stages
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
+          for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
+        }
       }
       // O^T += V^T P^T. The transpose load gives lane lr of group lq, for
       // keys kb*16 + 4*lq + (0..3), the values at d = db*16 + lr.
@@ -406,8 +449,8 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
             const uint32_t va = sV + v_off[dh * DBH + dbi];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-              const u32x2_t h0 = lds_read_tr16(va + kk * 32 * ROWB);
-              const u32x2_t h1 = lds_read_tr16(va + (kk * 32 + 16) * ROWB);
+              const u32x2_t h0 = kk == 0 ? lds_read_tr16<0>(va) : lds_read_tr16<32 * ROWB>(va);
+              const u32x2_t h1 = kk == 0 ? lds_read_tr16<16 * ROWB>(va) : lds_read_tr16<48 * ROWB>(va);
               vf[dbi * NKK + kk] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
             }
           }
@@ -484,37 +527,13 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
     const float l_tot = wave_sum_across_quads(l_run[rb]);
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
-    float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    const float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (!row_ok[rb]) continue;
     const int64_t row = (int64_t)row_tok[rb] * a.hq + row_head[rb];
     if (a.direct) {
       f32x4_t acc[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] = o[db][rb] * inv;
-      if (a.merge_slots > 0) {
-        // LSE merge of this state with the prefix phase's partial states of
-        // the same row (online form). The loads of a batch of slots are all
-        // issued before the first use: one memory round trip per batch.
-        float m = lse, wsum = live ? 1.f : 0.f;
-        for (int s0 = 0; s0 < a.merge_slots; s0 += kMergeBatch) {
-          float ls[kMergeBatch];
-          f32x4_t po[kMergeBatch][DB];
-#pragma unroll
-          for (int k = 0; k < kMergeBatch; ++k) {
-            const int sl = min(s0 + k, a.merge_slots - 1);
-            ls[k] = (s0 + k < a.merge_slots) ? a.part_lse[(int64_t)sl * a.slot_rows + row] : -INFINITY;
-            const float* src = a.part_o + (int64_t)sl * a.slot_elems + row * D + lq * 4;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) po[k][db] = *reinterpret_cast<const f32x4_t*>(src + db * 16);
-          }
-#pragma unroll
-          for (int k = 0; k < kMergeBatch; ++k) merge_step(m, wsum, acc, ls[k], po[k]);
-        }
-        const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= winv;
-        lse = wsum > 0.f ? m + logf(wsum) : -INFINITY;
-      }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<u32x2_t*>(a.out + row * D + db * 16 + lq * 4) =
@@ -527,6 +546,24 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
       if (lq == 0) a.part_lse[(int64_t)slot * a.slot_rows + row] = lse;
     }
   }
+}
+
+template <int D, int RB, int RW, int KG, int NS>
+__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS>::BYTES];
+  attn_item<D, RB, RW, KG, NS>(a, blockIdx.x, smem);
+}
+
+// One launch for both cascade phases: work-groups [0, n_prefix) run prefix
+// items, the rest run suffix items, so the MFMA-heavy prefix and the
+// bandwidth-heavy suffix share the CUs. Both write partial states.
+template <int D, int PRB, int PRW, int PKG, int SRB, int SRW, int SKG, int NS>
+__global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs sa, const int n_prefix) {
+  static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS>::BYTES];
+  const int bid = blockIdx.x;
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, NS>(pa, bid, smem);
+  else attn_item<D, SRB, SRW, SKG, NS>(sa, bid - n_prefix, smem);
 }
 
 }  // namespace ca

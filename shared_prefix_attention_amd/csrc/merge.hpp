@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   // Online merge over slots in batches whose loads (LSE and o, the latter
   // unconditionally: every slot is in bounds) are all issued before the first
   // use, so a row costs one memory round trip per batch.
-  constexpr int B = 8;
+  constexpr int B = 16;
   float m = -INFINITY, wsum = 0.f;
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < a.slots; s0 += B) {

@@ -64,13 +64,14 @@ struct CostModel {
 };
 
 // Work-group shapes of the tiled kernel (all 64-key stages):
-//   kRowsConfig   64 rows (4 waves x 16), each stage split over 2 key groups
-//                 -> 8 waves; for packed prefix rows and prefill suffixes;
+//   kRowsConfig   64 rows (4 waves x 16); for packed prefix rows and
+//                 prefill suffixes;
 //   kMfmaConfig   128 rows (4 waves x 32), one key group; when the prefix
 //                 is large enough to be bound by the MFMA rate;
 //   kDecodeConfig 16 rows (1 wave), each stage split over 4 key groups;
 //                 for suffixes whose rows (q_len * G) fit one MFMA block.
-static PhaseTile rows_config() { PhaseTile t; t.row_blocks = 1; t.row_waves = 4; t.key_groups = 2; return t; }
+static PhaseTile rows_config() { PhaseTile t; t.row_blocks = 1; t.row_waves = 4; t.key_groups = 1; return t; }
+static PhaseTile half_rows_config() { PhaseTile t; t.row_blocks = 1; t.row_waves = 2; t.key_groups = 2; return t; }
 static PhaseTile mfma_config() { PhaseTile t; t.row_blocks = 2; t.row_waves = 4; t.key_groups = 1; return t; }
 static PhaseTile decode_config() {
   PhaseTile t;
@@ -302,7 +303,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pre = choose_prefix(*pl, cus, cm, &pre_us);
     pl->key_start = (int32_t)plen;
     pl->max_suffix_len = max_seq - (int32_t)plen;
-    suf = choose_suffix(*pl, cus, false);
+    suf = choose_suffix(*pl, cus, true);
     const double t_suf = est_suffix_us(*pl, pl->kv_tokens_cascade - plen,
                                        suffix_padded_flops(*pl, qsl, seq_lens, (int32_t)plen), suf.splits, false,
                                        cus, cm, 0.0);
@@ -322,9 +323,11 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->max_suffix_len = max_seq - (int32_t)plen;
     pl->prefix = pre;
     pl->suffix = suf;
-    pl->merge_in_suffix = suf.splits == 1 ? 1 : 0;
-    pl->num_slots = pre.splits + (pl->merge_in_suffix ? 0 : suf.splits);
-    pl->direct_out = pl->merge_in_suffix != 0;
+    pl->prefix.stages = 2;   // both phases share one launch (two work-groups per CU)
+    pl->suffix.stages = 2;
+    pl->merge_in_suffix = 0;
+    pl->num_slots = pre.splits + suf.splits;
+    pl->direct_out = false;
   } else {
     pl->key_start = 0;
     pl->max_suffix_len = max_seq;

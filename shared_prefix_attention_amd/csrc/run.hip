@@ -79,19 +79,62 @@ void launch_tile_ns(const TileArgs& args, int ns, int grid, hipStream_t s) {
   else launch_tile<D, RB, RW, KG, 2>(args, grid, s);
 }
 
+bool item_ok(const PhaseTile& ph) { return ph.split_tokens > 0 && ph.split_tokens <= kMaxItemTokens && ph.split_tokens % kTileKeys == 0; }
+
+// 4-wave work-group shapes (row_blocks, row_waves, key_groups):
+// 0 = rows (1,4,1), 1 = MFMA (2,4,1), 2 = decode (1,1,4), 3 = half rows (1,2,2)
+int shape_id(const PhaseTile& ph) {
+  if (ph.row_blocks == 1 && ph.row_waves == 2 && ph.key_groups == 2) return 3;
+  if (ph.row_blocks == 1 && ph.row_waves == 4 && ph.key_groups == 1) return 0;
+  if (ph.row_blocks == 2 && ph.row_waves == 4 && ph.key_groups == 1) return 1;
+  if (ph.row_blocks == 1 && ph.row_waves == 1 && ph.key_groups == 4) return 2;
+  return -1;
+}
+
 template <int D>
 ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hipStream_t s, int kind) {
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
-  if (ph.split_tokens > kMaxItemTokens || ph.split_tokens % kTileKeys)
-    return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
+  if (!item_ok(ph)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   LaunchTimer tm(kind, s);
-  if (ph.row_blocks == 1 && ph.row_waves == 4 && ph.key_groups == 2) launch_tile_ns<D, 1, 4, 2>(args, ph.stages, (int)grid, s);
-  else if (ph.row_blocks == 2 && ph.row_waves == 4 && ph.key_groups == 1) launch_tile_ns<D, 2, 4, 1>(args, ph.stages, (int)grid, s);
-  else if (ph.row_blocks == 1 && ph.row_waves == 1 && ph.key_groups == 4) launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s);
-  else return fail(CA_EINVAL, "unsupported work-group shape in plan");
+  switch (shape_id(ph)) {
+    case 0: launch_tile_ns<D, 1, 4, 1>(args, ph.stages, (int)grid, s); break;
+    case 2: launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s); break;
+    default: return fail(CA_EINVAL, "unsupported work-group shape in plan");
+  }
   tm.done();
   return check_launch("attention kernel launch");
+}
+
+template <int D, int P, int S>
+void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, hipStream_t s) {
+  constexpr int PRB = P == 1 ? 2 : 1;
+  constexpr int PRW = P == 3 ? 2 : 4, PKG = P == 3 ? 2 : 1;
+  constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
+  hipLaunchKernelGGL((cascade_phases_kernel<D, PRB, PRW, PKG, 1, SRW, SKG, 2>), dim3(grid), dim3(256), 0, s, pa, sa,
+                     n_prefix);
+}
+
+template <int D>
+ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix, const TileArgs& sa,
+                       const PhaseTile& sp, int64_t n_suffix, hipStream_t s) {
+  if (n_prefix + n_suffix > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
+  if (!item_ok(pp) || !item_ok(sp)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
+  const int pid = shape_id(pp), sid = shape_id(sp);
+  if (pid < 0 || pid == 2 || (sid != 0 && sid != 2)) return fail(CA_EINVAL, "unsupported work-group shape in plan");
+  const int grid = (int)(n_prefix + n_suffix);
+  LaunchTimer tm(K_PREFIX, s);
+  if (sid == 0) {
+    if (pid == 0) launch_phases<D, 0, 0>(pa, sa, (int)n_prefix, grid, s);
+    else if (pid == 1) launch_phases<D, 1, 0>(pa, sa, (int)n_prefix, grid, s);
+    else launch_phases<D, 3, 0>(pa, sa, (int)n_prefix, grid, s);
+  } else {
+    if (pid == 0) launch_phases<D, 0, 2>(pa, sa, (int)n_prefix, grid, s);
+    else if (pid == 1) launch_phases<D, 1, 2>(pa, sa, (int)n_prefix, grid, s);
+    else launch_phases<D, 3, 2>(pa, sa, (int)n_prefix, grid, s);
+  }
+  tm.done();
+  return check_launch("cascade phases kernel launch");
 }
 
 template <int D>
@@ -134,6 +177,15 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   base.part_lse = part_lse;
 
   ca_status_t st;
+  TileArgs sa = base;
+  sa.prefix_mode = 0;
+  sa.key_start = pl->key_start;
+  sa.mtiles = pl->suffix.mtiles;
+  sa.splits = pl->suffix.splits;
+  sa.split_tokens = pl->suffix.split_tokens;
+  sa.slot_base = pl->use_cascade ? pl->prefix.splits : 0;
+  sa.direct = pl->direct_out ? 1 : 0;
+  const int64_t n_suffix = (int64_t)pl->num_reqs * sa.mtiles * pl->hkv * sa.splits;
   if (pl->use_cascade) {
     TileArgs pa = base;
     pa.prefix_mode = 1;
@@ -144,20 +196,10 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     pa.split_tokens = pl->prefix.split_tokens;
     pa.slot_base = 0;
     pa.direct = 0;
-    st = run_tile<D>(pa, pl->prefix, (int64_t)pa.mtiles * pl->hkv * pa.splits, s, K_PREFIX);
-    if (st != CA_OK) return st;
+    st = run_phases<D>(pa, pl->prefix, (int64_t)pa.mtiles * pl->hkv * pa.splits, sa, pl->suffix, n_suffix, s);
+  } else {
+    st = run_tile<D>(sa, pl->suffix, n_suffix, s, pl->suffix.kernel == 1 ? K_DECODE : K_SUFFIX);
   }
-  TileArgs sa = base;
-  sa.prefix_mode = 0;
-  sa.key_start = pl->key_start;
-  sa.mtiles = pl->suffix.mtiles;
-  sa.splits = pl->suffix.splits;
-  sa.split_tokens = pl->suffix.split_tokens;
-  sa.slot_base = pl->use_cascade ? pl->prefix.splits : 0;
-  sa.direct = pl->direct_out ? 1 : 0;
-  sa.merge_slots = pl->merge_in_suffix ? pl->prefix.splits : 0;
-  st = run_tile<D>(sa, pl->suffix, (int64_t)pl->num_reqs * sa.mtiles * pl->hkv * sa.splits, s,
-                   pl->suffix.kernel == 1 ? K_DECODE : K_SUFFIX);
   if (st != CA_OK) return st;
   if (!pl->direct_out) {
     MergeArgs ma{};

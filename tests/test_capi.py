@@ -186,9 +186,8 @@ def test_plan_partition_is_consistent():
             slots = info["num_partial_slots"]
             assert info["workspace_bytes"] >= slots * T * hq * (d + 1) * 4
             if info["use_cascade"]:
-                merged = info["merge_in_suffix"]
-                assert merged == int(info["suffix_chunks"] == 1)
-                assert slots == info["prefix_splits"] + (0 if merged else info["suffix_chunks"])
+                assert info["merge_in_suffix"] == 0
+                assert slots == info["prefix_splits"] + info["suffix_chunks"]
                 assert info["prefix_splits"] >= 1
             assert info["suffix_chunk_tokens"] % 64 == 0
             assert 0 < info["suffix_chunk_tokens"] <= 8192
