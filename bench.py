@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of one cascade-attention step on one MI355X.
 
-A step is one cascade_attn_run() over one batch (prefix kernel + suffix kernel
-+ merge for the cascade path). Default workload: the pages' worked example,
-N=64 requests, a 4096-token shared prefix, 128-token suffixes, 1 query token
-each, 32 query / 8 KV heads, head_dim 128, bf16, page size 16.
+A step is one cascade_attn_run() over one batch: for the cascade path one
+launch running the prefix and suffix work-groups plus one merge launch.
+Default workload: the pages' worked example, N=64 requests, a 4096-token
+shared prefix, 128-token suffixes, one query token each, 32 query / 8 KV
+heads, head_dim 128, bf16, page size 16 (synthetic inputs).
 
-Inputs are resident in HBM before timing. To keep the 256 MB Infinity Cache
-from serving the KV a step reads, the timed loop rotates over several
-identical copies of Q and the KV cache (same plan), so each step reads data
-the previous steps have not touched for >= 1 GiB of traffic.
+Inputs are resident in HBM before timing. So that the 256 MB Infinity Cache
+cannot serve the KV a step reads, the timed loop rotates over identical copies
+of Q and the KV cache (same plan): each step reads data that >= 1 GiB of other
+traffic has passed since its last use.
 
-Prints one JSON line (the driver's contract); extra fields carry the
-per-kernel breakdown, the non-cascade GPU path and a warm-cache number.
+Prints one JSON line; extra fields carry the per-kernel breakdown, the GPU
+non-cascade path, a warm-cache number and the oracle's CPU rate.
+
+Other modes (measurement plumbing, used under rocprofv3):
+  --traffic-probe       one device copy of known size, then --steps steps
+                        (no timing; for `rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE`)
+  --summarize-pmc F W   read the counter CSVs of those two runs and write the
+                        HBM-traffic summary profiles/traffic_<workload>.json
 """
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -30,7 +39,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, TFLOP/s
-KERNEL_SOURCES = ["attn_tile.hpp", "merge.hpp", "device_common.hpp", "run.hip"]
+# device code and the partition: what the traffic counters depend on
+KERNEL_SOURCES = ["attn_tile.hpp", "merge.hpp", "device_common.hpp", "plan.cpp"]
+COPY_BYTES = 512 << 20         # calibration copy for the traffic counters
+KIND_KERNEL = {"cascade_phases": "cascade_phases_kernel", "attention": "attn_tile_kernel",
+               "decode": "attn_tile_kernel", "merge": "merge_kernel"}
 
 
 def kernel_source_hash():
@@ -41,19 +54,21 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, kernel):
-    """HBM bytes per launch measured by rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE)
-    for this kernel source; None when absent or taken on other source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def load_traffic(workload, kind):
+    """HBM bytes per launch of `kind` from the committed rocprofv3 summary,
+    or None when absent or taken on other kernel source."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k["hbm_bytes_per_launch"]
+    k = rec.get("kernels", {}).get(KIND_KERNEL.get(kind, kind))
+    return None if not k else k["hbm_bytes_per_launch"]
 
 
 def time_steps(fn, steps, rotate):
@@ -66,8 +81,9 @@ def time_steps(fn, steps, rotate):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def cpu_baseline(b, kv_bytes, budget_s=12.0, max_runs=5):
-    """The fp64 oracle (test infrastructure) on this host, one BLAS thread."""
+def cpu_baseline(b, kv_bytes, budget_s=15.0, max_runs=60):
+    """The fp64 oracle (test infrastructure) on this host, one BLAS thread,
+    over the whole batch, repeated for about budget_s seconds."""
     import oracle
     from threadpoolctl import threadpool_limits
     kc, vc = b.k_cache.float().numpy(), b.v_cache.float().numpy()
@@ -82,8 +98,37 @@ def cpu_baseline(b, kv_bytes, budget_s=12.0, max_runs=5):
             times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole batch ({b.workload.num_reqs} requests), {len(times)} runs, median {t:.2f} s; "
-                      f"fp64 numpy, 1 BLAS thread"}
+            "sample": f"whole batch ({b.workload.num_reqs} requests) x {len(times)} runs "
+                      f"({sum(times):.1f} s), median {t:.3f} s per batch; fp64 numpy, 1 BLAS thread"}
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, steps):
+    """Traffic per launch = counter (KiB) x (bytes the calibration copy moves /
+    what the same counter reads for it)."""
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        return rows
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "kernels": {},
+           "command": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -- python3 bench.py --traffic-probe "
+                      f"--workload {workload} --steps {steps}; same with WRITE_SIZE into {write_dir}"}
+    for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
+        rows = read(d, counter)
+        copy = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not copy:
+            raise SystemExit(f"no calibration copy dispatch in {d}")
+        factor = COPY_BYTES / (max(copy) * 1024.0)
+        out[f"{key}_factor"] = factor
+        for kname in sorted(set(KIND_KERNEL.values())):
+            vals = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
+            if vals:
+                k = out["kernels"].setdefault(kname, {})
+                k[f"{key}_kib_raw"] = statistics.median(vals)
+                k[f"{key}_bytes"] = statistics.median(vals) * 1024.0 * factor
+    for k in out["kernels"].values():
+        k["hbm_bytes_per_launch"] = k.get("fetch_bytes", 0.0) + k.get("write_bytes", 0.0)
+    return out
 
 
 def main():
@@ -95,11 +140,20 @@ def main():
     ap.add_argument("--mode", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-noncascade", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_pmc:
+        rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.steps)
+        os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)
+        with open(traffic_path(args.workload), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
 
     import torch
     import workloads
@@ -108,7 +162,6 @@ def main():
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
     b = workloads.make_batch(w)
-    G = w.num_q_heads // w.num_kv_heads
     bpt = 2 * w.num_kv_heads * w.head_dim * 2
 
     def make_plan(mode):
@@ -119,14 +172,13 @@ def main():
     plan = make_plan(args.mode)
     info = plan.info
     T = b.total_q
-    plen = info["common_prefix_len"] if info["use_cascade"] else 0
-    kv_tokens = info["kv_tokens_cascade"] if info["use_cascade"] else info["kv_tokens_noncascade"]
+    casc = bool(info["use_cascade"])
+    plen = info["common_prefix_len"] if casc else 0
+    kv_tokens = info["kv_tokens_cascade"] if casc else info["kv_tokens_noncascade"]
     kv_bytes = kv_tokens * bpt
     touched = kv_bytes + b.q.numel() * 2
-    rotate = int(min(64, max(2, math.ceil((1 << 30) / max(touched, 1)))))
-    copies = []
-    for _ in range(rotate):
-        copies.append((b.q.to(dev), b.k_cache.to(dev), b.v_cache.to(dev)))
+    rotate = 1 if args.traffic_probe else int(min(64, max(2, math.ceil((1 << 30) / max(touched, 1)))))
+    copies = [(b.q.to(dev), b.k_cache.to(dev), b.v_cache.to(dev)) for _ in range(rotate)]
     bt, qsl, sl = b.block_table.to(dev), b.query_start_loc.to(dev), b.seq_lens.to(dev)
     out = torch.empty_like(copies[0][0])
     lse = torch.empty(T, w.num_q_heads, dtype=torch.float32, device=dev)
@@ -143,11 +195,21 @@ def main():
         return f
 
     step = step_with(plan, ws)
+    if args.traffic_probe:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        for i in range(args.steps):
+            step(0)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": args.workload, "steps": args.steps}))
+        return
+
     for i in range(args.warmup):
         step(i % rotate)
     ms = time_steps(step, args.steps, rotate)
 
-    # per-kernel durations: HIP events around every launch, same stream
+    # per-kernel durations: HIP events around every launch, on the run's stream
     spa.cascade_attn_profile_enable(True)
     ms_prof = time_steps(step, args.steps, rotate)
     spa.cascade_attn_profile_enable(False)
@@ -157,30 +219,31 @@ def main():
         if cnt:
             kern[kind] = {"avg_us": round(tot_ms * 1e3 / cnt, 3), "launches": int(cnt)}
 
-    # algorithmic work per launch
+    # algorithmic work of one launch of each attention kernel: the KV
+    # positions it must read (prefix once + each request's suffix) plus Q, and
+    # its QK^T / PV flops
     q_bytes = T * w.num_q_heads * w.head_dim * 2
-    suffix_tokens = int(info["kv_tokens_cascade"] - plen) if info["use_cascade"] else int(info["kv_tokens_noncascade"])
-    work = {
-        "prefix": {"bytes": plen * bpt + q_bytes, "flops": 4.0 * T * w.num_q_heads * plen * w.head_dim},
-        "suffix": {"bytes": suffix_tokens * bpt + q_bytes, "flops": None},
-    }
-    for kind in ("prefix", "suffix"):
-        if kind in kern:
-            sec = kern[kind]["avg_us"] * 1e-6
-            kern[kind]["gbs"] = round(work[kind]["bytes"] / sec / 1e9, 1)
-            kern[kind]["hbm_frac"] = round(work[kind]["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4)
-            if work[kind]["flops"]:
-                kern[kind]["tflops"] = round(work[kind]["flops"] / sec / 1e12, 2)
-                kern[kind]["mfma_frac"] = round(work[kind]["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)
-    dom = max((k for k in ("prefix", "suffix") if k in kern), key=lambda k: kern[k]["avg_us"])
-    traffic = load_traffic(args.workload, dom)
-    roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": kern[dom]["hbm_frac"], "traffic": traffic}
+    qlen = (b.query_start_loc[1:] - b.query_start_loc[:-1]).tolist()
+    seq = b.seq_lens.tolist()
+    visible = sum(ql * (s - ql) + ql * (ql + 1) // 2 for ql, s in zip(qlen, seq))   # causal keys per query
+    flops = 4.0 * w.num_q_heads * w.head_dim * visible
+    attn_kind = "cascade_phases" if casc else ("decode" if info["suffix_kernel"] == 1 else "attention")
+    work = {"bytes": kv_bytes + q_bytes, "flops": flops}
+    if attn_kind in kern:
+        sec = kern[attn_kind]["avg_us"] * 1e-6
+        kern[attn_kind]["gbs"] = round(work["bytes"] / sec / 1e9, 1)
+        kern[attn_kind]["hbm_frac"] = round(work["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4)
+        kern[attn_kind]["tflops"] = round(work["flops"] / sec / 1e12, 2)
+        kern[attn_kind]["mfma_frac"] = round(work["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)
+    traffic = load_traffic(args.workload, attn_kind)
+    roof = {"kernel": attn_kind, "bound": "hbm", "achieved": kern[attn_kind]["gbs"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kern[attn_kind]["hbm_frac"],
+            "traffic": None if traffic is None else round(traffic)}
 
     # warm-cache number (no rotation) and the GPU non-cascade path
     ms_warm = time_steps(step, args.steps, 1)
     extra = {}
-    if not args.no_noncascade:
+    if not args.no_noncascade and casc:
         plan_off = make_plan("off")
         ws_off = workspace_for(plan_off)
         step_off = step_with(plan_off, ws_off)
@@ -213,7 +276,7 @@ def main():
         "config": {"workload": args.workload, "num_reqs": w.num_reqs, "prefix": w.prefix,
                    "suffix": list(w.suffix), "q_len": list(w.q_len), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
-                   "mode": args.mode, "use_cascade": info["use_cascade"], "common_prefix_len": plen,
+                   "mode": args.mode, "use_cascade": int(casc), "common_prefix_len": plen,
                    "kv_bytes_per_step": kv_bytes, "rotating_copies": rotate},
         "roofline": roof,
         "kernels": kern,

@@ -192,9 +192,11 @@ const char* cascade_attn_last_error(void);
  * Kernel timing for measurement. While enabled, run() records a HIP event
  * pair around every kernel it launches, on the launch stream.
  * cascade_attn_profile_read() waits for the recorded events, writes the
- * summed milliseconds and launch counts per kernel kind
- * (0 = prefix, 1 = suffix / non-cascade attention, 2 = merge,
- * 3 = decode attention) into ms[4] and counts[4], and clears the record.
+ * summed milliseconds and launch counts per kernel kind into ms[4] and
+ * counts[4], and clears the record. Kinds: 0 = cascade phases (prefix and
+ * suffix work-groups of the cascade path in one launch), 1 = tiled
+ * attention of the non-cascade path, 2 = merge, 3 = decode attention of the
+ * non-cascade path.
  * Errors: CA_EHIP if an event call fails, CA_EINVAL for null outputs.
  */
 ca_status_t cascade_attn_profile_enable(int32_t enable);

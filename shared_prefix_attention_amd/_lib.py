@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "cascade_attn.h")
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_EMETA, CA_EWORKSPACE, CA_EHIP = range(6)
 MODE_AUTO, MODE_FORCE_ON, MODE_FORCE_OFF = 0, 1, 2
 _MODES = {"auto": MODE_AUTO, "on": MODE_FORCE_ON, "off": MODE_FORCE_OFF}
-KERNEL_KINDS = ("prefix", "suffix", "merge", "decode")
+KERNEL_KINDS = ("cascade_phases", "attention", "merge", "decode")
 
 
 class CascadeAttnError(RuntimeError):

@@ -7,6 +7,7 @@
 // a merge when the plan splits the KV range. All launches go to the
 // caller's stream in order; nothing here allocates or synchronises.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -21,7 +22,7 @@ using namespace ca;
 
 namespace {
 
-enum KernelKind { K_PREFIX = 0, K_SUFFIX = 1, K_MERGE = 2, K_DECODE = 3, K_KINDS = 4 };
+enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_KINDS = 4 };
 
 struct Profiler {
   std::mutex mu;
@@ -34,28 +35,26 @@ struct Profiler {
 };
 Profiler g_prof;
 
-struct LaunchTimer {
+// Launches `kernel`; while timing is enabled the launch carries a start /
+// stop event pair on its own dispatch (hipExtLaunchKernelGGL), so the
+// recorded time is the kernel's execution only.
+template <typename K, typename... Args>
+void launch(int kind, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  bool timed = false;
   hipEvent_t a = nullptr, b = nullptr;
-  int kind;
-  hipStream_t s;
-  bool on;
-  LaunchTimer(int k, hipStream_t st) : kind(k), s(st) {
-    on = g_prof.enabled;
-    if (on) {
-      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
-        on = false;
-        return;
-      }
-      (void)hipEventRecord(a, s);
-    }
+  {
+    std::lock_guard<std::mutex> g(g_prof.mu);
+    timed = g_prof.enabled;
   }
-  void done() {
-    if (!on) return;
-    (void)hipEventRecord(b, s);
+  if (timed && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
     std::lock_guard<std::mutex> g(g_prof.mu);
     g_prof.recs.push_back({kind, a, b});
+    return;
   }
-};
+  if (a) (void)hipEventDestroy(a);
+  hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 ca_status_t fail(ca_status_t c, const std::string& m) {
   set_error(m);
@@ -69,14 +68,14 @@ ca_status_t check_launch(const char* what) {
 }
 
 template <int D, int RB, int RW, int KG, int NS>
-void launch_tile(const TileArgs& args, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_tile_kernel<D, RB, RW, KG, NS>), dim3(grid), dim3(64 * RW * KG), 0, s, args);
+void launch_tile(const TileArgs& args, int grid, hipStream_t s, int kind) {
+  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS>, dim3(grid), dim3(64 * RW * KG), s, args);
 }
 
 template <int D, int RB, int RW, int KG>
-void launch_tile_ns(const TileArgs& args, int ns, int grid, hipStream_t s) {
-  if (ns == 4) launch_tile<D, RB, RW, KG, 4>(args, grid, s);
-  else launch_tile<D, RB, RW, KG, 2>(args, grid, s);
+void launch_tile_ns(const TileArgs& args, int ns, int grid, hipStream_t s, int kind) {
+  if (ns == 4) launch_tile<D, RB, RW, KG, 4>(args, grid, s, kind);
+  else launch_tile<D, RB, RW, KG, 2>(args, grid, s, kind);
 }
 
 bool item_ok(const PhaseTile& ph) { return ph.split_tokens > 0 && ph.split_tokens <= kMaxItemTokens && ph.split_tokens % kTileKeys == 0; }
@@ -96,13 +95,11 @@ ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hi
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(ph)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
-  LaunchTimer tm(kind, s);
   switch (shape_id(ph)) {
-    case 0: launch_tile_ns<D, 1, 4, 1>(args, ph.stages, (int)grid, s); break;
-    case 2: launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s); break;
+    case 0: launch_tile_ns<D, 1, 4, 1>(args, ph.stages, (int)grid, s, kind); break;
+    case 2: launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s, kind); break;
     default: return fail(CA_EINVAL, "unsupported work-group shape in plan");
   }
-  tm.done();
   return check_launch("attention kernel launch");
 }
 
@@ -111,8 +108,8 @@ void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int gri
   constexpr int PRB = P == 1 ? 2 : 1;
   constexpr int PRW = P == 3 ? 2 : 4, PKG = P == 3 ? 2 : 1;
   constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
-  hipLaunchKernelGGL((cascade_phases_kernel<D, PRB, PRW, PKG, 1, SRW, SKG, 2>), dim3(grid), dim3(256), 0, s, pa, sa,
-                     n_prefix);
+  launch(K_PHASES, cascade_phases_kernel<D, PRB, PRW, PKG, 1, SRW, SKG, 2>, dim3(grid), dim3(256), s, pa, sa,
+         n_prefix);
 }
 
 template <int D>
@@ -123,7 +120,6 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
   const int pid = shape_id(pp), sid = shape_id(sp);
   if (pid < 0 || pid == 2 || (sid != 0 && sid != 2)) return fail(CA_EINVAL, "unsupported work-group shape in plan");
   const int grid = (int)(n_prefix + n_suffix);
-  LaunchTimer tm(K_PREFIX, s);
   if (sid == 0) {
     if (pid == 0) launch_phases<D, 0, 0>(pa, sa, (int)n_prefix, grid, s);
     else if (pid == 1) launch_phases<D, 1, 0>(pa, sa, (int)n_prefix, grid, s);
@@ -133,7 +129,6 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
     else if (pid == 1) launch_phases<D, 1, 2>(pa, sa, (int)n_prefix, grid, s);
     else launch_phases<D, 3, 2>(pa, sa, (int)n_prefix, grid, s);
   }
-  tm.done();
   return check_launch("cascade phases kernel launch");
 }
 
@@ -142,9 +137,7 @@ ca_status_t run_merge(const MergeArgs& args, hipStream_t s) {
   constexpr int RPB = 256 / (D / 4);
   const int64_t grid = (args.rows + RPB - 1) / RPB;
   if (grid <= 0) return CA_OK;
-  LaunchTimer tm(K_MERGE, s);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, args);
-  tm.done();
+  launch(K_MERGE, merge_kernel<D>, dim3((unsigned)grid), dim3(256), s, args);
   return check_launch("merge kernel launch");
 }
 
@@ -198,7 +191,7 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     pa.direct = 0;
     st = run_phases<D>(pa, pl->prefix, (int64_t)pa.mtiles * pl->hkv * pa.splits, sa, pl->suffix, n_suffix, s);
   } else {
-    st = run_tile<D>(sa, pl->suffix, n_suffix, s, pl->suffix.kernel == 1 ? K_DECODE : K_SUFFIX);
+    st = run_tile<D>(sa, pl->suffix, n_suffix, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
   }
   if (st != CA_OK) return st;
   if (!pl->direct_out) {
