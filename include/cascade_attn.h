@@ -78,7 +78,8 @@ typedef struct {
    * [page][slot][kv_head][d] with d contiguous; NHD layout
    * [num_pages, page_size, Hkv, d] has (page_size*Hkv*d, Hkv*d, d), HND
    * layout [num_pages, Hkv, page_size, d] has (Hkv*page_size*d, d, page_size*d).
-   * All three must be multiples of 8 (16-byte aligned rows). */
+   * All three must be multiples of 8 (16-byte aligned rows), and
+   * kv_stride_token at most 2^26 (byte offsets within one page fit 32 bits). */
   int64_t kv_stride_page;
   int64_t kv_stride_token;
   int64_t kv_stride_head;

@@ -14,12 +14,12 @@
 // each query sees.)
 //
 // Work-group: RW * KG wave64s owning one (KV head, row tile, KV range) item.
-// K/V are streamed 64 keys (4 pages) per stage straight from HBM into LDS
-// with global_load_lds_dwordx4 (no register staging), NS stages in flight.
+// K/V are streamed SK keys (SK/16 pages) per stage straight from HBM into
+// LDS with global_load_lds_dwordx4 (no register staging), NS stages in flight.
 // Each LDS row (one key, d contiguous) has its 16-byte chunks XOR-swizzled
 // by the key index so the MFMA operand reads are bank-conflict free.
 // Wave (rw, kg) owns query rows [rw*16*RB, +16*RB) of the tile and keys
-// [kg*64/KG, +64/KG) of every stage, with its own online-softmax state; the
+// [kg*SK/KG, +SK/KG) of every stage, with its own online-softmax state; the
 // KG states of a row block are merged through LDS at the end. Per wave and
 // stage:
 //   S^T[key][row] = K Q^T   (v_mfma_f32_16x16x32_bf16: A = K from LDS,
@@ -73,9 +73,9 @@ struct TileArgs {
 
 constexpr int kMaxItemPages = 512;
 
-template <int D, int NS>
+template <int D, int NS, int SK>
 struct TileSmem {
-  static constexpr int TILE_BYTES = 64 * D * 2;            // one of K or V, one stage
+  static constexpr int TILE_BYTES = SK * D * 2;            // one of K or V, one stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int BYTES = NS * STAGE_BYTES + kMaxItemPages * 4;
 };
@@ -94,8 +94,10 @@ __device__ __forceinline__ int chunk_swz_v(int key) {
   return D == 128 ? ((2 * key) & 15) : ((key >> 1) & 7);
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_block + 16 l (the block address must be wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(uintptr_t)lds_block, 16, 0, 0);
 }
 
 // Waits until at most N vector-memory ops of this wave are outstanding
@@ -162,7 +164,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
                                                    0, 0, 0);
 }
 
-template <int D, int RB, int RW, int KG, int NS>
+template <int D, int RB, int RW, int KG, int NS, int SK>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
@@ -171,20 +173,21 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   constexpr int DB = D / 16;              // 16-wide d blocks of the output
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   constexpr int KPB = 64 / CPR;           // keys per 1 KB DMA block
-  constexpr int BLK = 64 / KPB;           // 1 KB DMA blocks per tile (K or V)
+  constexpr int BLK = SK / KPB;           // 1 KB DMA blocks per tile (K or V)
   static_assert(BLK % W == 0, "DMA blocks must divide among the waves");
   constexpr int BLK_PER_WAVE = BLK / W;
   constexpr int OPS = 2 * BLK_PER_WAVE;   // vector-memory ops per wave per stage
-  constexpr int NKB = 4 / KG;             // 16-key blocks per wave per stage
+  constexpr int NKB = SK / 16 / KG;       // 16-key blocks per wave per stage
+  static_assert(NKB >= 1 && SK % (16 * KG) == 0, "each wave needs whole 16-key blocks");
   constexpr int ROWB = D * 2;             // LDS bytes per key row
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
-  using SM = TileSmem<D, NS>;
+  using SM = TileSmem<D, NS, SK>;
   static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= NS * SM::STAGE_BYTES, "merge scratch");
   int32_t* s_pages = reinterpret_cast<int32_t*>(smem + NS * SM::STAGE_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int rw = wave % RW;
   const int kg = wave / RW;
   const int lr = lane & 15;
@@ -244,7 +247,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     tok_base = q0;
     q_pos_base = seq_len - q_len;        // num_computed_tokens
   }
-  const int n_tiles = (key_end - key_begin + 63) >> 6;
+  const int n_tiles = (key_end - key_begin + SK - 1) / SK;
   // keys at or below this position are visible to every row of the item
   const int all_visible_to = causal ? q_pos_base + row_begin / a.group : 0x7fffffff;
 #pragma unroll
@@ -307,41 +310,68 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     v_off[db] = tr_row * ROWB + (((d0 >> 3) ^ chunk_swz_v<D>(tr_row)) * 16) + (d0 & 7) * 2;
   }
 
-  const int64_t head_off = (int64_t)g * a.sh;
-  // DMA one stage: this wave moves BLK_PER_WAVE 1 KB blocks of K and of V.
-  // Lane l of a block writes LDS bytes [16 l, 16 l + 16) = (key, chunk
-  // column) of the swizzled layout; it loads the matching source chunk. The
-  // key-slot / chunk part of each source offset is the same every stage.
-  int dma_key[BLK_PER_WAVE];
-  int64_t dma_koff[BLK_PER_WAVE], dma_voff[BLK_PER_WAVE];
+  // ---------------------------------------------------- K/V DMA sources
+  // The KPW keys a wave moves per stage lie inside one 16-token page (every
+  // stage starts on a page boundary), so the page id, the source base and the
+  // LDS destinations are wave-uniform (scalar registers); per lane only a
+  // 32-bit byte offset within the page remains, the same every stage. Lane l
+  // of DMA block i writes LDS bytes [16 l, 16 l + 16) = (key, chunk column)
+  // of the swizzled layout and loads the matching source chunk.
+  // Page table: lane j of register r holds this wave's page id for stage
+  // 64 r + j, read once from LDS; a stage takes its entry with v_readlane.
+  constexpr int KPW = SK / W;                                   // keys per wave per stage
+  static_assert(16 % KPW == 0, "a wave's keys of a stage must lie in one page");
+  constexpr int NPR = (kMaxItemPages * 16 / SK + 63) / 64;      // page-table registers
+  int ptab[NPR];
+#pragma unroll
+  for (int r = 0; r < NPR; ++r) {
+    const int st_i = lane + 64 * r;
+    ptab[r] = st_i < n_tiles ? s_pages[(st_i * SK + wave * KPW) >> 4] : 0;
+  }
+  // page of the item's last position: the source of every clamped lane
+  const int last_pid = n_tiles > 0 ? s_pages[((key_end - 1) >> 4) - first_page] : 0;
+  auto stage_pid = [&](int t) {
+    int v = ptab[0];
+#pragma unroll
+    for (int r = 1; r < NPR; ++r) v = (t >> 6) == r ? ptab[r] : v;
+    return __builtin_amdgcn_readlane(v, t & 63);
+  };
+  const int col = lane % CPR;
+  uint32_t dma_koff[BLK_PER_WAVE], dma_voff[BLK_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < BLK_PER_WAVE; ++i) {
-    const int blk = wave * BLK_PER_WAVE + i;
-    const int key = blk * KPB + lane / CPR;
-    const int col = lane % CPR;
-    dma_key[i] = key;
-    dma_koff[i] = (int64_t)(key & 15) * a.st + head_off + (col ^ chunk_swz<D>(key)) * 8;
-    dma_voff[i] = (int64_t)(key & 15) * a.st + head_off + (col ^ chunk_swz_v<D>(key)) * 8;
+    const int key = wave * KPW + i * KPB + lane / CPR;          // key within the stage
+    dma_koff[i] = (uint32_t)(((key & 15) * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
+    dma_voff[i] = (uint32_t)(((key & 15) * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
   }
+  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(a.k) + (int64_t)g * a.sh * 2;
+  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(a.v) + (int64_t)g * a.sh * 2;
   auto issue_stage = [&](int t) {
-    uint8_t* sK = smem + (t % NS) * SM::STAGE_BYTES;
-    uint8_t* sV = sK + SM::TILE_BYTES;
-    const int kt0 = key_begin + t * 64;
+    const uint32_t lds_k = smem_base + (t % NS) * SM::STAGE_BYTES + wave * BLK_PER_WAVE * 1024;
+    const uint32_t lds_v = lds_k + SM::TILE_BYTES;
+    const int kt0 = key_begin + t * SK;
+    const int wpos = kt0 + wave * KPW;
+    if (wpos + KPW <= key_end) {
+      const int64_t pg = (int64_t)stage_pid(t) * a.sp * 2;
 #pragma unroll
-    for (int i = 0; i < BLK_PER_WAVE; ++i) {
-      const int blk = wave * BLK_PER_WAVE + i;
-      const int key = dma_key[i];
-      int pos = kt0 + key;
-      int64_t koff = dma_koff[i], voff = dma_voff[i];
-      if (pos >= key_end) {   // past the item: re-read its last position
-        pos = key_end - 1;
-        const int col = lane % CPR;
-        koff = (int64_t)(pos & 15) * a.st + head_off + (col ^ chunk_swz<D>(key)) * 8;
-        voff = (int64_t)(pos & 15) * a.st + head_off + (col ^ chunk_swz_v<D>(key)) * 8;
+      for (int i = 0; i < BLK_PER_WAVE; ++i) {
+        lds_dma16(k_head + pg + dma_koff[i], lds_k + i * 1024);
+        lds_dma16(v_head + pg + dma_voff[i], lds_v + i * 1024);
       }
-      const int64_t pg = (int64_t)s_pages[(pos >> 4) - first_page] * a.sp;
-      lds_dma16(a.k + pg + koff, sK + blk * 1024);
-      lds_dma16(a.v + pg + voff, sV + blk * 1024);
+    } else {
+      // last stage: positions past the item re-read its last position, which
+      // lies in this wave's page or, if the whole range is past it, in last_pid
+      const int pid = wpos < key_end ? stage_pid(t) : last_pid;
+      const int64_t pg = (int64_t)pid * a.sp * 2;
+#pragma unroll
+      for (int i = 0; i < BLK_PER_WAVE; ++i) {
+        const int key = wave * KPW + i * KPB + lane / CPR;
+        const int slot = min(kt0 + key, key_end - 1) & 15;
+        const uint32_t ko = (uint32_t)((slot * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
+        const uint32_t vo = (uint32_t)((slot * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
+        lds_dma16(k_head + pg + ko, lds_k + i * 1024);
+        lds_dma16(v_head + pg + vo, lds_v + i * 1024);
+      }
     }
   };
   auto wait_stage = [&](int after) {   // `after` stages were issued after the one needed
@@ -366,7 +396,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
       const uint32_t stage = smem_base + (t % NS) * SM::STAGE_BYTES;
       const uint32_t sK = stage + kg * NKB * 16 * ROWB;
       const uint32_t sV = stage + SM::TILE_BYTES + kg * NKB * 16 * ROWB;
-      const int kt0 = key_begin + t * 64 + kg * NKB * 16;   // first key of this wave's group
+      const int kt0 = key_begin + t * SK + kg * NKB * 16;   // first key of this wave's group
       // S^T = K Q^T for NKB blocks of 16 keys
       f32x4_t s[NKB][RB];
 #pragma unroll
@@ -398,9 +428,9 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb][rb][0], s[kb][rb][1]), fmaxf(s[kb][rb][2], s[kb][rb][3])));
+          tmax = vmax(tmax, vmax(vmax(s[kb][rb][0], s[kb][rb][1]), vmax(s[kb][rb][2], s[kb][rb][3])));
         tmax = wave_max_across_quads(tmax) * a.scale_log2;
-        const float m_new = fmaxf(m_run[rb], tmax);
+        const float m_new = vmax(m_run[rb], tmax);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
         float psum = 0.f;
@@ -503,7 +533,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
         for (int k2 = 1; k2 < KG; ++k2) {
           const float* r = xs + ((k2 - 1) * RW + rw) * SLOT_F + (rb * 16 + lr) * XS_ROW;
           const float m2 = r[D], l2 = r[D + 1];
-          const float mn = fmaxf(m, m2);
+          const float mn = vmax(m, m2);
           const float mu = (mn == -INFINITY) ? 0.f : mn;
           const float a1 = __builtin_amdgcn_exp2f(m - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
 #pragma unroll
@@ -548,22 +578,25 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   }
 }
 
-template <int D, int RB, int RW, int KG, int NS>
+template <int D, int RB, int RW, int KG, int NS, int SK>
 __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS>::BYTES];
-  attn_item<D, RB, RW, KG, NS>(a, blockIdx.x, smem);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK>::BYTES];
+  attn_item<D, RB, RW, KG, NS, SK>(a, blockIdx.x, smem);
 }
 
 // One launch for both cascade phases: work-groups [0, n_prefix) run prefix
 // items, the rest run suffix items, so the MFMA-heavy prefix and the
-// bandwidth-heavy suffix share the CUs. Both write partial states.
-template <int D, int PRB, int PRW, int PKG, int SRB, int SRW, int SKG, int NS>
+// bandwidth-heavy suffix share the CUs. Both write partial states. Each role
+// has its own pipeline shape (stages x keys per stage) inside one LDS
+// allocation, sized so that two work-groups fit on a CU.
+template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK>
 __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs sa, const int n_prefix) {
   static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS>::BYTES];
+  constexpr int PB = TileSmem<D, PNS, PSK>::BYTES, SB = TileSmem<D, SNS, SSK>::BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, NS>(pa, bid, smem);
-  else attn_item<D, SRB, SRW, SKG, NS>(sa, bid - n_prefix, smem);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK>(pa, bid, smem);
+  else attn_item<D, SRB, SRW, SKG, SNS, SSK>(sa, bid - n_prefix, smem);
 }
 
 }  // namespace ca

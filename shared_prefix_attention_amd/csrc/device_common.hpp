@@ -11,6 +11,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -25,25 +27,51 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two fp32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// max without the NaN-quieting operand copies fmaxf needs in IEEE mode
+// (v_maximum3_f32; NaN-propagating, which no finite or -inf input sees).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48 hold the same MFMA row). v_permlane32_swap of x with itself leaves the
+// low rows' values in one register and the high rows' in the other (XOR 32);
+// v_permlane16_swap does the same for even / odd rows (XOR 16). No LDS; every
+// lane ends with the same, bitwise identical, result.
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 __device__ __forceinline__ float wave_max_across_quads(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same MFMA row
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  float a, b;
+  swap32(x, a, b);
+  x = vmax(a, b);
+  swap16(x, a, b);
+  return vmax(a, b);
 }
 
 __device__ __forceinline__ float wave_sum_across_quads(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  float a, b;
+  swap32(x, a, b);
+  x = a + b;
+  swap16(x, a, b);
+  return a + b;
 }
 
 // Online LSE merge step: folds one partial state (lse_s natural log, o_s

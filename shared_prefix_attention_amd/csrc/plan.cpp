@@ -217,6 +217,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.kv_stride_page <= 0 || p.kv_stride_token <= 0 || p.kv_stride_head <= 0 || p.kv_stride_page % 8 ||
       p.kv_stride_token % 8 || p.kv_stride_head % 8)
     return fail(CA_EUNSUPPORTED, "KV strides must be positive multiples of 8 elements");
+  if (p.kv_stride_token > (int64_t(1) << 26)) return fail(CA_EUNSUPPORTED, "kv_stride_token must be <= 2^26");
   if (p.mode < CA_MODE_AUTO || p.mode > CA_MODE_FORCE_OFF) return fail(CA_EINVAL, "unknown mode");
 
   const int32_t n = p.num_reqs, ps = p.page_size, stride = p.block_table_stride;

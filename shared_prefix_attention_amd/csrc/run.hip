@@ -69,7 +69,7 @@ ca_status_t check_launch(const char* what) {
 
 template <int D, int RB, int RW, int KG, int NS>
 void launch_tile(const TileArgs& args, int grid, hipStream_t s, int kind) {
-  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS>, dim3(grid), dim3(64 * RW * KG), s, args);
+  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64>, dim3(grid), dim3(64 * RW * KG), s, args);
 }
 
 template <int D, int RB, int RW, int KG>
@@ -103,13 +103,21 @@ ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hi
   return check_launch("attention kernel launch");
 }
 
-template <int D, int P, int S>
-void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, hipStream_t s) {
+// Prefix role: pipeline of 4 stages x 32 keys (deep enough to cover HBM
+// latency) or 2 x 64; suffix role: 2 stages x 64 keys. Both 64 KB of LDS.
+template <int D, int P, int S, int PNS, int PSK>
+void launch_phases_cfg(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, hipStream_t s) {
   constexpr int PRB = P == 1 ? 2 : 1;
   constexpr int PRW = P == 3 ? 2 : 4, PKG = P == 3 ? 2 : 1;
   constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
-  launch(K_PHASES, cascade_phases_kernel<D, PRB, PRW, PKG, 1, SRW, SKG, 2>, dim3(grid), dim3(256), s, pa, sa,
-         n_prefix);
+  launch(K_PHASES, cascade_phases_kernel<D, PRB, PRW, PKG, PNS, PSK, 1, SRW, SKG, 2, 64>, dim3(grid), dim3(256), s,
+         pa, sa, n_prefix);
+}
+
+template <int D, int P, int S>
+void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, int ns, hipStream_t s) {
+  if (ns == 4) launch_phases_cfg<D, P, S, 4, 32>(pa, sa, n_prefix, grid, s);
+  else launch_phases_cfg<D, P, S, 2, 64>(pa, sa, n_prefix, grid, s);
 }
 
 template <int D>
@@ -121,13 +129,13 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
   if (pid < 0 || pid == 2 || (sid != 0 && sid != 2)) return fail(CA_EINVAL, "unsupported work-group shape in plan");
   const int grid = (int)(n_prefix + n_suffix);
   if (sid == 0) {
-    if (pid == 0) launch_phases<D, 0, 0>(pa, sa, (int)n_prefix, grid, s);
-    else if (pid == 1) launch_phases<D, 1, 0>(pa, sa, (int)n_prefix, grid, s);
-    else launch_phases<D, 3, 0>(pa, sa, (int)n_prefix, grid, s);
+    if (pid == 0) launch_phases<D, 0, 0>(pa, sa, (int)n_prefix, grid, pp.stages, s);
+    else if (pid == 1) launch_phases<D, 1, 0>(pa, sa, (int)n_prefix, grid, pp.stages, s);
+    else launch_phases<D, 3, 0>(pa, sa, (int)n_prefix, grid, pp.stages, s);
   } else {
-    if (pid == 0) launch_phases<D, 0, 2>(pa, sa, (int)n_prefix, grid, s);
-    else if (pid == 1) launch_phases<D, 1, 2>(pa, sa, (int)n_prefix, grid, s);
-    else launch_phases<D, 3, 2>(pa, sa, (int)n_prefix, grid, s);
+    if (pid == 0) launch_phases<D, 0, 2>(pa, sa, (int)n_prefix, grid, pp.stages, s);
+    else if (pid == 1) launch_phases<D, 1, 2>(pa, sa, (int)n_prefix, grid, pp.stages, s);
+    else launch_phases<D, 3, 2>(pa, sa, (int)n_prefix, grid, pp.stages, s);
   }
   return check_launch("cascade phases kernel launch");
 }
