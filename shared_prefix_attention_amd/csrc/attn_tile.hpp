@@ -112,16 +112,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-__device__ __forceinline__ u32x4_t lds_load16(uint32_t addr) {
-  return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)addr;
+// LDS reads through inline asm: the compiler does not track them, so it
+// neither inserts waits of its own (the builtin transpose read would make it
+// wait for every in-flight LDS DMA, vmcnt 0) nor interleaves them with their
+// consumers. Their results must pass through lds_wait_regs() before use.
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// 16-key block kb of a K tile (key rows STRIDE bytes apart), kb a constant
+// after unrolling
+template <int STRIDE>
+__device__ __forceinline__ u32x4_t lds_read_b128_kb(uint32_t addr, int kb) {
+  switch (kb) {
+    case 0: return lds_read_b128<0>(addr);
+    case 1: return lds_read_b128<16 * STRIDE>(addr);
+    case 2: return lds_read_b128<32 * STRIDE>(addr);
+    default: return lds_read_b128<48 * STRIDE>(addr);
+  }
 }
 
-// ds_read_b64_tr_b16 through inline asm: the builtin form makes the compiler
-// wait for every in-flight LDS DMA before it (vmcnt 0). The compiler does not
-// track this read, so its result must pass through lds_wait_regs() before use.
-// Within each 16-lane group, lane 4*j + c supplies the address of row j,
-// columns [4c, 4c+4) of a 4 x 16 block of 16-bit values; lane i receives
-// column i of the four rows.
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4*j + c supplies the
+// address of row j, columns [4c, 4c+4) of a 4 x 16 block of 16-bit values;
+// lane i receives column i of the four rows.
 template <int OFF = 0>
 __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
@@ -130,23 +146,24 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
   return r;
 }
 
+// Pins a value in program order: code that produces it stays above, code
+// that consumes it stays below (inline asm statements keep their order).
+template <typename T>
+__device__ __forceinline__ void reg_fence(T& x) {
+  asm volatile("" : "+v"(x));
+}
+template <typename T, int N>
+__device__ __forceinline__ void reg_fence(T (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) reg_fence(x[i]);
+}
+
 // Waits for this wave's LDS reads and makes the registers that received them
 // outputs of the wait, so no consumer can be scheduled above it.
-template <int N>
-__device__ __forceinline__ void lds_wait_regs(u32x4_t (&r)[N]) {
-  static_assert(N == 2 || N == 4 || N == 8, "register batch");
-  if constexpr (N == 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1])::"memory");
-  } else if constexpr (N == 4) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])::"memory");
-  } else {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
-                 :: "memory");
-  }
-}
-__device__ __forceinline__ void lds_wait_regs(u32x2_t (&r)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])::"memory");
+template <typename T, int N>
+__device__ __forceinline__ void lds_wait_regs(T (&r)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  reg_fence(r);
 }
 
 // Work-group barrier without the memory fences of __syncthreads() (which
@@ -178,7 +195,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   constexpr int BLK_PER_WAVE = BLK / W;
   constexpr int OPS = 2 * BLK_PER_WAVE;   // vector-memory ops per wave per stage
   constexpr int NKB = SK / 16 / KG;       // 16-key blocks per wave per stage
-  static_assert(NKB >= 1 && SK % (16 * KG) == 0, "each wave needs whole 16-key blocks");
+  static_assert((NKB == 1 || NKB == 2 || NKB == 4) && SK % (16 * KG) == 0, "each wave needs 1, 2 or 4 16-key blocks");
   constexpr int ROWB = D * 2;             // LDS bytes per key row
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
   using SM = TileSmem<D, NS, SK>;
@@ -351,26 +368,38 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     const uint32_t lds_v = lds_k + SM::TILE_BYTES;
     const int kt0 = key_begin + t * SK;
     const int wpos = kt0 + wave * KPW;
+    // positions past the item re-read its last position, which lies in this
+    // wave's page or, if the whole range is past it, in last_pid
+    const int pid = wpos < key_end ? stage_pid(t) : last_pid;
+    const int64_t pg = (int64_t)pid * a.sp * 2;
+    const uint8_t* kb = k_head + pg;
+    const uint8_t* vb = v_head + pg;
     if (wpos + KPW <= key_end) {
-      const int64_t pg = (int64_t)stage_pid(t) * a.sp * 2;
+      // fresh 32-bit offsets, all live at once: each address is (scalar base
+      // + its own lane offset), so no VGPR is rewritten while an earlier DMA
+      // may still be waiting to read it
+      uint32_t ko[BLK_PER_WAVE], vo[BLK_PER_WAVE];
 #pragma unroll
       for (int i = 0; i < BLK_PER_WAVE; ++i) {
-        lds_dma16(k_head + pg + dma_koff[i], lds_k + i * 1024);
-        lds_dma16(v_head + pg + dma_voff[i], lds_v + i * 1024);
+        ko[i] = dma_koff[i];
+        vo[i] = dma_voff[i];
+      }
+      reg_fence(ko);
+      reg_fence(vo);
+#pragma unroll
+      for (int i = 0; i < BLK_PER_WAVE; ++i) {
+        lds_dma16(kb + ko[i], lds_k + i * 1024);
+        lds_dma16(vb + vo[i], lds_v + i * 1024);
       }
     } else {
-      // last stage: positions past the item re-read its last position, which
-      // lies in this wave's page or, if the whole range is past it, in last_pid
-      const int pid = wpos < key_end ? stage_pid(t) : last_pid;
-      const int64_t pg = (int64_t)pid * a.sp * 2;
 #pragma unroll
       for (int i = 0; i < BLK_PER_WAVE; ++i) {
         const int key = wave * KPW + i * KPB + lane / CPR;
         const int slot = min(kt0 + key, key_end - 1) & 15;
         const uint32_t ko = (uint32_t)((slot * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
         const uint32_t vo = (uint32_t)((slot * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
-        lds_dma16(k_head + pg + ko, lds_k + i * 1024);
-        lds_dma16(v_head + pg + vo, lds_v + i * 1024);
+        lds_dma16(kb + ko, lds_k + i * 1024);
+        lds_dma16(vb + vo, lds_v + i * 1024);
       }
     }
   };
@@ -391,39 +420,82 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     // and iteration i >= 1 issued stage i + NS - 1
     wait_stage(t == 0 ? min(NS - 1, n_tiles - 1) : min(NS - 2, n_tiles - 1 - t));
     block_barrier();
+    // The next stage's DMA goes into the buffer every wave finished with
+    // before this barrier. Active waves issue it once their S^T MFMAs and V
+    // reads are queued, so waiting for the address unit overlaps them.
+    // The next stage goes into the buffer every wave finished with before
+    // this barrier.
     if (t >= 1 && t + NS - 1 < n_tiles) issue_stage(t + NS - 1);
     if (wave_active) {
       const uint32_t stage = smem_base + (t % NS) * SM::STAGE_BYTES;
       const uint32_t sK = stage + kg * NKB * 16 * ROWB;
       const uint32_t sV = stage + SM::TILE_BYTES + kg * NKB * 16 * ROWB;
       const int kt0 = key_begin + t * SK + kg * NKB * 16;   // first key of this wave's group
-      // S^T = K Q^T for NKB blocks of 16 keys
+      // S^T = K Q^T for NKB blocks of 16 keys. All K fragments of the stage
+      // are read before one wait; the MFMA chains of the blocks interleave.
+      u32x4_t kf[NKB * KC];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) kf[kb * KC + kc] = lds_read_b128_kb<ROWB>(sK + k_off[kc], kb);
+      lds_wait_regs(kf);
       f32x4_t s[NKB][RB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const u32x4_t kf = lds_load16(sK + kb * 16 * ROWB + k_off[kc]);
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[kb][rb] = mfma16x16x32(kf, qf[rb][kc], s[kb][rb]);
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[kb][rb] = mfma16x16x32(kf[kb * KC + kc], qf[rb][kc], s[kb][rb]);
+      // V^T fragments do not depend on the softmax: read them now so that
+      // their latency overlaps it. The transpose load gives lane lr of group
+      // lq, for keys kb*16 + 4*lq + (0..3), the values at d = db*16 + lr.
+      // For 32-key MFMAs, k-slot (lq, j) <-> key kk*32 + (j < 4 ? 4*lq + j :
+      // 16 + 4*lq + j - 4), the map the S^T accumulators give P^T.
+      // With two row blocks the fragments are read in two halves of d (the
+      // second after the first is consumed) to stay within 256 VGPRs.
+      constexpr int NKK = NKB >= 2 ? NKB / 2 : 1;
+      constexpr int VH = (RB >= 2 && NKB >= 2) ? 2 : 1;   // d halves
+      constexpr int DBV = DB / VH;                          // d blocks per half
+      u32x4_t vf[NKB >= 2 ? DBV * NKK : 1];
+      u32x2_t vh[NKB == 1 ? DB : 1];
+      auto read_v = [&](int half) {
+#pragma unroll
+        for (int i = 0; i < DBV; ++i) {
+          const uint32_t va = sV + v_off[half * DBV + i];
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const u32x2_t h0 = kk == 0 ? lds_read_tr16<0>(va) : lds_read_tr16<32 * ROWB>(va);
+            const u32x2_t h1 = kk == 0 ? lds_read_tr16<16 * ROWB>(va) : lds_read_tr16<48 * ROWB>(va);
+            vf[i * NKK + kk] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+          }
         }
+      };
+      if constexpr (NKB == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vh[db] = lds_read_tr16(sV + v_off[db]);
+      } else {
+        read_v(0);
       }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) reg_fence(s[kb]);   // softmax below the V reads
       // online softmax over this wave's keys of the stage, per row (lane lr)
       const bool need_mask = (kt0 + NKB * 16 > key_end) || (kt0 + NKB * 16 - 1 > all_visible_to);
       u32x2_t pb[RB][NKB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (need_mask) {
+          // key kt0 + kb*16 + lq*4 + i is visible iff it is below both the
+          // item end and (causal) the row's position + 1
+          const int lim = causal ? min(key_end, row_qpos[rb] + 1) : key_end;
+          const int rem = lim - (kt0 + lq * 4);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kpos = kt0 + kb * 16 + lq * 4 + i;
-              const bool vis = kpos < key_end && (!causal || kpos <= row_qpos[rb]);
-              s[kb][rb][i] = vis ? s[kb][rb][i] : -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i) s[kb][rb][i] = (kb * 16 + i < rem) ? s[kb][rb][i] : -INFINITY;
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -452,48 +524,29 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
           for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
         }
       }
-      // O^T += V^T P^T. The transpose load gives lane lr of group lq, for
-      // keys kb*16 + 4*lq + (0..3), the values at d = db*16 + lr.
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) reg_fence(pb[rb]);   // softmax done before the V wait
+      // O^T += V^T P^T
       if constexpr (NKB == 1) {
+        lds_wait_regs(vh);
 #pragma unroll
-        for (int dh = 0; dh < DB / 4; ++dh) {
-          u32x2_t vr[4];
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vr[i] = lds_read_tr16(sV + v_off[dh * 4 + i]);
-          lds_wait_regs(vr);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) o[dh * 4 + i][rb] = mfma16x16x16(vr[i], pb[rb][0], o[dh * 4 + i][rb]);
-        }
+          for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma16x16x16(vh[db], pb[rb][0], o[db][rb]);
       } else {
-        // 32 keys per MFMA: k-slot (lq, j) <-> key kk*32 + (j < 4 ? 4*lq + j
-        // : 16 + 4*lq + j - 4), the map the S^T accumulators give P^T.
-        constexpr int NKK = NKB / 2;
-        constexpr int DBH = DB / 2;
 #pragma unroll
-        for (int dh = 0; dh < 2; ++dh) {
-          u32x4_t vf[DBH * NKK];
-#pragma unroll
-          for (int dbi = 0; dbi < DBH; ++dbi) {
-            const uint32_t va = sV + v_off[dh * DBH + dbi];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-              const u32x2_t h0 = kk == 0 ? lds_read_tr16<0>(va) : lds_read_tr16<32 * ROWB>(va);
-              const u32x2_t h1 = kk == 0 ? lds_read_tr16<16 * ROWB>(va) : lds_read_tr16<48 * ROWB>(va);
-              vf[dbi * NKK + kk] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
-            }
-          }
+        for (int half = 0; half < VH; ++half) {
+          if (half > 0) read_v(half);
           lds_wait_regs(vf);
 #pragma unroll
-          for (int dbi = 0; dbi < DBH; ++dbi)
+          for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
+            for (int i = 0; i < DBV; ++i)
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb) {
                 const u32x4_t pk = u32x4_t{pb[rb][2 * kk][0], pb[rb][2 * kk][1], pb[rb][2 * kk + 1][0],
                                            pb[rb][2 * kk + 1][1]};
-                o[dh * DBH + dbi][rb] = mfma16x16x32(vf[dbi * NKK + kk], pk, o[dh * DBH + dbi][rb]);
+                o[half * DBV + i][rb] = mfma16x16x32(vf[i * NKK + kk], pk, o[half * DBV + i][rb]);
               }
         }
       }

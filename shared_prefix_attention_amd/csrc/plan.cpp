@@ -71,7 +71,6 @@ struct CostModel {
 //   kDecodeConfig 16 rows (1 wave), each stage split over 4 key groups;
 //                 for suffixes whose rows (q_len * G) fit one MFMA block.
 static PhaseTile rows_config() { PhaseTile t; t.row_blocks = 1; t.row_waves = 4; t.key_groups = 1; return t; }
-static PhaseTile half_rows_config() { PhaseTile t; t.row_blocks = 1; t.row_waves = 2; t.key_groups = 2; return t; }
 static PhaseTile mfma_config() { PhaseTile t; t.row_blocks = 2; t.row_waves = 4; t.key_groups = 1; return t; }
 static PhaseTile decode_config() {
   PhaseTile t;

@@ -81,9 +81,8 @@ void launch_tile_ns(const TileArgs& args, int ns, int grid, hipStream_t s, int k
 bool item_ok(const PhaseTile& ph) { return ph.split_tokens > 0 && ph.split_tokens <= kMaxItemTokens && ph.split_tokens % kTileKeys == 0; }
 
 // 4-wave work-group shapes (row_blocks, row_waves, key_groups):
-// 0 = rows (1,4,1), 1 = MFMA (2,4,1), 2 = decode (1,1,4), 3 = half rows (1,2,2)
+// 0 = rows (1,4,1), 1 = MFMA (2,4,1), 2 = decode (1,1,4)
 int shape_id(const PhaseTile& ph) {
-  if (ph.row_blocks == 1 && ph.row_waves == 2 && ph.key_groups == 2) return 3;
   if (ph.row_blocks == 1 && ph.row_waves == 4 && ph.key_groups == 1) return 0;
   if (ph.row_blocks == 2 && ph.row_waves == 4 && ph.key_groups == 1) return 1;
   if (ph.row_blocks == 1 && ph.row_waves == 1 && ph.key_groups == 4) return 2;
@@ -103,21 +102,13 @@ ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hi
   return check_launch("attention kernel launch");
 }
 
-// Prefix role: pipeline of 4 stages x 32 keys (deep enough to cover HBM
-// latency) or 2 x 64; suffix role: 2 stages x 64 keys. Both 64 KB of LDS.
-template <int D, int P, int S, int PNS, int PSK>
-void launch_phases_cfg(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, hipStream_t s) {
-  constexpr int PRB = P == 1 ? 2 : 1;
-  constexpr int PRW = P == 3 ? 2 : 4, PKG = P == 3 ? 2 : 1;
-  constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
-  launch(K_PHASES, cascade_phases_kernel<D, PRB, PRW, PKG, PNS, PSK, 1, SRW, SKG, 2, 64>, dim3(grid), dim3(256), s,
-         pa, sa, n_prefix);
-}
-
+// Both roles: 2 stages x 64 keys (64 KB of LDS, two work-groups per CU).
 template <int D, int P, int S>
-void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, int ns, hipStream_t s) {
-  if (ns == 4) launch_phases_cfg<D, P, S, 4, 32>(pa, sa, n_prefix, grid, s);
-  else launch_phases_cfg<D, P, S, 2, 64>(pa, sa, n_prefix, grid, s);
+void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, hipStream_t s) {
+  constexpr int PRB = P == 1 ? 2 : 1;
+  constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
+  launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, 2, 64, 1, SRW, SKG, 2, 64>, dim3(grid), dim3(256), s,
+         pa, sa, n_prefix);
 }
 
 template <int D>
@@ -126,16 +117,16 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
   if (n_prefix + n_suffix > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(pp) || !item_ok(sp)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   const int pid = shape_id(pp), sid = shape_id(sp);
-  if (pid < 0 || pid == 2 || (sid != 0 && sid != 2)) return fail(CA_EINVAL, "unsupported work-group shape in plan");
+  if ((pid != 0 && pid != 1) || (sid != 0 && sid != 2) || pp.stages != 2 || sp.stages != 2)
+    return fail(CA_EINVAL, "unsupported work-group shape in plan");
   const int grid = (int)(n_prefix + n_suffix);
+  const int np = (int)n_prefix;
   if (sid == 0) {
-    if (pid == 0) launch_phases<D, 0, 0>(pa, sa, (int)n_prefix, grid, pp.stages, s);
-    else if (pid == 1) launch_phases<D, 1, 0>(pa, sa, (int)n_prefix, grid, pp.stages, s);
-    else launch_phases<D, 3, 0>(pa, sa, (int)n_prefix, grid, pp.stages, s);
+    if (pid == 0) launch_phases<D, 0, 0>(pa, sa, np, grid, s);
+    else launch_phases<D, 1, 0>(pa, sa, np, grid, s);
   } else {
-    if (pid == 0) launch_phases<D, 0, 2>(pa, sa, (int)n_prefix, grid, pp.stages, s);
-    else if (pid == 1) launch_phases<D, 1, 2>(pa, sa, (int)n_prefix, grid, pp.stages, s);
-    else launch_phases<D, 3, 2>(pa, sa, (int)n_prefix, grid, pp.stages, s);
+    if (pid == 0) launch_phases<D, 0, 2>(pa, sa, np, grid, s);
+    else launch_phases<D, 1, 2>(pa, sa, np, grid, s);
   }
   return check_launch("cascade phases kernel launch");
 }
