@@ -81,6 +81,22 @@ def time_steps(fn, steps, rotate):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def step_distribution(fn, steps, rotate):
+    """Per-step GPU time (us) from events recorded around every run on the
+    stream the runs use; returns p10 / median / p90."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        fn(i % rotate)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    pick = lambda q: round(us[min(len(us) - 1, int(q * (len(us) - 1) + 0.5))], 3)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
 def cpu_baseline(b, kv_bytes, budget_s=15.0, max_runs=60):
     """The fp64 oracle (test infrastructure) on this host, one BLAS thread,
     over the whole batch, repeated for about budget_s seconds."""
@@ -208,6 +224,7 @@ def main():
     for i in range(args.warmup):
         step(i % rotate)
     ms = time_steps(step, args.steps, rotate)
+    dist = step_distribution(step, args.steps, rotate)
 
     # per-kernel durations: HIP events around every launch, on the run's stream
     spa.cascade_attn_profile_enable(True)
@@ -267,6 +284,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "us_per_step": round(ms * 1e3, 3),
+        "us_per_step_events": dist,
         "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
