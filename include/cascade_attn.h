@@ -86,7 +86,9 @@ typedef struct {
   float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
   int32_t mode;                /* ca_mode_t */
   int32_t num_cus;             /* compute units to plan for; 0 = query the current device */
-  int32_t reserved1;
+  int32_t heads_per_item;      /* KV heads one decode-shaped suffix item runs back to back
+                                  (0 = planner's choice; else must divide num_kv_heads;
+                                  ignored for items of more than 16 rows) */
 } ca_params_t;
 
 typedef struct {
@@ -103,7 +105,7 @@ typedef struct {
   int32_t prefix_stages;               /* LDS pipeline depth of the prefix kernel */
   int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
   int32_t merge_in_suffix;             /* 1: the suffix kernel merges and writes the output */
-  int32_t reserved0;
+  int32_t suffix_heads_per_item;       /* consecutive KV heads one suffix (or only) work item runs */
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
   int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */

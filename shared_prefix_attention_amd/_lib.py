@@ -44,7 +44,7 @@ class ca_params_t(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("mode", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
-        ("reserved1", ctypes.c_int32),
+        ("heads_per_item", ctypes.c_int32),
     ]
 
 
@@ -63,7 +63,7 @@ class ca_plan_info_t(ctypes.Structure):
         ("prefix_stages", ctypes.c_int32),
         ("suffix_stages", ctypes.c_int32),
         ("merge_in_suffix", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("suffix_heads_per_item", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("kv_tokens_cascade", ctypes.c_int64),
@@ -175,7 +175,7 @@ class Plan:
 def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                       num_pages: int, kv_strides, block_table, query_start_loc, seq_lens,
                       num_computed_tokens=None, softmax_scale: float = 0.0, mode="auto",
-                      num_cus: int = 0) -> Plan:
+                      num_cus: int = 0, heads_per_item: int = 0) -> Plan:
     """Host-only planner (see cascade_attn_plan in the header).
 
     kv_strides: (page, token-slot, head) element strides of the K/V caches.
@@ -202,6 +202,7 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
     prm.softmax_scale = float(softmax_scale)
     prm.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
     prm.num_cus = int(num_cus)
+    prm.heads_per_item = int(heads_per_item)
     h = ctypes.c_void_p(0)
     _check(load().cascade_attn_plan(ctypes.byref(prm), bt_p, qsl_p, sl_p, nc_p, ctypes.byref(h)))
     return Plan(h.value)

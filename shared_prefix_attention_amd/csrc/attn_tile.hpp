@@ -60,6 +60,7 @@ struct TileArgs {
   int32_t num_reqs;
   int32_t mtiles;               // row tiles (prefix) / max row tiles per request
   int32_t splits;               // KV splits (prefix) / chunks per request
+  int32_t heads_per_item;       // per-request phase: consecutive KV heads one item runs (divides hkv)
   int32_t split_tokens;         // multiple of 64, <= kMaxItemPages * 16
   float* part_o;                // [slots][T][hq][D] fp32 (partial mode)
   float* part_lse;              // [slots][T][hq] fp32, natural log
@@ -181,7 +182,9 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
                                                    0, 0, 0);
 }
 
-template <int D, int RB, int RW, int KG, int NS, int SK>
+// MH: the item may cover several consecutive KV heads of one request (same
+// pages and key range), run as one continuous stage pipeline.
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
@@ -199,7 +202,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   constexpr int ROWB = D * 2;             // LDS bytes per key row
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
   using SM = TileSmem<D, NS, SK>;
-  static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= NS * SM::STAGE_BYTES, "merge scratch");
+  // the key-group states are combined in the stage buffer just consumed
+  static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= SM::STAGE_BYTES, "merge scratch");
   int32_t* s_pages = reinterpret_cast<int32_t*>(smem + NS * SM::STAGE_BYTES);
 
   const int tid = threadIdx.x;
@@ -215,17 +219,18 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   // of the item's KV range are fetched speculatively (the block-table row is
   // known before the lengths are) in the same round trip as the per-request
   // lengths; entries past the request's pages are read but never used.
-  int g, row_begin, row_end, key_begin, key_end, slot;
+  int g0, row_begin, row_end, key_begin, key_end, slot;
   int tok_base = 0, q_pos_base = 0;      // token of row 0, causal position of row 0's token
   bool causal;
   const int32_t* bt_row;
   int req = 0, c = 0, mt = 0;
+  const int H = MH ? a.heads_per_item : 1;   // KV heads g0 .. g0 + H - 1, one after another
   if (a.prefix_mode) {
     const int kv_items = a.hkv * a.splits;
     mt = bid / kv_items;
     const int kvi = bid - mt * kv_items;
-    g = kvi / a.splits;
-    c = kvi - g * a.splits;
+    g0 = kvi / a.splits;
+    c = kvi - g0 * a.splits;
     key_begin = c * a.split_tokens;
     causal = false;
     bt_row = a.bt;
@@ -234,8 +239,9 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     int rest = bid / a.splits;
     mt = rest % a.mtiles;
     rest /= a.mtiles;
-    g = rest % a.hkv;
-    req = rest / a.hkv;
+    const int groups = a.hkv / H;
+    g0 = (rest % groups) * H;
+    req = rest / groups;
     key_begin = a.key_start + c * a.split_tokens;
     causal = true;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
@@ -275,43 +281,51 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   __syncthreads();
 
   // ------------------------------------------------- per-lane query rows
-  // Loaded before the K/V stages are issued, so waiting for the first stage
-  // also waits for Q.
+  // Row m of the tile is (token m / G, head-in-group m % G); the query head
+  // of KV head g is g*G + m % G. Q of the first head is loaded before the
+  // K/V stages are issued, so waiting for the first stage also waits for it.
   const int wrow0 = row_begin + rw * 16 * RB;
   const bool wave_active = wrow0 < row_end;
-  u32x4_t qf[RB][KC];
-  int row_tok[RB], row_head[RB], row_qpos[RB];
+  int row_tok[RB], row_j[RB], row_qpos[RB];
   bool row_ok[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int m = wrow0 + rb * 16 + lr;
     row_ok[rb] = m < row_end;
     const int t_in = m / a.group;
-    const int j = m - t_in * a.group;
+    row_j[rb] = m - t_in * a.group;
     row_tok[rb] = tok_base + t_in;
-    row_head[rb] = g * a.group + j;
     row_qpos[rb] = q_pos_base + t_in;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (row_ok[rb]) {
-        qf[rb][kc] = load16(a.q + ((int64_t)row_tok[rb] * a.hq + row_head[rb]) * D + kc * 32 + lq * 8);
-      } else {
-        qf[rb][kc] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
   }
+  auto load_q = [&](int g, u32x4_t (&q)[RB][KC]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (row_ok[rb]) {
+          q[rb][kc] = load16(a.q + ((int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb]) * D + kc * 32 + lq * 8);
+        } else {
+          q[rb][kc] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+  };
+  u32x4_t qf[RB][KC];
+  load_q(g0, qf);
 
   f32x4_t o[DB][RB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[RB], l_run[RB];
+  auto reset_state = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
-  }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m_run[rb] = -INFINITY;
+      l_run[rb] = 0.f;
+    }
+  };
+  reset_state();
 
   // Lane-constant parts of the LDS operand addresses (the XOR swizzle
   // depends on key mod 16 only, so 16-key blocks differ by a constant).
@@ -361,19 +375,22 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     dma_koff[i] = (uint32_t)(((key & 15) * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
     dma_voff[i] = (uint32_t)(((key & 15) * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
   }
-  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(a.k) + (int64_t)g * a.sh * 2;
-  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(a.v) + (int64_t)g * a.sh * 2;
-  auto issue_stage = [&](int t) {
-    const uint32_t lds_k = smem_base + (t % NS) * SM::STAGE_BYTES + wave * BLK_PER_WAVE * 1024;
+  // Stage u of the item is tile t of head h (u = h * n_tiles + t); stages are
+  // issued in order, so the issue position advances one (h, t) at a time.
+  int iss_u = 0, iss_h = 0, iss_t = 0;
+  auto issue_next = [&]() {
+    const int t = iss_t;
+    const int64_t head_bytes = (int64_t)(g0 + iss_h) * a.sh * 2;
+    const uint32_t lds_k = smem_base + (iss_u % NS) * SM::STAGE_BYTES + wave * BLK_PER_WAVE * 1024;
     const uint32_t lds_v = lds_k + SM::TILE_BYTES;
     const int kt0 = key_begin + t * SK;
     const int wpos = kt0 + wave * KPW;
     // positions past the item re-read its last position, which lies in this
     // wave's page or, if the whole range is past it, in last_pid
     const int pid = wpos < key_end ? stage_pid(t) : last_pid;
-    const int64_t pg = (int64_t)pid * a.sp * 2;
-    const uint8_t* kb = k_head + pg;
-    const uint8_t* vb = v_head + pg;
+    const int64_t pg = (int64_t)pid * a.sp * 2 + head_bytes;
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + pg;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + pg;
     if (wpos + KPW <= key_end) {
       // fresh 32-bit offsets, all live at once: each address is (scalar base
       // + its own lane offset), so no VGPR is rewritten while an earlier DMA
@@ -395,12 +412,17 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
 #pragma unroll
       for (int i = 0; i < BLK_PER_WAVE; ++i) {
         const int key = wave * KPW + i * KPB + lane / CPR;
-        const int slot = min(kt0 + key, key_end - 1) & 15;
-        const uint32_t ko = (uint32_t)((slot * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
-        const uint32_t vo = (uint32_t)((slot * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
+        const int slot_t = min(kt0 + key, key_end - 1) & 15;
+        const uint32_t ko = (uint32_t)((slot_t * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
+        const uint32_t vo = (uint32_t)((slot_t * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
         lds_dma16(kb + ko, lds_k + i * 1024);
         lds_dma16(vb + vo, lds_v + i * 1024);
       }
+    }
+    ++iss_u;
+    if (++iss_t == n_tiles) {
+      iss_t = 0;
+      ++iss_h;
     }
   };
   auto wait_stage = [&](int after) {   // `after` stages were issued after the one needed
@@ -410,24 +432,107 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     else wait_vmcnt<0>();
   };
 
-  // All NS buffers are filled up front; afterwards stage t + NS - 1 goes into
-  // the buffer that stage t - 1 used, once every wave is past stage t's barrier.
-  const int pro = min(NS, n_tiles);
-  for (int t = 0; t < pro; ++t) issue_stage(t);
+  // All NS buffers are filled up front; afterwards stage u + NS - 1 goes into
+  // the buffer that stage u - 1 used, once every wave is past stage u's barrier.
+  const int U = H * n_tiles;
+  const int pro = min(NS, U);
+  for (int p = 0; p < pro; ++p) issue_next();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    // stages issued after stage t so far: the prologue filled NS buffers,
+  // ------------------------------------------------- end of one KV head
+  // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). Waves
+  // kg > 0 publish theirs in the stage buffer every wave has just finished
+  // with (the DMA in flight targets the other buffers); wave kg = 0 of each
+  // row block folds them in and writes the head's rows.
+  auto finish_head = [&](int g, int buf) {
+    if constexpr (KG > 1) {
+      constexpr int SLOT_F = 16 * RB * XS_ROW;   // floats per published wave state
+      float* xs = reinterpret_cast<float*>(smem + buf * SM::STAGE_BYTES);
+      block_barrier();                           // every wave is done with this buffer
+      if (kg > 0 && wave_active) {
+        float* my = xs + ((kg - 1) * RW + rw) * SLOT_F;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float* r = my + (rb * 16 + lr) * XS_ROW;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(r + db * 16 + lq * 4) = o[db][rb];
+          const float l_tot = wave_sum_across_quads(l_run[rb]);
+          if (lq == 0) {
+            r[D] = m_run[rb];
+            r[D + 1] = l_tot;
+          }
+        }
+      }
+      block_barrier();                           // states published
+      if (kg == 0 && wave_active) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float l_tot = wave_sum_across_quads(l_run[rb]);
+          float m = m_run[rb];
+#pragma unroll
+          for (int k2 = 1; k2 < KG; ++k2) {
+            const float* r = xs + ((k2 - 1) * RW + rw) * SLOT_F + (rb * 16 + lr) * XS_ROW;
+            const float m2 = r[D], l2 = r[D + 1];
+            const float mn = vmax(m, m2);
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            const float a1 = __builtin_amdgcn_exp2f(m - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              o[db][rb] = o[db][rb] * a1 + *reinterpret_cast<const f32x4_t*>(r + db * 16 + lq * 4) * a2;
+            l_tot = l_tot * a1 + l2 * a2;
+            m = mn;
+          }
+          m_run[rb] = m;
+          // the combined sum sits in lane group 0 so the epilogue's quad sum
+          // reproduces it
+          l_run[rb] = (lq == 0) ? l_tot : 0.f;
+        }
+      }
+    }
+    if (!wave_active || (KG > 1 && kg > 0)) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = wave_sum_across_quads(l_run[rb]);
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.f / l_tot : 0.f;
+      const float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      if (!row_ok[rb]) continue;
+      const int64_t row = (int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb];
+      if (a.direct) {
+        f32x4_t acc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = o[db][rb] * inv;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<u32x2_t*>(a.out + row * D + db * 16 + lq * 4) =
+              u32x2_t{pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
+        if (lq == 0 && a.lse_out) a.lse_out[row] = lse;
+      } else {
+        float* dst = a.part_o + (int64_t)slot * a.slot_elems + row * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(dst + db * 16 + lq * 4) = o[db][rb] * inv;
+        if (lq == 0) a.part_lse[(int64_t)slot * a.slot_rows + row] = lse;
+      }
+    }
+  };
+
+  // An empty KV range (a chunk past a short request's end) still writes its
+  // rows: o = 0, lse = -inf, which the merge ignores.
+  if (U == 0) {
+    for (int hh = 0; hh < H; ++hh) finish_head(g0 + hh, 0);
+    return;
+  }
+
+  int h = 0, t = 0;   // head and tile of stage u
+  for (int u = 0; u < U; ++u) {
+    // stages issued after stage u so far: the prologue filled NS buffers,
     // and iteration i >= 1 issued stage i + NS - 1
-    wait_stage(t == 0 ? min(NS - 1, n_tiles - 1) : min(NS - 2, n_tiles - 1 - t));
+    wait_stage(u == 0 ? min(NS - 1, U - 1) : min(NS - 2, U - 1 - u));
     block_barrier();
-    // The next stage's DMA goes into the buffer every wave finished with
-    // before this barrier. Active waves issue it once their S^T MFMAs and V
-    // reads are queued, so waiting for the address unit overlaps them.
-    // The next stage goes into the buffer every wave finished with before
-    // this barrier.
-    if (t >= 1 && t + NS - 1 < n_tiles) issue_stage(t + NS - 1);
+    // the next stage goes into the buffer every wave finished with before
+    // this barrier
+    if (u >= 1 && u + NS - 1 < U) issue_next();
+    const uint32_t stage = smem_base + (u % NS) * SM::STAGE_BYTES;
     if (wave_active) {
-      const uint32_t stage = smem_base + (t % NS) * SM::STAGE_BYTES;
       const uint32_t sK = stage + kg * NKB * 16 * ROWB;
       const uint32_t sV = stage + SM::TILE_BYTES + kg * NKB * 16 * ROWB;
       const int kt0 = key_begin + t * SK + kg * NKB * 16;   // first key of this wave's group
@@ -551,90 +656,32 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
         }
       }
     }
-  }
-
-  // ------------------------------------------- combine the key groups
-  // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). Waves
-  // kg > 0 publish theirs in LDS; wave kg = 0 of each row block folds them in.
-  // The stage buffers are free once every wave is past the loop.
-  if constexpr (KG > 1) {
-    constexpr int SLOT_F = 16 * RB * XS_ROW;   // floats per published wave state
-    float* xs = reinterpret_cast<float*>(smem);
-    __syncthreads();
-    if (kg > 0 && wave_active) {
-      float* my = xs + ((kg - 1) * RW + rw) * SLOT_F;
+    if (t == n_tiles - 1) {
+      // last tile of head g0 + h: the next head's Q is requested first so
+      // that its latency overlaps the combine
+      u32x4_t qn[RB][KC];
+      const bool more = MH && h + 1 < H;
+      if (more) load_q(g0 + h + 1, qn);
+      finish_head(g0 + h, u % NS);
+      if (more) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float* r = my + (rb * 16 + lr) * XS_ROW;
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(r + db * 16 + lq * 4) = o[db][rb];
-        const float l_tot = wave_sum_across_quads(l_run[rb]);
-        if (lq == 0) {
-          r[D] = m_run[rb];
-          r[D + 1] = l_tot;
-        }
+          for (int kc = 0; kc < KC; ++kc) qf[rb][kc] = qn[rb][kc];
+        reset_state();
       }
-    }
-    __syncthreads();
-    if (kg > 0) return;
-    if (wave_active) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float l_tot = wave_sum_across_quads(l_run[rb]);
-        float m = m_run[rb];
-#pragma unroll
-        for (int k2 = 1; k2 < KG; ++k2) {
-          const float* r = xs + ((k2 - 1) * RW + rw) * SLOT_F + (rb * 16 + lr) * XS_ROW;
-          const float m2 = r[D], l2 = r[D + 1];
-          const float mn = vmax(m, m2);
-          const float mu = (mn == -INFINITY) ? 0.f : mn;
-          const float a1 = __builtin_amdgcn_exp2f(m - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            o[db][rb] = o[db][rb] * a1 + *reinterpret_cast<const f32x4_t*>(r + db * 16 + lq * 4) * a2;
-          l_tot = l_tot * a1 + l2 * a2;
-          m = mn;
-        }
-        m_run[rb] = m;
-        // the combined sum sits in lane group 0 so the epilogue's quad sum
-        // reproduces it
-        l_run[rb] = (lq == 0) ? l_tot : 0.f;
-      }
-    }
-  }
-
-  // ------------------------------------------------------------ epilogue
-  if (!wave_active) return;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = wave_sum_across_quads(l_run[rb]);
-    const bool live = l_tot > 0.f;
-    const float inv = live ? 1.f / l_tot : 0.f;
-    const float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    if (!row_ok[rb]) continue;
-    const int64_t row = (int64_t)row_tok[rb] * a.hq + row_head[rb];
-    if (a.direct) {
-      f32x4_t acc[DB];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = o[db][rb] * inv;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<u32x2_t*>(a.out + row * D + db * 16 + lq * 4) =
-            u32x2_t{pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
-      if (lq == 0 && a.lse_out) a.lse_out[row] = lse;
+      ++h;
+      t = 0;
     } else {
-      float* dst = a.part_o + (int64_t)slot * a.slot_elems + row * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(dst + db * 16 + lq * 4) = o[db][rb] * inv;
-      if (lq == 0) a.part_lse[(int64_t)slot * a.slot_rows + row] = lse;
+      ++t;
     }
   }
 }
 
-template <int D, int RB, int RW, int KG, int NS, int SK>
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH>
 __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK>::BYTES];
-  attn_item<D, RB, RW, KG, NS, SK>(a, blockIdx.x, smem);
+  attn_item<D, RB, RW, KG, NS, SK, MH>(a, blockIdx.x, smem);
 }
 
 // One launch for both cascade phases: work-groups [0, n_prefix) run prefix
@@ -648,8 +695,8 @@ __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, 
   constexpr int PB = TileSmem<D, PNS, PSK>::BYTES, SB = TileSmem<D, SNS, SSK>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK>(pa, bid, smem);
-  else attn_item<D, SRB, SRW, SKG, SNS, SSK>(sa, bid - n_prefix, smem);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false>(pa, bid, smem);
+  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1)>(sa, bid - n_prefix, smem);
 }
 
 }  // namespace ca

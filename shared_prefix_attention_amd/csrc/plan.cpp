@@ -146,6 +146,28 @@ static PhaseTile choose_suffix(const ca_plan& pl, int32_t cus, bool fill) {
   return t;
 }
 
+// Decode-shaped items may run several consecutive KV heads of one request as
+// one stage pipeline (same pages and key range). Worth it when that keeps the
+// whole cascade launch within two resident work-groups per CU (no item waits
+// for a slot, and each item's first round trips are paid once for all its
+// heads) and the grouped item stays at most half as long as a prefix item: a
+// decode stage costs about one memory round trip, so longer chains become the
+// launch's critical path. Otherwise one head per item.
+static int32_t pick_heads_per_item(const ca_plan& pl, const PhaseTile& pre, const PhaseTile& suf, int32_t cus) {
+  if (suf.kernel != 1) return 1;
+  if (pl.p.heads_per_item > 0) return pl.p.heads_per_item;
+  const int64_t prefix_items = (int64_t)pre.mtiles * pl.hkv * pre.splits;
+  const int64_t per_head = (int64_t)pl.num_reqs * suf.mtiles * suf.splits;
+  const int64_t prefix_stages = pre.split_tokens / kTileKeys;
+  const int64_t suffix_stages = suf.split_tokens / kTileKeys;
+  for (int32_t h = 1; h <= pl.hkv && h <= 8; ++h) {
+    if (pl.hkv % h) continue;
+    if (prefix_items + per_head * (pl.hkv / h) <= 2 * (int64_t)cus)
+      return h * suffix_stages <= std::max<int64_t>(1, prefix_stages / 2) ? h : 1;
+  }
+  return 1;
+}
+
 // Per-request phase over KV positions [key_start, seq_len): HBM bytes for the
 // KV actually streamed, plus the MFMA work of 16-row padded query blocks.
 static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_flops, int32_t chunks, bool merge,
@@ -218,6 +240,8 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     return fail(CA_EUNSUPPORTED, "KV strides must be positive multiples of 8 elements");
   if (p.kv_stride_token > (int64_t(1) << 26)) return fail(CA_EUNSUPPORTED, "kv_stride_token must be <= 2^26");
   if (p.mode < CA_MODE_AUTO || p.mode > CA_MODE_FORCE_OFF) return fail(CA_EINVAL, "unknown mode");
+  if (p.heads_per_item < 0 || (p.heads_per_item > 0 && p.num_kv_heads % p.heads_per_item != 0))
+    return fail(CA_EINVAL, "heads_per_item must be 0 or divide num_kv_heads");
 
   const int32_t n = p.num_reqs, ps = p.page_size, stride = p.block_table_stride;
   if (qsl[0] != 0) return fail(CA_EMETA, "query_start_loc[0] must be 0");
@@ -325,6 +349,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->suffix = suf;
     pl->prefix.stages = 2;   // both phases share one launch (two work-groups per CU)
     pl->suffix.stages = 2;
+    pl->suffix.heads_per_item = pick_heads_per_item(*pl, pre, suf, cus);
     pl->merge_in_suffix = 0;
     pl->num_slots = pre.splits + suf.splits;
     pl->direct_out = false;
@@ -333,6 +358,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->max_suffix_len = max_seq;
     pl->prefix = PhaseTile{};
     pl->suffix = nc;
+    pl->suffix.heads_per_item = (nc.kernel == 1 && p.heads_per_item > 0) ? p.heads_per_item : 1;
     pl->merge_in_suffix = 0;
     pl->num_slots = nc.splits > 1 ? nc.splits : 0;
     pl->direct_out = nc.splits == 1;
@@ -367,6 +393,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->prefix_stages = pl->use_cascade ? pl->prefix.stages : 0;
   out->suffix_stages = pl->suffix.stages;
   out->merge_in_suffix = pl->merge_in_suffix;
+  out->suffix_heads_per_item = pl->suffix.heads_per_item;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

@@ -23,6 +23,7 @@ struct PhaseTile {
   int32_t split_tokens = 0;    // tokens per split / chunk (multiple of kTileKeys)
   int32_t kernel = 0;          // 0 = tiled rows, 1 = decode (rows <= 16, waves split the keys)
   int32_t stages = 2;          // LDS pipeline depth of the tiled kernel (2 or 4)
+  int32_t heads_per_item = 1;  // per-request phase, decode shape: consecutive KV heads one item runs
   int32_t rows_per_wg() const { return 16 * row_blocks * row_waves; }
 };
 

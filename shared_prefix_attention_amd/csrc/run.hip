@@ -69,7 +69,7 @@ ca_status_t check_launch(const char* what) {
 
 template <int D, int RB, int RW, int KG, int NS>
 void launch_tile(const TileArgs& args, int grid, hipStream_t s, int kind) {
-  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64>, dim3(grid), dim3(64 * RW * KG), s, args);
+  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, (KG > 1)>, dim3(grid), dim3(64 * RW * KG), s, args);
 }
 
 template <int D, int RB, int RW, int KG>
@@ -144,6 +144,7 @@ template <int D>
 ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void* v, const int32_t* bt,
                      const int32_t* qsl, const int32_t* sl, void* out, float* lse, void* ws, hipStream_t s) {
   TileArgs base{};
+  base.heads_per_item = 1;
   base.q = static_cast<const uint16_t*>(q);
   base.k = static_cast<const uint16_t*>(k);
   base.v = static_cast<const uint16_t*>(v);
@@ -175,9 +176,14 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   sa.mtiles = pl->suffix.mtiles;
   sa.splits = pl->suffix.splits;
   sa.split_tokens = pl->suffix.split_tokens;
+  sa.heads_per_item = pl->suffix.heads_per_item;
   sa.slot_base = pl->use_cascade ? pl->prefix.splits : 0;
   sa.direct = pl->direct_out ? 1 : 0;
-  const int64_t n_suffix = (int64_t)pl->num_reqs * sa.mtiles * pl->hkv * sa.splits;
+  // several KV heads per item only in the decode shape (its waves split the keys)
+  if (sa.heads_per_item < 1 || pl->hkv % sa.heads_per_item != 0 ||
+      (sa.heads_per_item > 1 && pl->suffix.key_groups == 1))
+    return fail(CA_EINVAL, "invalid heads per item in plan");
+  const int64_t n_suffix = (int64_t)pl->num_reqs * sa.mtiles * (pl->hkv / sa.heads_per_item) * sa.splits;
   if (pl->use_cascade) {
     TileArgs pa = base;
     pa.prefix_mode = 1;

@@ -175,6 +175,12 @@ def test_error_codes():
         _try(kv_strides=(16 * 2 * 64, 2 * 64, 60))
     assert e.value.status == _lib.CA_EUNSUPPORTED
     assert "stride" in _lib.load().cascade_attn_last_error().decode()
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(heads_per_item=3)                     # must divide num_kv_heads (2)
+    assert e.value.status == _lib.CA_EINVAL
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(heads_per_item=-1)
+    assert e.value.status == _lib.CA_EINVAL
 
 
 def test_plan_partition_is_consistent():
@@ -192,3 +198,19 @@ def test_plan_partition_is_consistent():
             assert info["suffix_chunk_tokens"] % 64 == 0
             assert 0 < info["suffix_chunk_tokens"] <= 8192
             assert info["suffix_stages"] in (2, 4)
+            h = info["suffix_heads_per_item"]
+            assert h >= 1 and b.workload.num_kv_heads % h == 0
+            if info["suffix_kernel"] != 1:
+                assert h == 1
+
+
+def test_heads_per_item_choice_and_override():
+    """Auto grouping for the worked example (two heads per decode item keeps
+    the launch within two work-groups per CU); the explicit setting is
+    reported as given and ignored for items of more than 16 rows."""
+    wd = workloads.make_batch(workloads.get("worked_decode"))
+    assert _plan(wd, mode="on").info["suffix_heads_per_item"] == 2
+    assert _plan(wd, mode="off").info["suffix_heads_per_item"] == 1
+    assert _plan(wd, mode="on", heads_per_item=8).info["suffix_heads_per_item"] == 8
+    mp = workloads.make_batch(workloads.get("mixed_prefill"))
+    assert _plan(mp, mode="on", heads_per_item=2).info["suffix_heads_per_item"] == 1

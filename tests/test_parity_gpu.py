@@ -54,6 +54,26 @@ def test_small_full_parity(name, mode):
     assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}")
 
 
+GROUPED = [("tiny_decode", 2), ("tiny_decode", 4), ("decode_ragged", 8), ("gqa8_outliers", 2),
+           ("long_prefix_split", 2), ("d64_gqa", 2), ("one_page_suffix", 4), ("prefill_mix", 2)]
+
+
+@pytest.mark.parametrize("mode", ["on", "off"])
+@pytest.mark.parametrize("name,heads", GROUPED)
+def test_grouped_heads(name, heads, mode):
+    """Decode-shaped items that run several KV heads each (one continuous
+    pipeline over consecutive heads of a request). prefill_mix has items of
+    more than 16 rows, where the setting does not apply."""
+    log(f"[parity] {name} mode={mode} heads/item={heads}")
+    b = workloads.make_batch(SMALL[name])
+    ref_o, ref_l = oracle_ref(b)
+    out, lse, info = run(DeviceBatch(b), mode=mode, heads_per_item=heads)
+    log(f"  plan: cascade={info['use_cascade']} heads/item={info['suffix_heads_per_item']} "
+        f"kernel={info['suffix_kernel']} schunks={info['suffix_chunks']}")
+    assert info["suffix_heads_per_item"] == (heads if info["suffix_kernel"] == 1 else 1)
+    assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}/h{heads}")
+
+
 @pytest.mark.parametrize("name", ["decode_ragged", "prefill_mix", "d64_gqa"])
 def test_small_hnd_layout(name):
     log(f"[parity] {name} HND")
