@@ -58,7 +58,9 @@ struct CostModel {
   double cu_bw = 40.0e9;          // bytes/s one CU's work-groups pull when few CUs are busy
   double item_latency_us = 4.0;   // fixed start / drain latency of one work item
   double mall_bw = 11.0e12;       // bytes/s for re-reads that hit L2 / Infinity Cache
-  double cu_mfma = 4.0e12;        // flop/s of one CU in the tiled MFMA kernel
+  double cu_mfma = 4.0e12;        // flop/s of one CU, 128-row tiles (2 row blocks per wave)
+  double cu_mfma_rows = 1.8e12;   // flop/s of one CU, 64-row tiles and prefill suffixes (causal, ragged)
+  double reread_bw = 14.0e12;     // bytes/s of the non-cascade path's shared-prefix re-reads (L2 / MALL)
   double launch_us = 2.5;         // per kernel launch on one stream
   double mall_bytes = 256.0e6;    // Infinity Cache capacity
 };
@@ -109,7 +111,7 @@ static PhaseTile choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& 
     const double active = (double)std::min<int64_t>(items, cus);
     const double item_flops = 4.0 * bm * pl.d * (double)tiles_per * kTileKeys;
     const double waves_of_items = std::ceil((double)items / cus);
-    const double t_mfma = waves_of_items * item_flops / cm.cu_mfma;
+    const double t_mfma = waves_of_items * item_flops / (t.row_blocks > 1 ? cm.cu_mfma : cm.cu_mfma_rows);
     const double hbm = bpt * pl.prefix_len + part_per_split * splits + (double)pl.total_q * pl.hq * pl.d * 2.0;
     const double t_hbm = hbm / std::min(cm.hbm_bw, active * cm.cu_bw);
     const double est = (std::max(t_mfma, t_hbm) + part_per_split * splits / cm.mall_bw) * 1e6 + cm.item_latency_us;
@@ -174,8 +176,8 @@ static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_
                             int32_t cus, const CostModel& cm, double extra_mall_bytes) {
   const double bpt = 4.0 * pl.hkv * pl.d;
   const double io = (double)pl.total_q * pl.hq * pl.d * 2.0 * 2.0;
-  const double t_bytes = (bpt * kv_tokens + io) / cm.hbm_bw + extra_mall_bytes / cm.mall_bw;
-  const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma);
+  const double t_bytes = (bpt * kv_tokens + io) / cm.hbm_bw + extra_mall_bytes / cm.reread_bw;
+  const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma_rows);
   double us = std::max(t_bytes, t_mfma) * 1e6 + cm.launch_us;
   if (merge) {
     const double part = (double)chunks * pl.total_q * pl.hq * (pl.d + 1) * 4.0;

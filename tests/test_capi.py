@@ -214,3 +214,17 @@ def test_heads_per_item_choice_and_override():
     assert _plan(wd, mode="on", heads_per_item=8).info["suffix_heads_per_item"] == 8
     mp = workloads.make_batch(workloads.get("mixed_prefill"))
     assert _plan(mp, mode="on", heads_per_item=2).info["suffix_heads_per_item"] == 1
+
+
+def test_auto_takes_the_measured_faster_path():
+    """AUTO's cost model (constants fitted to this library's kernels on
+    MI355X) picks, for each workload, the path that measured faster when both
+    were timed on the device: cascade for the worked example, the mixed and
+    capped prefill batches, self-consistency and both long-document batches;
+    non-cascade where the gates fail (255-token prefix) or the two paths tie
+    (the tiny batch)."""
+    expect = {"worked_decode": 1, "mixed_prefill": 1, "mixed_prefill_capped": 1, "self_consistency": 1,
+              "long_doc": 1, "long_doc_n8": 1, "long_doc_p255": 0}
+    for name, casc in expect.items():
+        b = workloads.make_batch(workloads.get(name))
+        assert _plan(b, mode="auto").info["use_cascade"] == casc, name
