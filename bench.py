@@ -156,6 +156,7 @@ def main():
     ap.add_argument("--mode", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-noncascade", action="store_true")
+    ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -180,10 +181,10 @@ def main():
     b = workloads.make_batch(w)
     bpt = 2 * w.num_kv_heads * w.head_dim * 2
 
-    def make_plan(mode):
+    def make_plan(mode, **kw):
         return spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                               k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
-                              seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode)
+                              seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode, **kw)
 
     plan = make_plan(args.mode)
     info = plan.info
@@ -269,6 +270,37 @@ def main():
         ms_off = time_steps(step_off, max(10, args.steps // 4), rotate)
         extra = {"noncascade_us_per_step": round(ms_off * 1e3, 3),
                  "speedup_vs_noncascade": round(ms_off / ms, 3)}
+
+    # each cascade phase on its own: the same work items as two launches, so
+    # the prefix phase's MFMA rate and the suffix phase's HBM rate can be
+    # read separately (the timed step above runs them as one launch)
+    if not args.no_phases and casc:
+        plan_sep = make_plan(args.mode, separate_phases=True)
+        step_sep = step_with(plan_sep, workspace_for(plan_sep))
+        for i in range(args.warmup):
+            step_sep(i % rotate)
+        spa.cascade_attn_profile_enable(True)
+        ms_sep = time_steps(step_sep, max(10, args.steps // 2), rotate)
+        spa.cascade_attn_profile_enable(False)
+        prof_sep = spa.cascade_attn_profile_read()
+        suffix_visible = visible - plen * T
+        ph_work = {"prefix": (plen * bpt + q_bytes, 4.0 * T * w.num_q_heads * plen * w.head_dim),
+                   "suffix": ((kv_tokens - plen) * bpt + q_bytes, 4.0 * w.num_q_heads * w.head_dim * suffix_visible)}
+        phases = {"us_per_step": round(ms_sep * 1e3, 3)}
+        for kind in ("prefix", "suffix", "merge"):
+            tot_ms, cnt = prof_sep[kind]
+            if not cnt:
+                continue
+            sec = tot_ms * 1e-3 / cnt
+            rec = {"avg_us": round(sec * 1e6, 3)}
+            if kind in ph_work:
+                nbytes, nflops = ph_work[kind]
+                rec.update({"bytes": int(nbytes), "gbs": round(nbytes / sec / 1e9, 1),
+                            "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                            "tflops": round(nflops / sec / 1e12, 2),
+                            "mfma_frac": round(nflops / sec / 1e12 / BF16_PEAK_TFLOPS, 4)})
+            phases[kind] = rec
+        extra["separate_phases"] = phases
 
     cpu = None
     if not args.no_cpu_baseline:

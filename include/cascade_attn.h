@@ -73,7 +73,9 @@ typedef struct {
   int32_t page_size;           /* tokens per KV page: 16 */
   int32_t block_table_stride;  /* int32 entries per block-table row */
   int32_t num_pages;           /* pages in the KV pool (bounds check of page ids) */
-  int32_t reserved0;
+  int32_t separate_phases;     /* cascade path only: 0 = prefix and suffix work-groups share one
+                                  launch; 1 = two launches (prefix, then suffix) doing the same
+                                  work with identical results, e.g. to time each phase */
   /* K/V cache element strides (bf16 elements). The cache is indexed
    * [page][slot][kv_head][d] with d contiguous; NHD layout
    * [num_pages, page_size, Hkv, d] has (page_size*Hkv*d, Hkv*d, d), HND
@@ -106,6 +108,8 @@ typedef struct {
   int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
   int32_t merge_in_suffix;             /* 1: the suffix kernel merges and writes the output */
   int32_t suffix_heads_per_item;       /* consecutive KV heads one suffix (or only) work item runs */
+  int32_t separate_phases;             /* 1 if the cascade phases run as two launches */
+  int32_t reserved0;
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
   int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */
@@ -195,13 +199,15 @@ const char* cascade_attn_last_error(void);
  * Kernel timing for measurement. While enabled, run() records a HIP event
  * pair around every kernel it launches, on the launch stream.
  * cascade_attn_profile_read() waits for the recorded events, writes the
- * summed milliseconds and launch counts per kernel kind into ms[4] and
- * counts[4], and clears the record. Kinds: 0 = cascade phases (prefix and
- * suffix work-groups of the cascade path in one launch), 1 = tiled
- * attention of the non-cascade path, 2 = merge, 3 = decode attention of the
- * non-cascade path.
+ * summed milliseconds and launch counts per kernel kind into
+ * ms[CA_PROFILE_KINDS] and counts[CA_PROFILE_KINDS], and clears the record.
+ * Kinds: 0 = cascade phases (prefix and suffix work-groups of the cascade
+ * path in one launch), 1 = tiled attention of the non-cascade path,
+ * 2 = merge, 3 = decode attention of the non-cascade path, 4 = prefix phase
+ * and 5 = suffix phase when a plan runs them as separate launches.
  * Errors: CA_EHIP if an event call fails, CA_EINVAL for null outputs.
  */
+#define CA_PROFILE_KINDS 6
 ca_status_t cascade_attn_profile_enable(int32_t enable);
 ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts);
 

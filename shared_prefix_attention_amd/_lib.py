@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "cascade_attn.h")
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_EMETA, CA_EWORKSPACE, CA_EHIP = range(6)
 MODE_AUTO, MODE_FORCE_ON, MODE_FORCE_OFF = 0, 1, 2
 _MODES = {"auto": MODE_AUTO, "on": MODE_FORCE_ON, "off": MODE_FORCE_OFF}
-KERNEL_KINDS = ("cascade_phases", "attention", "merge", "decode")
+KERNEL_KINDS = ("cascade_phases", "attention", "merge", "decode", "prefix", "suffix")
 
 
 class CascadeAttnError(RuntimeError):
@@ -37,7 +37,7 @@ class ca_params_t(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("block_table_stride", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("separate_phases", ctypes.c_int32),
         ("kv_stride_page", ctypes.c_int64),
         ("kv_stride_token", ctypes.c_int64),
         ("kv_stride_head", ctypes.c_int64),
@@ -64,6 +64,8 @@ class ca_plan_info_t(ctypes.Structure):
         ("suffix_stages", ctypes.c_int32),
         ("merge_in_suffix", ctypes.c_int32),
         ("suffix_heads_per_item", ctypes.c_int32),
+        ("separate_phases", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("kv_tokens_cascade", ctypes.c_int64),
@@ -175,7 +177,7 @@ class Plan:
 def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                       num_pages: int, kv_strides, block_table, query_start_loc, seq_lens,
                       num_computed_tokens=None, softmax_scale: float = 0.0, mode="auto",
-                      num_cus: int = 0, heads_per_item: int = 0) -> Plan:
+                      num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False) -> Plan:
     """Host-only planner (see cascade_attn_plan in the header).
 
     kv_strides: (page, token-slot, head) element strides of the K/V caches.
@@ -203,6 +205,7 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
     prm.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
     prm.num_cus = int(num_cus)
     prm.heads_per_item = int(heads_per_item)
+    prm.separate_phases = int(separate_phases)
     h = ctypes.c_void_p(0)
     _check(load().cascade_attn_plan(ctypes.byref(prm), bt_p, qsl_p, sl_p, nc_p, ctypes.byref(h)))
     return Plan(h.value)
@@ -239,7 +242,8 @@ def cascade_attn_profile_enable(enable: bool = True) -> None:
 
 
 def cascade_attn_profile_read():
-    ms = (ctypes.c_double * 4)()
-    cnt = (ctypes.c_int64 * 4)()
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
     _check(load().cascade_attn_profile_read(ms, cnt))
     return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}

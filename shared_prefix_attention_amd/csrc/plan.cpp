@@ -244,6 +244,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.mode < CA_MODE_AUTO || p.mode > CA_MODE_FORCE_OFF) return fail(CA_EINVAL, "unknown mode");
   if (p.heads_per_item < 0 || (p.heads_per_item > 0 && p.num_kv_heads % p.heads_per_item != 0))
     return fail(CA_EINVAL, "heads_per_item must be 0 or divide num_kv_heads");
+  if (p.separate_phases != 0 && p.separate_phases != 1) return fail(CA_EINVAL, "separate_phases must be 0 or 1");
 
   const int32_t n = p.num_reqs, ps = p.page_size, stride = p.block_table_stride;
   if (qsl[0] != 0) return fail(CA_EMETA, "query_start_loc[0] must be 0");
@@ -353,6 +354,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->suffix.stages = 2;
     pl->suffix.heads_per_item = pick_heads_per_item(*pl, pre, suf, cus);
     pl->merge_in_suffix = 0;
+    pl->separate_phases = p.separate_phases;
     pl->num_slots = pre.splits + suf.splits;
     pl->direct_out = false;
   } else {
@@ -362,6 +364,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->suffix = nc;
     pl->suffix.heads_per_item = (nc.kernel == 1 && p.heads_per_item > 0) ? p.heads_per_item : 1;
     pl->merge_in_suffix = 0;
+    pl->separate_phases = 0;
     pl->num_slots = nc.splits > 1 ? nc.splits : 0;
     pl->direct_out = nc.splits == 1;
   }
@@ -396,6 +399,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->suffix_stages = pl->suffix.stages;
   out->merge_in_suffix = pl->merge_in_suffix;
   out->suffix_heads_per_item = pl->suffix.heads_per_item;
+  out->separate_phases = pl->separate_phases;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

@@ -52,6 +52,7 @@ struct ca_plan {
   int32_t num_slots = 0;      // fp32 partial states per (token, head)
   bool direct_out = false;    // the last attention launch writes the bf16 output directly
   int32_t merge_in_suffix = 0;// cascade: the suffix kernel folds in the prefix partials
+  int32_t separate_phases = 0;// cascade: prefix and suffix as two launches
   int64_t slot_elems = 0;     // T * Hq * d
   int64_t ws_lse_offset = 0;  // byte offset of the partial LSE array
   int64_t workspace_bytes = 0;

@@ -22,7 +22,8 @@ using namespace ca;
 
 namespace {
 
-enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_KINDS = 4 };
+enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_PREFIX = 4, K_SUFFIX = 5, K_KINDS = 6 };
+static_assert(K_KINDS == CA_PROFILE_KINDS, "profile kinds");
 
 struct Profiler {
   std::mutex mu;
@@ -96,6 +97,7 @@ ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hi
   if (!item_ok(ph)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   switch (shape_id(ph)) {
     case 0: launch_tile_ns<D, 1, 4, 1>(args, ph.stages, (int)grid, s, kind); break;
+    case 1: launch_tile_ns<D, 2, 4, 1>(args, ph.stages, (int)grid, s, kind); break;
     case 2: launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s, kind); break;
     default: return fail(CA_EINVAL, "unsupported work-group shape in plan");
   }
@@ -194,7 +196,13 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     pa.split_tokens = pl->prefix.split_tokens;
     pa.slot_base = 0;
     pa.direct = 0;
-    st = run_phases<D>(pa, pl->prefix, (int64_t)pa.mtiles * pl->hkv * pa.splits, sa, pl->suffix, n_suffix, s);
+    const int64_t n_prefix = (int64_t)pa.mtiles * pl->hkv * pa.splits;
+    if (pl->separate_phases) {
+      st = run_tile<D>(pa, pl->prefix, n_prefix, s, K_PREFIX);
+      if (st == CA_OK) st = run_tile<D>(sa, pl->suffix, n_suffix, s, K_SUFFIX);
+    } else {
+      st = run_phases<D>(pa, pl->prefix, n_prefix, sa, pl->suffix, n_suffix, s);
+    }
   } else {
     st = run_tile<D>(sa, pl->suffix, n_suffix, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
   }

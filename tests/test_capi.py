@@ -181,6 +181,9 @@ def test_error_codes():
     with pytest.raises(spa.CascadeAttnError) as e:
         _try(heads_per_item=-1)
     assert e.value.status == _lib.CA_EINVAL
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(separate_phases=2)
+    assert e.value.status == _lib.CA_EINVAL
 
 
 def test_plan_partition_is_consistent():
@@ -214,6 +217,17 @@ def test_heads_per_item_choice_and_override():
     assert _plan(wd, mode="on", heads_per_item=8).info["suffix_heads_per_item"] == 8
     mp = workloads.make_batch(workloads.get("mixed_prefill"))
     assert _plan(mp, mode="on", heads_per_item=2).info["suffix_heads_per_item"] == 1
+
+
+def test_separate_phases_changes_only_the_launch_count():
+    """Asking for the cascade phases as two launches leaves every other
+    decision of the plan as it was; a non-cascade plan ignores it."""
+    wd = workloads.make_batch(workloads.get("worked_decode"))
+    fused, split = _plan(wd, mode="on").info, _plan(wd, mode="on", separate_phases=1).info
+    assert fused["separate_phases"] == 0 and split["separate_phases"] == 1
+    assert {k: v for k, v in fused.items() if k != "separate_phases"} == \
+        {k: v for k, v in split.items() if k != "separate_phases"}
+    assert _plan(wd, mode="off", separate_phases=1).info["separate_phases"] == 0
 
 
 def test_auto_takes_the_measured_faster_path():

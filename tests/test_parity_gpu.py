@@ -113,3 +113,25 @@ def test_full_size_sampled_parity(name):
     o_off, l_off = outs["off"]
     assert np.all(np.abs(o_on - o_off) <= 2e-2 + 1e-2 * np.abs(o_off))
     assert np.abs(l_on - l_off).max() <= 1e-3
+
+
+SEPARATE = ["tiny_decode", "prefill_mix", "prefill_capped", "gqa8_outliers", "many_rows", "d64_gqa",
+            "worked_decode", "mixed_prefill", "self_consistency"]
+
+
+@pytest.mark.parametrize("name", SEPARATE)
+def test_separate_phase_launches_match_fused(name):
+    """The prefix and suffix phases as two launches run the same work items
+    as the single launch, so the results are bitwise the same."""
+    log(f"[separate] {name}")
+    w = SMALL[name] if name in SMALL else workloads.get(name)
+    db = DeviceBatch(workloads.make_batch(w))
+    fo, fl, finfo = run(db, mode="on")
+    so, sl, sinfo = run(db, mode="on", separate_phases=True)
+    assert finfo["use_cascade"] == 1 and finfo["separate_phases"] == 0 and sinfo["separate_phases"] == 1
+    log(f"  prefix row tile {sinfo['prefix_row_tile']}, suffix kernel {sinfo['suffix_kernel']}, "
+        f"heads/item {sinfo['suffix_heads_per_item']}")
+    assert np.array_equal(fo, so) and np.array_equal(fl, sl), f"{name}: separate launches differ from the fused one"
+    if name in SMALL:
+        ref_o, ref_l = oracle_ref(db.b)
+        assert_close(so, sl, ref_o, ref_l, what=f"{name}/separate")
