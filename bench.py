@@ -157,6 +157,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-noncascade", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
+    ap.add_argument("--max-levels", type=int, default=0, help="shared levels of the cascade plan (0 = default)")
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -184,7 +185,8 @@ def main():
     def make_plan(mode, **kw):
         return spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                               k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
-                              seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode, **kw)
+                              seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode,
+                              max_levels=args.max_levels, **kw)
 
     plan = make_plan(args.mode)
     info = plan.info
@@ -332,8 +334,9 @@ def main():
         "kernels": kern,
         "profiled_us_per_step": round(ms_prof * 1e3, 3),
         "warm_us_per_step": round(ms_warm * 1e3, 3),
-        "plan": {k: info[k] for k in ("prefix_splits", "prefix_row_tile", "suffix_chunks", "suffix_chunk_tokens",
-                                       "suffix_kernel", "num_partial_slots", "workspace_bytes")},
+        "plan": {k: info[k] for k in ("prefix_splits", "prefix_row_tile", "num_level1_groups", "level1_splits",
+                                       "suffix_chunks", "suffix_chunk_tokens", "suffix_kernel", "num_partial_slots",
+                                       "workspace_bytes")},
         **extra,
         "cpu_baseline": cpu,
     }

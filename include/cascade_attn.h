@@ -91,6 +91,9 @@ typedef struct {
   int32_t heads_per_item;      /* KV heads one decode-shaped suffix item runs back to back
                                   (0 = planner's choice; else must divide num_kv_heads;
                                   ignored for items of more than 16 rows) */
+  int32_t max_levels;          /* shared levels of the cascade path: 0 = planner default (2);
+                                  1 = the batch-wide prefix only; 2 = also groups of consecutive
+                                  requests sharing more pages (see cascade_attn_plan_groups) */
 } ca_params_t;
 
 typedef struct {
@@ -108,7 +111,9 @@ typedef struct {
   int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
   int32_t merge_in_suffix;             /* 1: the suffix kernel merges and writes the output */
   int32_t suffix_heads_per_item;       /* consecutive KV heads one suffix (or only) work item runs */
-  int32_t separate_phases;             /* 1 if the cascade phases run as two launches */
+  int32_t separate_phases;             /* 1 if the cascade phases run as separate launches */
+  int32_t num_level1_groups;           /* request groups of the second shared level (0 = none) */
+  int32_t level1_splits;               /* KV splits of every group (partial slots of that level) */
   int32_t reserved0;
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
@@ -164,6 +169,26 @@ ca_status_t cascade_attn_plan(const ca_params_t* params, const int32_t* block_ta
 ca_status_t cascade_attn_plan_info(ca_plan_t plan, ca_plan_info_t* out);
 
 /*
+ * Second shared level of the plan. FlashInfer's cascade takes any number of
+ * levels ([p2] section 7) and the workloads of [p2] section 3 nest (system
+ * prompt -> document -> request). When the cascade path is taken and
+ * params->max_levels != 1, the planner looks for groups: maximal runs of
+ * consecutive requests in which every adjacent pair shares more leading
+ * pages than the batch-wide prefix. A group's shared length is the pages
+ * all its members share, capped at their smallest num_computed_tokens and
+ * floored to a page (the batch-wide rule of section 8 Step 2); it is used if
+ * the group has >= 2 requests and shares >= 256 tokens more than the
+ * batch-wide prefix. At most 64 groups (those that save the most KV reads).
+ * The group's queries, packed, attend non-causally once to its extra
+ * positions [common_prefix_len, shared_len); its members' suffixes start at
+ * shared_len. Writes min(n, capacity) triples (first request, end request
+ * (exclusive), shared_len) to groups_out [capacity][3] and n to *n_out.
+ * Errors: CA_EINVAL (null plan / n_out, capacity < 0, null groups_out with
+ * capacity > 0).
+ */
+ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* groups_out, int32_t* n_out);
+
+/*
  * Runs one attention step of the plan on `stream` (a hipStream_t; NULL =
  * the null stream). Asynchronous: no host synchronisation, no allocation,
  * no host-to-device copy; inputs must stay alive until the stream passes
@@ -179,7 +204,7 @@ ca_status_t cascade_attn_plan_info(ca_plan_t plan, ca_plan_info_t* out);
  *                    need no initialisation and are meaningless afterwards;
  *                    two runs that overlap in time must not share it.
  * Cascade path: prefix kernel + suffix kernel + merge kernel ([p2] section 8
- * Step 5). Non-cascade path: one attention over each request's full block
+ * Step 5), with the group level beside the prefix when the plan has one. Non-cascade path: one attention over each request's full block
  * table (Step 4), plus a merge when the plan splits the KV range.
  * Errors: CA_EINVAL (null pointers/handle), CA_EWORKSPACE (too small),
  * CA_EHIP (launch failure).
@@ -203,11 +228,12 @@ const char* cascade_attn_last_error(void);
  * ms[CA_PROFILE_KINDS] and counts[CA_PROFILE_KINDS], and clears the record.
  * Kinds: 0 = cascade phases (prefix and suffix work-groups of the cascade
  * path in one launch), 1 = tiled attention of the non-cascade path,
- * 2 = merge, 3 = decode attention of the non-cascade path, 4 = prefix phase
- * and 5 = suffix phase when a plan runs them as separate launches.
+ * 2 = merge, 3 = decode attention of the non-cascade path, 4 = prefix phase,
+ * 5 = suffix phase and 6 = group level when a plan runs the phases as
+ * separate launches.
  * Errors: CA_EHIP if an event call fails, CA_EINVAL for null outputs.
  */
-#define CA_PROFILE_KINDS 6
+#define CA_PROFILE_KINDS 7
 ca_status_t cascade_attn_profile_enable(int32_t enable);
 ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts);
 

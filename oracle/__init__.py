@@ -30,6 +30,8 @@ from .cascade_ref import (  # noqa: F401
     passes_cascade_gates,
     kv_tokens_standard,
     kv_tokens_cascade,
+    level1_groups,
+    kv_tokens_multilevel,
     MIN_PREFIX_TOKENS,
     MIN_NUM_REQS,
 )

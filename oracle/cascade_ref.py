@@ -211,3 +211,53 @@ def kv_tokens_cascade(prefix_len, seq_lens):
     """KV positions read by cascade: the prefix once plus each request's
     suffix ([p2] section 5: P + N x S)."""
     return int(prefix_len) + int(sum(int(s) - int(prefix_len) for s in seq_lens))
+
+
+def level1_groups(block_table, seq_lens, num_computed_tokens, page_size, level0_len,
+                  min_members=2, min_extra_tokens=MIN_PREFIX_TOKENS):
+    """Request groups of a second shared level, as (first, end, shared_len).
+
+    FlashInfer's cascade runs any number of levels ([p2] section 7 table) and
+    the workloads of [p2] section 3 nest (a system prompt shared by all, a
+    document shared by some). The pages give no detector for the inner
+    level, so this is the plainest extension of the batch-wide rule
+    ([p2] section 8 Steps 1-2) to runs of consecutive requests: starting
+    from request a, extend the run while all its requests still share more
+    leading pages than the batch-wide prefix (common_prefix_blocks of the
+    run), then give the run the pages all of it shares, capped at its
+    smallest num_computed_tokens and floored to a page. A run is a group if
+    it has at least ``min_members`` requests and shares at least
+    ``min_extra_tokens`` more positions than the batch-wide prefix (the
+    prefix-length gate of section 3 by default).
+    """
+    bt = [list(map(int, row)) for row in block_table]
+    sl = [int(s) for s in seq_lens]
+    nc = [int(x) for x in num_computed_tokens]
+    n = len(bt)
+    level0_pages = int(level0_len) // int(page_size)
+    groups = []
+    a = 0
+    while a < n:
+        b = a + 1
+        while b < n and common_prefix_blocks(bt[a:b + 1], sl[a:b + 1], page_size) > level0_pages:
+            b += 1
+        if b - a >= min_members:
+            blocks = common_prefix_blocks(bt[a:b], sl[a:b], page_size)
+            length = cascade_prefix_len(blocks, page_size, nc[a:b])
+            if length - int(level0_len) >= min_extra_tokens:
+                groups.append((a, b, length))
+        a = b
+    return groups
+
+
+def kv_tokens_multilevel(level0_len, groups, seq_lens):
+    """KV positions read with a second shared level: the batch-wide prefix
+    once, each group's extra positions once, and each request's remaining
+    positions ([p2] section 5's accounting, one level deeper)."""
+    start = [int(level0_len)] * len(seq_lens)
+    extra = 0
+    for a, b, length in groups:
+        extra += int(length) - int(level0_len)
+        for r in range(a, b):
+            start[r] = int(length)
+    return int(level0_len) + extra + int(sum(int(s) - st for s, st in zip(seq_lens, start)))

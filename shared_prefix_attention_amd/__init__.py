@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     Plan,
     cascade_attn_num_common_prefix_blocks,
     cascade_attn_plan,
+    cascade_attn_plan_groups,
     cascade_attn_plan_info,
     cascade_attn_profile_enable,
     cascade_attn_profile_read,

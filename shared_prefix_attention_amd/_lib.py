@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "cascade_attn.h")
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_EMETA, CA_EWORKSPACE, CA_EHIP = range(6)
 MODE_AUTO, MODE_FORCE_ON, MODE_FORCE_OFF = 0, 1, 2
 _MODES = {"auto": MODE_AUTO, "on": MODE_FORCE_ON, "off": MODE_FORCE_OFF}
-KERNEL_KINDS = ("cascade_phases", "attention", "merge", "decode", "prefix", "suffix")
+KERNEL_KINDS = ("cascade_phases", "attention", "merge", "decode", "prefix", "suffix", "level1")
 
 
 class CascadeAttnError(RuntimeError):
@@ -45,6 +45,7 @@ class ca_params_t(ctypes.Structure):
         ("mode", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("heads_per_item", ctypes.c_int32),
+        ("max_levels", ctypes.c_int32),
     ]
 
 
@@ -65,6 +66,8 @@ class ca_plan_info_t(ctypes.Structure):
         ("merge_in_suffix", ctypes.c_int32),
         ("suffix_heads_per_item", ctypes.c_int32),
         ("separate_phases", ctypes.c_int32),
+        ("num_level1_groups", ctypes.c_int32),
+        ("level1_splits", ctypes.c_int32),
         ("reserved0", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
@@ -100,12 +103,13 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(ca_plan_info_t)]
     lib.cascade_attn_run.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
         [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
     lib.cascade_attn_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.cascade_attn_plan_destroy.restype = None
     lib.cascade_attn_profile_enable.argtypes = [ctypes.c_int32]
     lib.cascade_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("cascade_attn_num_common_prefix_blocks", "cascade_attn_plan", "cascade_attn_plan_info",
-                 "cascade_attn_run", "cascade_attn_profile_enable", "cascade_attn_profile_read"):
+                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_profile_enable", "cascade_attn_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -177,7 +181,8 @@ class Plan:
 def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                       num_pages: int, kv_strides, block_table, query_start_loc, seq_lens,
                       num_computed_tokens=None, softmax_scale: float = 0.0, mode="auto",
-                      num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False) -> Plan:
+                      num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
+                      max_levels: int = 0) -> Plan:
     """Host-only planner (see cascade_attn_plan in the header).
 
     kv_strides: (page, token-slot, head) element strides of the K/V caches.
@@ -206,6 +211,7 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
     prm.num_cus = int(num_cus)
     prm.heads_per_item = int(heads_per_item)
     prm.separate_phases = int(separate_phases)
+    prm.max_levels = int(max_levels)
     h = ctypes.c_void_p(0)
     _check(load().cascade_attn_plan(ctypes.byref(prm), bt_p, qsl_p, sl_p, nc_p, ctypes.byref(h)))
     return Plan(h.value)
@@ -213,6 +219,16 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
 
 def cascade_attn_plan_info(plan: Plan) -> dict:
     return dict(plan.info)
+
+
+def cascade_attn_plan_groups(plan: Plan):
+    """Second shared level of the plan: [(first request, end request, shared_len)]."""
+    n = ctypes.c_int32(0)
+    _check(load().cascade_attn_plan_groups(plan.handle, 0, None, ctypes.byref(n)))
+    cap = int(n.value)
+    buf = (ctypes.c_int32 * max(1, 3 * cap))()
+    _check(load().cascade_attn_plan_groups(plan.handle, cap, buf, ctypes.byref(n)))
+    return [(buf[3 * j], buf[3 * j + 1], buf[3 * j + 2]) for j in range(cap)]
 
 
 def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d,

@@ -5,9 +5,12 @@
 //     non-causally to the shared-prefix pages (block-table row 0);
 //   * the suffix phase: each request's rows attend causally to its own KV
 //     range [key_start, seq_len) through its block-table row;
+//   * a second shared level: the rows of each group of consecutive requests
+//     that share more pages than the whole batch attend non-causally to
+//     those extra pages (block-table row of the group's first request);
 //   * the non-cascade path: the suffix phase with key_start = 0, writing the
 //     final bf16 output directly when its KV range is one work item.
-// Both cascade phases run in one launch (cascade_phases_kernel); their
+// The cascade phases run in one launch (cascade_phases_kernel); their
 // partial states are combined by the merge kernel.
 // ("vLLM Cascade Attention：用法、场景与原理解析", beaiera.top, section 8
 // Step 5: prefix phase, suffix phase, LSE merge; section 4 for which keys
@@ -53,7 +56,7 @@ struct TileArgs {
   int32_t bt_stride;
   int32_t hq, hkv, group;
   float scale_log2;             // softmax_scale * log2(e)
-  int32_t prefix_mode;          // 1: prefix phase, 0: per-request phase
+  int32_t prefix_mode;          // 1: prefix phase, 2: group level, 0: per-request phase
   int32_t total_rows;           // prefix: T * group
   int32_t key_start;            // per-request phase: first KV position
   int32_t prefix_len;           // prefix phase: number of shared KV positions
@@ -70,7 +73,36 @@ struct TileArgs {
   uint16_t* out;                // [T][hq][D] bf16 (direct / merge mode)
   float* lse_out;               // [T][hq] (may be null)
   int32_t direct;               // write the final output (no partial)
+  int32_t lvl1_slot_base;       // per-request phase: first partial slot of the group level
+  int32_t lvl1_slots;           //   and its slot count (rows of requests in no group get -inf there)
 };
+
+// Second shared level: request groups [req_begin, req_end) whose members
+// share KV positions [key_start, key_end) beyond the batch-wide prefix. Group
+// j's work items are [item_begin[j], item_begin[j + 1]) of the group-level
+// launch, (row tile, KV head, split) with `splits` splits of split_tokens
+// keys. Passed by value (kernel arguments), so the plan needs no device copy.
+constexpr int kMaxGroups = 64;
+struct GroupTable {
+  int32_t n;                            // groups (0: one shared level)
+  int32_t item_begin[kMaxGroups + 1];
+  int32_t req_begin[kMaxGroups];        // ascending, ranges disjoint
+  int32_t req_end[kMaxGroups];
+  int32_t key_end[kMaxGroups];          // shared positions end (page multiple)
+  int32_t split_tokens[kMaxGroups];     // multiple of 64
+};
+
+// Group holding request `req` (or -1): the last group starting at or before
+// it, if it also ends after it. Uniform arguments: scalar binary search.
+__device__ __forceinline__ int group_of_request(const GroupTable& gt, int req) {
+  int lo = 0, hi = gt.n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (gt.req_begin[mid] <= req) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo > 0 && req < gt.req_end[lo - 1]) ? lo - 1 : -1;
+}
 
 constexpr int kMaxItemPages = 512;
 
@@ -185,7 +217,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
 // MH: the item may cover several consecutive KV heads of one request (same
 // pages and key range), run as one continuous stage pipeline.
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH>
-__device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint8_t* smem) {
+__device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const int bid, uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
   constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
@@ -223,17 +255,32 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   int tok_base = 0, q_pos_base = 0;      // token of row 0, causal position of row 0's token
   bool causal;
   const int32_t* bt_row;
-  int req = 0, c = 0, mt = 0;
+  int req = 0, c = 0, mt = 0, grp = -1;
+  int split_tokens = a.split_tokens;
   const int H = MH ? a.heads_per_item : 1;   // KV heads g0 .. g0 + H - 1, one after another
   if (a.prefix_mode) {
+    int local = bid;
+    if (a.prefix_mode == 2) {
+      // group level: find the group whose items contain bid
+      int lo = 0, hi = gt.n - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (gt.item_begin[mid] <= bid) lo = mid;
+        else hi = mid - 1;
+      }
+      grp = lo;
+      local = bid - gt.item_begin[grp];
+      split_tokens = gt.split_tokens[grp];
+      req = gt.req_begin[grp];
+    }
     const int kv_items = a.hkv * a.splits;
-    mt = bid / kv_items;
-    const int kvi = bid - mt * kv_items;
+    mt = local / kv_items;
+    const int kvi = local - mt * kv_items;
     g0 = kvi / a.splits;
     c = kvi - g0 * a.splits;
-    key_begin = c * a.split_tokens;
+    key_begin = a.key_start + c * split_tokens;
     causal = false;
-    bt_row = a.bt;
+    bt_row = a.bt + (int64_t)req * a.bt_stride;
   } else {
     c = bid % a.splits;
     int rest = bid / a.splits;
@@ -242,14 +289,16 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
     const int groups = a.hkv / H;
     g0 = (rest % groups) * H;
     req = rest / groups;
-    key_begin = a.key_start + c * a.split_tokens;
+    // a request in a group starts after the group's shared positions
+    grp = gt.n > 0 ? group_of_request(gt, req) : -1;
+    key_begin = (grp >= 0 ? gt.key_end[grp] : a.key_start) + c * split_tokens;
     causal = true;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
   }
   const int first_page = key_begin >> 4;
   constexpr int PG_PER_THREAD = (kMaxItemPages + NT - 1) / NT;
   int pg_reg[PG_PER_THREAD];
-  const int item_pages = a.split_tokens >> 4;
+  const int item_pages = split_tokens >> 4;
 #pragma unroll
   for (int k = 0; k < PG_PER_THREAD; ++k) {
     const int i = tid + k * NT;
@@ -257,18 +306,37 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
   }
   row_begin = mt * ROWS;
   slot = a.slot_base + c;
-  if (a.prefix_mode) {
+  if (a.prefix_mode == 1) {
     row_end = min(row_begin + ROWS, a.total_rows);
-    key_end = min(key_begin + a.split_tokens, a.prefix_len);
+    key_end = min(key_begin + split_tokens, a.prefix_len);
+  } else if (a.prefix_mode == 2) {
+    const int q0 = a.qsl[req];
+    row_end = min(row_begin + ROWS, (a.qsl[gt.req_end[grp]] - q0) * a.group);
+    if (row_begin >= row_end) return;   // uniform across the work-group
+    key_end = max(key_begin, min(key_begin + split_tokens, gt.key_end[grp]));
+    tok_base = q0;
   } else {
     const int q0 = a.qsl[req];
     const int q_len = a.qsl[req + 1] - q0;
     const int seq_len = a.seq_lens[req];
     row_end = min(row_begin + ROWS, q_len * a.group);
     if (row_begin >= row_end) return;   // uniform across the work-group
-    key_end = max(key_begin, min(key_begin + a.split_tokens, seq_len));
+    key_end = max(key_begin, min(key_begin + split_tokens, seq_len));
     tok_base = q0;
     q_pos_base = seq_len - q_len;        // num_computed_tokens
+    // rows of a request in no group have no group-level state: mark those
+    // partial slots empty (weight 0 in the merge)
+    if (grp < 0 && c == 0 && a.lvl1_slots > 0) {
+      const int nrows = row_end - row_begin;
+      for (int e = tid; e < nrows * H * a.lvl1_slots; e += NT) {
+        const int s = e / (nrows * H);
+        const int rh = e - s * (nrows * H);
+        const int hh = rh / nrows;
+        const int m = row_begin + (rh - hh * nrows);
+        const int64_t row = (int64_t)(tok_base + m / a.group) * a.hq + (g0 + hh) * a.group + m % a.group;
+        a.part_lse[(int64_t)(a.lvl1_slot_base + s) * a.slot_rows + row] = -INFINITY;
+      }
+    }
   }
   const int n_tiles = (key_end - key_begin + SK - 1) / SK;
   // keys at or below this position are visible to every row of the item
@@ -679,24 +747,28 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const int bid, uint
 }
 
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH>
-__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a) {
+__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK>::BYTES];
-  attn_item<D, RB, RW, KG, NS, SK, MH>(a, blockIdx.x, smem);
+  attn_item<D, RB, RW, KG, NS, SK, MH>(a, gt, blockIdx.x, smem);
 }
 
-// One launch for both cascade phases: work-groups [0, n_prefix) run prefix
-// items, the rest run suffix items, so the MFMA-heavy prefix and the
-// bandwidth-heavy suffix share the CUs. Both write partial states. Each role
+// One launch for all cascade phases: work-groups [0, n_prefix) run prefix
+// items, the next n_group run group-level items (same shape as the prefix),
+// the rest run suffix items, so the MFMA-heavy shared levels and the
+// bandwidth-heavy suffix share the CUs. All write partial states. Each role
 // has its own pipeline shape (stages x keys per stage) inside one LDS
 // allocation, sized so that two work-groups fit on a CU.
 template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK>
-__global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs sa, const int n_prefix) {
+__global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs ga, const TileArgs sa,
+                                                             const int n_prefix, const int n_group,
+                                                             const GroupTable gt) {
   static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
   constexpr int PB = TileSmem<D, PNS, PSK>::BYTES, SB = TileSmem<D, SNS, SSK>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false>(pa, bid, smem);
-  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1)>(sa, bid - n_prefix, smem);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false>(pa, gt, bid, smem);
+  else if (bid < n_prefix + n_group) attn_item<D, PRB, PRW, PKG, PNS, PSK, false>(ga, gt, bid - n_prefix, smem);
+  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1)>(sa, gt, bid - n_prefix - n_group, smem);
 }
 
 }  // namespace ca

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "plan.h"
 
@@ -155,12 +156,11 @@ static PhaseTile choose_suffix(const ca_plan& pl, int32_t cus, bool fill) {
 // heads) and the grouped item stays at most half as long as a prefix item: a
 // decode stage costs about one memory round trip, so longer chains become the
 // launch's critical path. Otherwise one head per item.
-static int32_t pick_heads_per_item(const ca_plan& pl, const PhaseTile& pre, const PhaseTile& suf, int32_t cus) {
+static int32_t pick_heads_per_item(const ca_plan& pl, int64_t prefix_items, int64_t prefix_stages,
+                                   const PhaseTile& suf, int32_t cus) {
   if (suf.kernel != 1) return 1;
   if (pl.p.heads_per_item > 0) return pl.p.heads_per_item;
-  const int64_t prefix_items = (int64_t)pre.mtiles * pl.hkv * pre.splits;
   const int64_t per_head = (int64_t)pl.num_reqs * suf.mtiles * suf.splits;
-  const int64_t prefix_stages = pre.split_tokens / kTileKeys;
   const int64_t suffix_stages = suf.split_tokens / kTileKeys;
   for (int32_t h = 1; h <= pl.hkv && h <= 8; ++h) {
     if (pl.hkv % h) continue;
@@ -187,18 +187,72 @@ static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_
 }
 
 // MFMA work of the per-request phase: every KV head of request r runs
-// ceil(q_len*G / 16) blocks of 16 rows over its keys (causal rows stop early,
+// ceil(q_len*G / 16) blocks of 16 rows over its keys from key_start[r] (null:
+// from 0) (causal rows stop early,
 // counted here as the mean of the first and last row's key count).
-static double suffix_padded_flops(const ca_plan& pl, const int32_t* qsl, const int32_t* seq_lens, int32_t key_start) {
+static double suffix_padded_flops(const ca_plan& pl, const int32_t* qsl, const int32_t* seq_lens,
+                                  const int64_t* key_start) {
   double f = 0.0;
   for (int32_t r = 0; r < pl.num_reqs; ++r) {
     const int64_t ql = (int64_t)qsl[r + 1] - qsl[r];
-    const int64_t keys_last = seq_lens[r] - key_start;
+    const int64_t keys_last = seq_lens[r] - (key_start ? key_start[r] : 0);
     const int64_t keys_first = keys_last - (ql - 1);
     const double blocks = (double)cdiv(ql * pl.group, 16);
     f += blocks * 16.0 * 0.5 * (double)(keys_first + keys_last);
   }
   return f * 4.0 * pl.d * pl.hkv;
+}
+
+// Second shared level. FlashInfer's cascade runs any number of levels
+// ([p2] section 7), and the workloads of [p2] section 3 nest: a system
+// prompt shared by every request, then a document or prompt shared by some,
+// then each request's own tokens. A candidate group is a maximal run of
+// consecutive requests in which every adjacent pair shares more leading
+// pages than the batch-wide prefix (equality of page ids is transitive, so
+// the run's members share exactly the minimum of those adjacent counts). Its
+// shared length follows the batch-wide rule ([p2] section 8 Step 2): capped
+// at the members' smallest num_computed, floored to a page. A group is kept
+// when it has >= 2 requests and shares >= 256 tokens beyond the batch-wide
+// prefix (the pages' prefix-length gate, [p2] section 3).
+struct GroupCand {
+  int32_t a, b, len;
+  int64_t saving;   // KV positions not re-read: (members - 1) * extra length
+};
+
+static std::vector<GroupCand> find_level1_groups(const int32_t* bt, int32_t n, int32_t stride,
+                                                 const int32_t* seq_lens, const int32_t* qsl, int32_t ps,
+                                                 int32_t common_blocks, int64_t plen) {
+  std::vector<GroupCand> out;
+  const int64_t j0 = plen / ps;
+  // pages shared by requests r and r + 1 (columns below common_blocks are
+  // shared by every request and inside every request's pages)
+  std::vector<int64_t> lcp(n > 1 ? n - 1 : 0);
+  for (int32_t r = 0; r + 1 < n; ++r) {
+    const int64_t lim = std::min(cdiv(seq_lens[r], ps), cdiv(seq_lens[r + 1], ps));
+    const int32_t* x = bt + (int64_t)r * stride;
+    const int32_t* y = x + stride;
+    int64_t j = std::min<int64_t>(common_blocks, lim);
+    while (j < lim && x[j] == y[j]) ++j;
+    lcp[r] = j;
+  }
+  for (int32_t a = 0; a < n;) {
+    int32_t b = a + 1;
+    int64_t shared = INT64_MAX;
+    while (b < n && lcp[b - 1] > j0) shared = std::min(shared, lcp[b++ - 1]);
+    if (b - a >= 2) {
+      int64_t len = shared * ps;
+      for (int32_t r = a; r < b; ++r) len = std::min<int64_t>(len, seq_lens[r] - (qsl[r + 1] - qsl[r]));
+      len = len / ps * ps;
+      if (len - plen >= 256) out.push_back({a, b, (int32_t)len, (int64_t)(b - a - 1) * (len - plen)});
+    }
+    a = b;
+  }
+  if ((int)out.size() > kMaxLevel1Groups) {   // keep the groups that save the most
+    std::stable_sort(out.begin(), out.end(), [](const GroupCand& x, const GroupCand& y) { return x.saving > y.saving; });
+    out.resize(kMaxLevel1Groups);
+    std::sort(out.begin(), out.end(), [](const GroupCand& x, const GroupCand& y) { return x.a < y.a; });
+  }
+  return out;
 }
 
 }  // namespace ca
@@ -245,6 +299,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.heads_per_item < 0 || (p.heads_per_item > 0 && p.num_kv_heads % p.heads_per_item != 0))
     return fail(CA_EINVAL, "heads_per_item must be 0 or divide num_kv_heads");
   if (p.separate_phases != 0 && p.separate_phases != 1) return fail(CA_EINVAL, "separate_phases must be 0 or 1");
+  if (p.max_levels < 0 || p.max_levels > 2) return fail(CA_EINVAL, "max_levels must be 0, 1 or 2");
 
   const int32_t n = p.num_reqs, ps = p.page_size, stride = p.block_table_stride;
   if (qsl[0] != 0) return fail(CA_EMETA, "query_start_loc[0] must be 0");
@@ -318,26 +373,70 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     double extra = 0.0;
     if (shared_bytes <= cm.mall_bytes) extra = reread;
     else hbm_tokens = sum_seq;
-    pl->est_us_noncascade = (float)est_suffix_us(*pl, hbm_tokens, suffix_padded_flops(*pl, qsl, seq_lens, 0),
+    pl->est_us_noncascade = (float)est_suffix_us(*pl, hbm_tokens, suffix_padded_flops(*pl, qsl, seq_lens, nullptr),
                                                  nc.splits, nc.splits > 1, cus, cm, extra);
   }
 
-  // Cascade estimate (only meaningful when something is shared).
+  // Cascade estimate (only meaningful when something is shared): the
+  // batch-wide prefix, the group level when there is one, each request's
+  // remaining positions, and the merge.
   PhaseTile pre, suf;
-  double pre_us = 0.0;
+  Level1 lvl1;
+  std::vector<int64_t> kstart(n, plen);   // first suffix position of each request
+  int64_t group_items = 0, group_stages = 0;
   if (plen > 0) {
     pl->prefix_len = (int32_t)plen;
+    double pre_us = 0.0;
     pre = choose_prefix(*pl, cus, cm, &pre_us);
+    std::vector<GroupCand> groups;
+    if (p.max_levels != 1) groups = find_level1_groups(bt, n, stride, seq_lens, qsl, ps, pl->common_blocks, plen);
+    double t_grp = 0.0;
+    int64_t group_tokens = 0;
+    if (!groups.empty()) {
+      // Every group gets the same number of KV splits (so a group's rows
+      // fill the same partial slots): about 512 keys per item for the
+      // longest group, at most 8 splits unless the per-item cap needs more.
+      lvl1.n = (int32_t)groups.size();
+      int64_t max_tiles = 1;
+      for (const auto& g : groups) max_tiles = std::max(max_tiles, cdiv(g.len - plen, kTileKeys));
+      const int64_t splits =
+          std::max(std::min<int64_t>(cdiv(max_tiles, 8), 8), cdiv(max_tiles, kMaxItemTokens / kTileKeys));
+      lvl1.splits = (int32_t)splits;
+      double flops = 0.0;
+      for (int32_t j = 0; j < lvl1.n; ++j) {
+        const GroupCand& g = groups[j];
+        lvl1.req_begin[j] = g.a;
+        lvl1.req_end[j] = g.b;
+        lvl1.key_end[j] = g.len;
+        const int64_t tiles_per = cdiv(cdiv(g.len - plen, kTileKeys), splits);
+        lvl1.split_tokens[j] = (int32_t)(tiles_per * kTileKeys);
+        group_stages = std::max(group_stages, tiles_per);
+        lvl1.item_begin[j] = (int32_t)group_items;
+        const int64_t mtiles = cdiv((int64_t)(qsl[g.b] - qsl[g.a]) * pl->group, pre.rows_per_wg());
+        group_items += mtiles * pl->hkv * splits;
+        group_tokens += g.len - plen;
+        flops += 4.0 * (double)(mtiles * pre.rows_per_wg()) * pl->hkv * pl->d * (double)(g.len - plen);
+        for (int32_t r = g.a; r < g.b; ++r) kstart[r] = g.len;
+      }
+      lvl1.item_begin[lvl1.n] = (int32_t)group_items;
+      t_grp = std::max(flops / ((double)cus * cm.cu_mfma_rows), bpt * group_tokens / cm.hbm_bw) * 1e6 +
+              cm.item_latency_us;
+    }
+    int64_t suffix_tokens = 0, max_suffix = 0;
+    for (int32_t r = 0; r < n; ++r) {
+      suffix_tokens += seq_lens[r] - kstart[r];
+      max_suffix = std::max<int64_t>(max_suffix, seq_lens[r] - kstart[r]);
+    }
     pl->key_start = (int32_t)plen;
-    pl->max_suffix_len = max_seq - (int32_t)plen;
+    pl->max_suffix_len = (int32_t)max_suffix;
     suf = choose_suffix(*pl, cus, true);
-    const double t_suf = est_suffix_us(*pl, pl->kv_tokens_cascade - plen,
-                                       suffix_padded_flops(*pl, qsl, seq_lens, (int32_t)plen), suf.splits, false,
-                                       cus, cm, 0.0);
-    const double merge_bytes = (double)(pre.splits + suf.splits) * total_q * pl->hq * (pl->d + 1) * 4.0 +
+    const double t_suf = est_suffix_us(*pl, suffix_tokens, suffix_padded_flops(*pl, qsl, seq_lens, kstart.data()),
+                                       suf.splits, false, cus, cm, 0.0);
+    const double merge_bytes = (double)(pre.splits + lvl1.splits + suf.splits) * total_q * pl->hq * (pl->d + 1) * 4.0 +
                                (double)total_q * pl->hq * pl->d * 2.0;
-    pl->est_us_cascade = (float)(pre_us + cm.launch_us + t_suf +
+    pl->est_us_cascade = (float)(pre_us + t_grp + cm.launch_us + t_suf +
                                  (merge_bytes / cm.mall_bw) * 1e6 + cm.launch_us);
+    pl->kv_tokens_cascade = plen + group_tokens + suffix_tokens;
   }
 
   bool cascade = false;
@@ -347,15 +446,17 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
 
   if (cascade) {
     pl->key_start = (int32_t)plen;
-    pl->max_suffix_len = max_seq - (int32_t)plen;
     pl->prefix = pre;
     pl->suffix = suf;
-    pl->prefix.stages = 2;   // both phases share one launch (two work-groups per CU)
+    pl->lvl1 = lvl1;
+    pl->prefix.stages = 2;   // all phases share one launch (two work-groups per CU)
     pl->suffix.stages = 2;
-    pl->suffix.heads_per_item = pick_heads_per_item(*pl, pre, suf, cus);
+    pl->suffix.heads_per_item =
+        pick_heads_per_item(*pl, (int64_t)pre.mtiles * pl->hkv * pre.splits + group_items,
+                            std::max<int64_t>(pre.split_tokens / kTileKeys, group_stages), suf, cus);
     pl->merge_in_suffix = 0;
     pl->separate_phases = p.separate_phases;
-    pl->num_slots = pre.splits + suf.splits;
+    pl->num_slots = pre.splits + lvl1.splits + suf.splits;
     pl->direct_out = false;
   } else {
     pl->key_start = 0;
@@ -400,12 +501,27 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->merge_in_suffix = pl->merge_in_suffix;
   out->suffix_heads_per_item = pl->suffix.heads_per_item;
   out->separate_phases = pl->separate_phases;
+  out->num_level1_groups = pl->lvl1.n;
+  out->level1_splits = pl->lvl1.splits;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;
   out->kv_tokens_noncascade = pl->kv_tokens_noncascade;
   out->est_us_cascade = pl->est_us_cascade;
   out->est_us_noncascade = pl->est_us_noncascade;
+  return CA_OK;
+}
+
+extern "C" ca_status_t cascade_attn_plan_groups(ca_plan_t pl, int32_t capacity, int32_t* groups_out, int32_t* n_out) {
+  if (!pl || !n_out || (capacity > 0 && !groups_out)) return fail(CA_EINVAL, "null plan or output");
+  if (capacity < 0) return fail(CA_EINVAL, "capacity must be >= 0");
+  const Level1& L = pl->lvl1;
+  for (int32_t j = 0; j < L.n && j < capacity; ++j) {
+    groups_out[3 * j] = L.req_begin[j];
+    groups_out[3 * j + 1] = L.req_end[j];
+    groups_out[3 * j + 2] = L.key_end[j];
+  }
+  *n_out = L.n;
   return CA_OK;
 }
 

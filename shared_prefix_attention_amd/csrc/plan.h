@@ -30,6 +30,20 @@ struct PhaseTile {
 // Longest KV range one work item may cover (its page ids are held in LDS).
 constexpr int kMaxItemTokens = 512 * 16;
 
+// Second shared level: groups of consecutive requests that share pages
+// beyond the batch-wide prefix. At most kMaxLevel1Groups (they travel to the
+// kernels as launch arguments).
+constexpr int kMaxLevel1Groups = 64;
+struct Level1 {
+  int32_t n = 0;                               // groups in use
+  int32_t splits = 0;                          // KV splits of every group
+  int32_t req_begin[kMaxLevel1Groups] = {};    // requests [req_begin, req_end), ascending
+  int32_t req_end[kMaxLevel1Groups] = {};
+  int32_t key_end[kMaxLevel1Groups] = {};      // group shares positions [prefix_len, key_end)
+  int32_t split_tokens[kMaxLevel1Groups] = {}; // keys per split (multiple of kTileKeys)
+  int32_t item_begin[kMaxLevel1Groups + 1] = {};
+};
+
 }  // namespace ca
 
 struct ca_plan {
@@ -53,6 +67,7 @@ struct ca_plan {
   bool direct_out = false;    // the last attention launch writes the bf16 output directly
   int32_t merge_in_suffix = 0;// cascade: the suffix kernel folds in the prefix partials
   int32_t separate_phases = 0;// cascade: prefix and suffix as two launches
+  ca::Level1 lvl1;            // cascade: second shared level (n = 0: none)
   int64_t slot_elems = 0;     // T * Hq * d
   int64_t ws_lse_offset = 0;  // byte offset of the partial LSE array
   int64_t workspace_bytes = 0;

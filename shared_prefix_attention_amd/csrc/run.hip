@@ -22,7 +22,8 @@ using namespace ca;
 
 namespace {
 
-enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_PREFIX = 4, K_SUFFIX = 5, K_KINDS = 6 };
+enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_PREFIX = 4, K_SUFFIX = 5, K_LEVEL1 = 6, K_KINDS = 7 };
+static_assert(kMaxGroups == kMaxLevel1Groups, "group table size");
 static_assert(K_KINDS == CA_PROFILE_KINDS, "profile kinds");
 
 struct Profiler {
@@ -69,14 +70,14 @@ ca_status_t check_launch(const char* what) {
 }
 
 template <int D, int RB, int RW, int KG, int NS>
-void launch_tile(const TileArgs& args, int grid, hipStream_t s, int kind) {
-  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, (KG > 1)>, dim3(grid), dim3(64 * RW * KG), s, args);
+void launch_tile(const TileArgs& args, const GroupTable& gt, int grid, hipStream_t s, int kind) {
+  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, (KG > 1)>, dim3(grid), dim3(64 * RW * KG), s, args, gt);
 }
 
 template <int D, int RB, int RW, int KG>
-void launch_tile_ns(const TileArgs& args, int ns, int grid, hipStream_t s, int kind) {
-  if (ns == 4) launch_tile<D, RB, RW, KG, 4>(args, grid, s, kind);
-  else launch_tile<D, RB, RW, KG, 2>(args, grid, s, kind);
+void launch_tile_ns(const TileArgs& args, const GroupTable& gt, int ns, int grid, hipStream_t s, int kind) {
+  if (ns == 4) launch_tile<D, RB, RW, KG, 4>(args, gt, grid, s, kind);
+  else launch_tile<D, RB, RW, KG, 2>(args, gt, grid, s, kind);
 }
 
 bool item_ok(const PhaseTile& ph) { return ph.split_tokens > 0 && ph.split_tokens <= kMaxItemTokens && ph.split_tokens % kTileKeys == 0; }
@@ -91,44 +92,47 @@ int shape_id(const PhaseTile& ph) {
 }
 
 template <int D>
-ca_status_t run_tile(const TileArgs& args, const PhaseTile& ph, int64_t grid, hipStream_t s, int kind) {
+ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const PhaseTile& ph, int64_t grid, hipStream_t s,
+                     int kind) {
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(ph)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   switch (shape_id(ph)) {
-    case 0: launch_tile_ns<D, 1, 4, 1>(args, ph.stages, (int)grid, s, kind); break;
-    case 1: launch_tile_ns<D, 2, 4, 1>(args, ph.stages, (int)grid, s, kind); break;
-    case 2: launch_tile_ns<D, 1, 1, 4>(args, ph.stages, (int)grid, s, kind); break;
+    case 0: launch_tile_ns<D, 1, 4, 1>(args, gt, ph.stages, (int)grid, s, kind); break;
+    case 1: launch_tile_ns<D, 2, 4, 1>(args, gt, ph.stages, (int)grid, s, kind); break;
+    case 2: launch_tile_ns<D, 1, 1, 4>(args, gt, ph.stages, (int)grid, s, kind); break;
     default: return fail(CA_EINVAL, "unsupported work-group shape in plan");
   }
   return check_launch("attention kernel launch");
 }
 
-// Both roles: 2 stages x 64 keys (64 KB of LDS, two work-groups per CU).
+// All roles: 2 stages x 64 keys (64 KB of LDS, two work-groups per CU).
 template <int D, int P, int S>
-void launch_phases(const TileArgs& pa, const TileArgs& sa, int n_prefix, int grid, hipStream_t s) {
+void launch_phases(const TileArgs& pa, const TileArgs& ga, const TileArgs& sa, int n_prefix, int n_group,
+                   const GroupTable& gt, int grid, hipStream_t s) {
   constexpr int PRB = P == 1 ? 2 : 1;
   constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
   launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, 2, 64, 1, SRW, SKG, 2, 64>, dim3(grid), dim3(256), s,
-         pa, sa, n_prefix);
+         pa, ga, sa, n_prefix, n_group, gt);
 }
 
 template <int D>
-ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix, const TileArgs& sa,
-                       const PhaseTile& sp, int64_t n_suffix, hipStream_t s) {
-  if (n_prefix + n_suffix > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
+ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix, const TileArgs& ga,
+                       int64_t n_group, const GroupTable& gt, const TileArgs& sa, const PhaseTile& sp,
+                       int64_t n_suffix, hipStream_t s) {
+  if (n_prefix + n_group + n_suffix > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(pp) || !item_ok(sp)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   const int pid = shape_id(pp), sid = shape_id(sp);
   if ((pid != 0 && pid != 1) || (sid != 0 && sid != 2) || pp.stages != 2 || sp.stages != 2)
     return fail(CA_EINVAL, "unsupported work-group shape in plan");
-  const int grid = (int)(n_prefix + n_suffix);
-  const int np = (int)n_prefix;
+  const int grid = (int)(n_prefix + n_group + n_suffix);
+  const int np = (int)n_prefix, ng = (int)n_group;
   if (sid == 0) {
-    if (pid == 0) launch_phases<D, 0, 0>(pa, sa, np, grid, s);
-    else launch_phases<D, 1, 0>(pa, sa, np, grid, s);
+    if (pid == 0) launch_phases<D, 0, 0>(pa, ga, sa, np, ng, gt, grid, s);
+    else launch_phases<D, 1, 0>(pa, ga, sa, np, ng, gt, grid, s);
   } else {
-    if (pid == 0) launch_phases<D, 0, 2>(pa, sa, np, grid, s);
-    else launch_phases<D, 1, 2>(pa, sa, np, grid, s);
+    if (pid == 0) launch_phases<D, 0, 2>(pa, ga, sa, np, ng, gt, grid, s);
+    else launch_phases<D, 1, 2>(pa, ga, sa, np, ng, gt, grid, s);
   }
   return check_launch("cascade phases kernel launch");
 }
@@ -171,6 +175,22 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   base.part_o = part_o;
   base.part_lse = part_lse;
 
+  // second shared level (none: n = 0)
+  GroupTable gt{};
+  const Level1& L = pl->lvl1;
+  gt.n = pl->use_cascade ? L.n : 0;
+  for (int j = 0; j < gt.n; ++j) {
+    gt.item_begin[j] = L.item_begin[j];
+    gt.req_begin[j] = L.req_begin[j];
+    gt.req_end[j] = L.req_end[j];
+    gt.key_end[j] = L.key_end[j];
+    gt.split_tokens[j] = L.split_tokens[j];
+  }
+  gt.item_begin[gt.n] = gt.n > 0 ? L.item_begin[gt.n] : 0;
+  for (int j = 0; j < gt.n; ++j)
+    if (L.split_tokens[j] <= 0 || L.split_tokens[j] > kMaxItemTokens || L.split_tokens[j] % kTileKeys)
+      return fail(CA_EINVAL, "group work item exceeds the per-item KV limit");
+
   ca_status_t st;
   TileArgs sa = base;
   sa.prefix_mode = 0;
@@ -179,8 +199,10 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   sa.splits = pl->suffix.splits;
   sa.split_tokens = pl->suffix.split_tokens;
   sa.heads_per_item = pl->suffix.heads_per_item;
-  sa.slot_base = pl->use_cascade ? pl->prefix.splits : 0;
+  sa.slot_base = pl->use_cascade ? pl->prefix.splits + (gt.n > 0 ? L.splits : 0) : 0;
   sa.direct = pl->direct_out ? 1 : 0;
+  sa.lvl1_slot_base = pl->prefix.splits;
+  sa.lvl1_slots = gt.n > 0 ? L.splits : 0;
   // several KV heads per item only in the decode shape (its waves split the keys)
   if (sa.heads_per_item < 1 || pl->hkv % sa.heads_per_item != 0 ||
       (sa.heads_per_item > 1 && pl->suffix.key_groups == 1))
@@ -197,14 +219,23 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     pa.slot_base = 0;
     pa.direct = 0;
     const int64_t n_prefix = (int64_t)pa.mtiles * pl->hkv * pa.splits;
+    TileArgs ga = base;   // group level: prefix-shaped items over each group's extra pages
+    ga.prefix_mode = 2;
+    ga.key_start = pl->prefix_len;
+    ga.splits = gt.n > 0 ? L.splits : 1;
+    ga.split_tokens = kTileKeys;   // per group in the table
+    ga.slot_base = pl->prefix.splits;
+    ga.direct = 0;
+    const int64_t n_group = gt.n > 0 ? gt.item_begin[gt.n] : 0;
     if (pl->separate_phases) {
-      st = run_tile<D>(pa, pl->prefix, n_prefix, s, K_PREFIX);
-      if (st == CA_OK) st = run_tile<D>(sa, pl->suffix, n_suffix, s, K_SUFFIX);
+      st = run_tile<D>(pa, gt, pl->prefix, n_prefix, s, K_PREFIX);
+      if (st == CA_OK) st = run_tile<D>(ga, gt, pl->prefix, n_group, s, K_LEVEL1);
+      if (st == CA_OK) st = run_tile<D>(sa, gt, pl->suffix, n_suffix, s, K_SUFFIX);
     } else {
-      st = run_phases<D>(pa, pl->prefix, n_prefix, sa, pl->suffix, n_suffix, s);
+      st = run_phases<D>(pa, pl->prefix, n_prefix, ga, n_group, gt, sa, pl->suffix, n_suffix, s);
     }
   } else {
-    st = run_tile<D>(sa, pl->suffix, n_suffix, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
+    st = run_tile<D>(sa, gt, pl->suffix, n_suffix, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
   }
   if (st != CA_OK) return st;
   if (!pl->direct_out) {

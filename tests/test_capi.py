@@ -88,8 +88,13 @@ def test_plan_matches_oracle_on_workloads(name):
     assert info["common_prefix_len"] == plen
     assert info["gates_pass"] == int(oracle.passes_cascade_gates(plen, b.workload.num_reqs))
     assert info["kv_tokens_noncascade"] == oracle.kv_tokens_standard(b.seq_lens.tolist())
-    assert info["kv_tokens_cascade"] == oracle.kv_tokens_cascade(plen, b.seq_lens.tolist())
+    groups = oracle.level1_groups(b.block_table.tolist(), b.seq_lens.tolist(), b.num_computed.tolist(), ps, plen)
+    assert info["kv_tokens_cascade"] == oracle.kv_tokens_multilevel(plen, groups, b.seq_lens.tolist())
+    if not groups:
+        assert info["kv_tokens_cascade"] == oracle.kv_tokens_cascade(plen, b.seq_lens.tolist())
     assert info["total_q"] == b.total_q
+    if plen > 0:
+        assert spa.cascade_attn_plan_groups(_plan(b, mode="on")) == groups
     if not info["gates_pass"]:
         assert info["use_cascade"] == 0
     on = _plan(b, mode="on").info
@@ -184,6 +189,9 @@ def test_error_codes():
     with pytest.raises(spa.CascadeAttnError) as e:
         _try(separate_phases=2)
     assert e.value.status == _lib.CA_EINVAL
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(max_levels=3)
+    assert e.value.status == _lib.CA_EINVAL
 
 
 def test_plan_partition_is_consistent():
@@ -196,7 +204,8 @@ def test_plan_partition_is_consistent():
             assert info["workspace_bytes"] >= slots * T * hq * (d + 1) * 4
             if info["use_cascade"]:
                 assert info["merge_in_suffix"] == 0
-                assert slots == info["prefix_splits"] + info["suffix_chunks"]
+                assert slots == info["prefix_splits"] + info["level1_splits"] + info["suffix_chunks"]
+                assert (info["level1_splits"] > 0) == (info["num_level1_groups"] > 0)
                 assert info["prefix_splits"] >= 1
             assert info["suffix_chunk_tokens"] % 64 == 0
             assert 0 < info["suffix_chunk_tokens"] <= 8192
@@ -242,3 +251,91 @@ def test_auto_takes_the_measured_faster_path():
     for name, casc in expect.items():
         b = workloads.make_batch(workloads.get(name))
         assert _plan(b, mode="auto").info["use_cascade"] == casc, name
+
+
+def _nested_tables(rng, n, ps=16):
+    """Random block tables with a level-0 prefix, runs of requests sharing
+    extra pages (sometimes only some of a run), and random lengths."""
+    level0 = int(rng.integers(16, 20))
+    rows, seq, nxt = [], [], [1000]
+
+    def fresh(k):
+        ids = list(range(nxt[0], nxt[0] + k))
+        nxt[0] += k
+        return ids
+
+    base = fresh(level0)
+    r = 0
+    while r < n:
+        m = int(rng.integers(1, 5))
+        extra = fresh(int(rng.integers(0, 40)))
+        for i in range(min(m, n - r)):
+            keep = len(extra) if rng.random() < 0.8 else int(rng.integers(0, len(extra) + 1))
+            own = fresh(int(rng.integers(1, 6)))
+            row = base + extra[:keep] + own
+            rows.append(row)
+            seq.append((len(row) - 1) * ps + int(rng.integers(1, ps + 1)))
+        r += m
+    stride = max(len(x) for x in rows) + 1
+    bt = np.zeros((n, stride), dtype=np.int32)
+    for i, row in enumerate(rows):
+        bt[i, :len(row)] = row
+        bt[i, len(row):] = row[0]
+    seq = np.array(seq, dtype=np.int32)
+    q = np.minimum(rng.integers(1, 40, n), seq - level0 * ps).astype(np.int32)
+    return bt, seq, q, nxt[0]
+
+
+def test_level1_groups_match_oracle_on_random_batches():
+    rng = np.random.default_rng(41)
+    for _ in range(300):
+        n = int(rng.integers(1, 24))
+        bt, seq, q, pages = _nested_tables(rng, n)
+        nc = seq - q
+        qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+        pl = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=pages,
+                                   kv_strides=(16 * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
+                                   seq_lens=seq, num_computed_tokens=nc, mode="on", num_cus=256)
+        info = pl.info
+        plen = info["common_prefix_len"]
+        want = oracle.level1_groups(bt.tolist(), seq.tolist(), nc.tolist(), 16, plen)
+        got = spa.cascade_attn_plan_groups(pl)
+        assert got == want
+        assert info["num_level1_groups"] == len(want)
+        assert info["kv_tokens_cascade"] == oracle.kv_tokens_multilevel(plen, want, seq.tolist())
+        single = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=pages,
+                                       kv_strides=(16 * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
+                                       seq_lens=seq, num_computed_tokens=nc, mode="on", num_cus=256, max_levels=1)
+        assert single.info["num_level1_groups"] == 0 and spa.cascade_attn_plan_groups(single) == []
+
+
+def test_level1_keeps_the_64_groups_that_save_most():
+    """100 pairs of requests, each pair sharing its own document of a
+    different length beyond the batch prefix: the plan keeps 64 groups, the
+    ones whose documents are longest (saving = extra tokens), in batch order."""
+    ps, level0 = 16, 16
+    rows, seq = [], []
+    nxt = 1000
+    doc_pages = [17 + (i * 37) % 50 for i in range(100)]
+    for i in range(100):
+        doc = list(range(nxt, nxt + doc_pages[i]))
+        nxt += doc_pages[i]
+        for _ in range(2):
+            row = list(range(level0)) + doc + [nxt]
+            nxt += 1
+            rows.append(row)
+            seq.append(len(row) * ps)
+    stride = max(len(x) for x in rows)
+    bt = np.zeros((200, stride), dtype=np.int32)
+    for i, row in enumerate(rows):
+        bt[i, :len(row)] = row
+    seq = np.array(seq, dtype=np.int32)
+    qsl = np.arange(201, dtype=np.int32)
+    pl = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=ps, num_pages=nxt,
+                               kv_strides=(ps * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
+                               seq_lens=seq, mode="on", num_cus=256)
+    got = spa.cascade_attn_plan_groups(pl)
+    every = oracle.level1_groups(bt.tolist(), seq.tolist(), (seq - 1).tolist(), ps, level0 * ps)
+    assert len(every) == 100 and len(got) == 64
+    by_saving = sorted(every, key=lambda g: -(g[2] - level0 * ps))
+    assert sorted(got) == sorted(by_saving[:64]) and got == sorted(got)

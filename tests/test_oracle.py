@@ -364,6 +364,123 @@ def test_common_blocks_brute_force_tiny():
         assert oracle.common_prefix_blocks(bt, lens, ps) == best
 
 
+# ------------------------------------------------------ second shared level
+
+# Seven requests, page size 4. Pages 0 and 1 are shared by all (level 0,
+# 8 tokens). Requests 0-2 also share pages 10 and 11 (0 and 1 share page 12
+# too); requests 4-6 share page 40 (4 and 5 also page 41); request 3 shares
+# nothing more. Row 1's padding column copies row 0's real page 21.
+_L1_BT = [[0, 1, 10, 11, 12, 20, 21],
+          [0, 1, 10, 11, 12, 22, 21],
+          [0, 1, 10, 11, 13, 23, 0],
+          [0, 1, 30, 31, 0, 0, 0],
+          [0, 1, 40, 41, 42, 0, 0],
+          [0, 1, 40, 41, 43, 0, 0],
+          [0, 1, 40, 50, 0, 0, 0]]
+_L1_SEQ = [26, 24, 22, 16, 20, 18, 14]
+
+
+def test_level1_groups_hand_case():
+    """Worked by hand. Adjacent shared pages: (0,1) 5, (1,2) 4, (2,3) 2,
+    (3,4) 2, (4,5) 4, (5,6) 3; the runs sharing more than the 2 level-0
+    pages are requests 0-2 (4 pages = 16 tokens) and 4-6 (3 pages = 12
+    tokens). Caps (num_computed = seq - 1): 0-2 min 21 -> 16; 4-6 min 13 ->
+    12."""
+    nc = [s - 1 for s in _L1_SEQ]
+    assert oracle.common_prefix_blocks(_L1_BT, _L1_SEQ, 4) == 2
+    assert oracle.level1_groups(_L1_BT, _L1_SEQ, nc, 4, 8, min_extra_tokens=4) == [(0, 3, 16), (4, 7, 12)]
+    # the gate on the extra length: 4-6 adds only 4 tokens
+    assert oracle.level1_groups(_L1_BT, _L1_SEQ, nc, 4, 8, min_extra_tokens=5) == [(0, 3, 16)]
+    # the cap binds: request 2 has computed only 14 tokens -> floor(14 / 4) * 4 = 12
+    nc2 = list(nc)
+    nc2[2] = 14
+    assert oracle.level1_groups(_L1_BT, _L1_SEQ, nc2, 4, 8, min_extra_tokens=4) == [(0, 3, 12), (4, 7, 12)]
+    # members: a group needs two requests, so 4-6 split at 5 leaves none there
+    bt3 = [row[:] for row in _L1_BT]
+    bt3[5][2] = 44
+    assert oracle.level1_groups(bt3, _L1_SEQ, nc, 4, 8, min_extra_tokens=4) == [(0, 3, 16)]
+    # nothing nested: no group
+    flat = [[0, 1, 100 + r, 0] for r in range(4)]
+    assert oracle.level1_groups(flat, [13] * 4, [12] * 4, 4, 8, min_extra_tokens=1) == []
+
+
+def test_level1_groups_brute_force_tiny():
+    """Random tiny tables against a differently written rule: rows a..b-1
+    share c columns when their first c real columns form one tuple; a run is
+    extended while some c above the level-0 pages is shared."""
+    rng = np.random.default_rng(31)
+    for _ in range(1500):
+        n = int(rng.integers(1, 6))
+        cols = int(rng.integers(2, 6))
+        ps = int(rng.integers(1, 4))
+        bt = rng.integers(0, 3, (n, cols)).tolist()
+        for row in bt:
+            row[0] = 7                           # one level-0 page
+        lens = rng.integers(ps + 1, cols * ps + 1, n).tolist()
+        nc = [int(rng.integers(1, x + 1)) for x in lens]
+        level0 = ps
+
+        def shared(a, b):
+            limit = min(-(-x // ps) for x in lens[a:b])
+            return max(c for c in range(limit + 1) if len({tuple(bt[r][:c]) for r in range(a, b)}) == 1)
+
+        want, a = [], 0
+        while a < n:
+            b = a + 1
+            while b < n and shared(a, b + 1) > 1:
+                b += 1
+            if b - a >= 2:
+                length = min(shared(a, b) * ps, min(nc[a:b])) // ps * ps
+                if length - level0 >= 1:
+                    want.append((a, b, length))
+            a = b
+        assert oracle.level1_groups(bt, lens, nc, ps, level0, min_extra_tokens=1) == want
+
+
+def test_multilevel_split_equals_full_attention():
+    """Three levels with the oracle's own pieces -- every query over the
+    level-0 prefix, each group's queries over the group's extra positions
+    (both non-causal), each request over the rest (causal), LSE merge --
+    equal full attention (every shared position is at or below every member
+    query's position because of the cap)."""
+    w = workloads.Workload("nested", 7, 16, (3, 20), (1, 4), 4, 2, 16, page_size=8, seed=17,
+                           groups=((3, 20), (2, 37)))
+    b = workloads.make_batch(w)
+    G = w.num_q_heads // w.num_kv_heads
+    bt, qsl, sl = b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy()
+    full_o, full_l = oracle.attention_full(b.q.float().numpy(), b.k_cache.float().numpy(),
+                                           b.v_cache.float().numpy(), bt, qsl, sl, w.page_size)
+    nc = b.num_computed.numpy()
+    p0 = oracle.cascade_prefix_len(oracle.common_prefix_blocks(bt, sl, 8), 8, nc)
+    groups = oracle.level1_groups(bt, sl, nc, 8, p0, min_extra_tokens=1)
+    assert p0 == 16 and groups == [(0, 3, 32), (3, 5, 48)]   # whole shared pages only
+    start = [p0] * w.num_reqs
+    for a, e, length in groups:
+        for r in range(a, e):
+            start[r] = length
+    for r in range(w.num_reqs):
+        q0, q1 = int(qsl[r]), int(qsl[r + 1])
+        k, v = _dense_kv(b, r)
+        pos = int(nc[r]) + np.arange(q1 - q0)
+        for h in range(w.num_q_heads):
+            g = h // G
+            rows = b.q[q0:q1, h].double().numpy()
+            parts = [oracle.attend(rows, k[:p0, g].numpy(), v[:p0, g].numpy(), w.softmax_scale),
+                     oracle.attend(rows, k[p0:start[r], g].numpy(), v[p0:start[r], g].numpy(), w.softmax_scale)]
+            t = np.arange(start[r], k.shape[0])
+            vis = t[None, :] <= pos[:, None]
+            parts.append(oracle.attend(rows, k[start[r]:, g].numpy(), v[start[r]:, g].numpy(), w.softmax_scale, vis))
+            o_m, l_m = oracle.merge_states([p[0] for p in parts], [p[1] for p in parts])
+            assert np.abs(o_m - full_o[q0:q1, h]).max() < 1e-12
+            assert np.abs(l_m - full_l[q0:q1, h]).max() < 1e-12
+
+
+def test_kv_tokens_multilevel_hand():
+    # level 0: 16; group (0, 2) shares 48 (32 extra); suffixes 12 + 22 + 14
+    assert oracle.kv_tokens_multilevel(16, [(0, 2, 48)], [60, 70, 30]) == 16 + 32 + 12 + 22 + 14
+    assert oracle.kv_tokens_multilevel(16, [], [60, 70, 30]) == oracle.kv_tokens_cascade(16, [60, 70, 30])
+
+
 # --------------------------------------------------------------- input recipe
 
 def test_workload_structure_matches_recipe():

@@ -33,6 +33,18 @@ SMALL = {
         Workload("fresh_prefill", 4, 0, (30, 50), (30, 50), 4, 1, 64, seed=2009),
         Workload("partial_page_prefix", 9, 250, (10, 30), (1, 2), 4, 2, 128, seed=2010),
         Workload("one_page_suffix", 12, 512, (1, 1), (1, 1), 8, 8, 128, seed=2011),
+        # second shared level: groups of consecutive requests share a document
+        Workload("nested_decode", 12, 256, (1, 40), (1, 1), 8, 2, 128, seed=2012,
+                 groups=((4, 512), (3, 300), (2, 1000))),
+        Workload("nested_prefill", 10, 256, (5, 60), (1, 12), 8, 2, 128, seed=2013,
+                 groups=((3, 400), (4, 640))),
+        Workload("nested_d64", 9, 256, (1, 30), (1, 3), 16, 4, 64, seed=2014,
+                 groups=((5, 300), (2, 700))),
+        Workload("nested_all_grouped", 8, 256, (1, 20), (1, 1), 8, 2, 128, seed=2015,
+                 groups=((4, 512), (4, 512))),
+        # request 1 has computed only 601 tokens: the group's share is capped (896 -> 592)
+        Workload("nested_capped", 8, 256, (10, 30), (1, 4), 8, 2, 128, seed=2016,
+                 groups=((4, 640),), override=((1, 901, 300),)),
     ]
 }
 
@@ -50,7 +62,10 @@ def test_small_full_parity(name, mode):
     ref_o, ref_l = oracle_ref(b)
     out, lse, info = run(DeviceBatch(b), mode=mode)
     log(f"  plan: cascade={info['use_cascade']} P_c={info['common_prefix_len']} "
-        f"psplit={info['prefix_splits']} schunks={info['suffix_chunks']}")
+        f"psplit={info['prefix_splits']} groups={info['num_level1_groups']}x{info['level1_splits']} "
+        f"schunks={info['suffix_chunks']}")
+    if mode == "on" and SMALL[name].groups:
+        assert info["num_level1_groups"] > 0
     assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}")
 
 
@@ -116,7 +131,7 @@ def test_full_size_sampled_parity(name):
 
 
 SEPARATE = ["tiny_decode", "prefill_mix", "prefill_capped", "gqa8_outliers", "many_rows", "d64_gqa",
-            "worked_decode", "mixed_prefill", "self_consistency"]
+            "nested_decode", "nested_prefill", "worked_decode", "mixed_prefill", "self_consistency", "multi_doc"]
 
 
 @pytest.mark.parametrize("name", SEPARATE)
@@ -135,3 +150,29 @@ def test_separate_phase_launches_match_fused(name):
     if name in SMALL:
         ref_o, ref_l = oracle_ref(db.b)
         assert_close(so, sl, ref_o, ref_l, what=f"{name}/separate")
+
+
+@pytest.mark.parametrize("name", ["nested_decode", "nested_prefill", "nested_capped", "multi_doc"])
+def test_second_level_against_single_level(name):
+    """The same batch with the second shared level and with the batch-wide
+    prefix only: both match the oracle (they split the keys differently, so
+    they are not bitwise equal) and agree with each other within the bar."""
+    log(f"[levels] {name}")
+    w = SMALL[name] if name in SMALL else workloads.get(name)
+    b = workloads.make_batch(w)
+    db = DeviceBatch(b)
+    o2, l2, i2 = run(db, mode="on")
+    o1, l1, i1 = run(db, mode="on", max_levels=1)
+    assert i2["num_level1_groups"] > 0 and i1["num_level1_groups"] == 0
+    log(f"  groups {i2['num_level1_groups']} x {i2['level1_splits']} splits; slots {i2['num_partial_slots']} "
+        f"vs {i1['num_partial_slots']}")
+    if name in SMALL:
+        ref_o, ref_l = oracle_ref(b)
+        rows = None
+    else:
+        reqs = _sample_requests(w.num_reqs, w.seed)
+        ref_o, ref_l = oracle_ref(b, requests=reqs)
+        rows = rows_of(b, reqs)
+    assert_close(o2, l2, ref_o, ref_l, rows=rows, what=f"{name}/two-level")
+    assert_close(o1, l1, ref_o, ref_l, rows=rows, what=f"{name}/one-level")
+    assert np.all(np.abs(o2 - o1) <= 2e-2 + 1e-2 * np.abs(o1)) and np.abs(l2 - l1).max() <= 1e-3

@@ -22,6 +22,12 @@ behind one shared system prompt or document, each with its own continuation):
 * block-table padding columns hold random *valid* page ids;
 * Q, K, V ~ N(0, 1) in fp32, optionally with a Bernoulli outlier mask scaled
   by a factor, then rounded to bf16.
+
+Nested sharing (``groups``): consecutive runs of requests additionally share
+a document of L_g tokens after the batch-wide prefix (system prompt ->
+document -> own tokens). Members get ``seq_len = P + L_g + S_r``; the
+document's full pages are physically shared by the members and a partial
+last document page is copied into each member's own first page.
 """
 
 from __future__ import annotations
@@ -50,6 +56,9 @@ class Workload:
     # request index -> (seq_len, q_len), applied after the random draws
     override: Tuple[Tuple[int, int, int], ...] = ()
     extra_stride: int = 1            # padding columns in the block table
+    # (members, shared tokens): runs of consecutive requests from request 0
+    # that share a document after the prefix; remaining requests share none
+    groups: Tuple[Tuple[int, int], ...] = ()
 
     @property
     def softmax_scale(self) -> float:
@@ -64,6 +73,8 @@ def _w(name, n, p, s, q, hq, hkv, d, seed, **kw) -> Workload:
 # The five workloads: tiny decode; the pages' worked example (N=64, P=4096,
 # S=128); mixed chunked prefill; many-sample self-consistency decode; long
 # shared document (+ at the 8-request threshold, + with a 255-token prefix).
+# Then two batches with nested sharing (system prompt -> document ->
+# request): decode and chunked prefill, some requests in no group.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in [
         _w("tiny_decode", 8, 256, (16, 16), (1, 1), 4, 4, 64, 1000),
@@ -78,6 +89,10 @@ WORKLOADS: Dict[str, Workload] = {
         _w("long_doc", 16, 32768, (256, 256), (1, 1), 32, 8, 128, 1004),
         _w("long_doc_n8", 8, 32768, (256, 256), (1, 1), 32, 8, 128, 1014),
         _w("long_doc_p255", 16, 255, (256, 256), (1, 1), 32, 8, 128, 1024),
+        _w("multi_doc", 32, 1024, (32, 160), (1, 1), 32, 8, 128, 1005,
+           groups=((8, 2048), (8, 2048), (6, 3072), (6, 1000))),
+        _w("multi_doc_prefill", 24, 512, (32, 200), (1, 24), 32, 8, 128, 1006,
+           groups=((6, 1024), (6, 768), (4, 2000))),
     ]
 }
 
@@ -119,7 +134,16 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
     suffix = torch.randint(s_lo, s_hi + 1, (n,), generator=gen)
     qlen = torch.randint(q_lo, q_hi + 1, (n,), generator=gen)
     qlen = torch.minimum(qlen, suffix)
-    seq = suffix + w.prefix
+    grp_of = [-1] * n
+    r = 0
+    for gi, (members, _) in enumerate(w.groups):
+        for _ in range(members):
+            grp_of[r] = gi
+            r += 1
+    assert r <= n and (not w.groups or w.prefix % ps == 0)
+    grp_len = [g[1] for g in w.groups]
+    doc = torch.tensor([grp_len[g] if g >= 0 else 0 for g in grp_of], dtype=suffix.dtype)
+    seq = suffix + w.prefix + doc
     for r, sl, ql in w.override:
         seq[r] = sl
         qlen[r] = ql
@@ -127,13 +151,19 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
     q_l = [int(x) for x in qlen]
 
     shared_pages = w.prefix // ps
-    own_pages = [-(-s // ps) - shared_pages for s in seq_l]
-    used = shared_pages + sum(own_pages)
+    grp_pages = [L // ps for L in grp_len]            # full document pages, shared by the members
+    lead = [shared_pages + (grp_pages[g] if g >= 0 else 0) for g in grp_of]   # shared columns of each row
+    own_pages = [-(-s // ps) - lead[r] for r, s in enumerate(seq_l)]
+    used = shared_pages + sum(grp_pages) + sum(own_pages)
     num_pages = used + max(1, int(math.ceil(0.05 * used)))
     perm = torch.randperm(num_pages, generator=gen)
     shared_ids = perm[:shared_pages]
-    own_ids = []
     pos = shared_pages
+    grp_ids = []
+    for k in grp_pages:
+        grp_ids.append(perm[pos:pos + k])
+        pos += k
+    own_ids = []
     for k in own_pages:
         own_ids.append(perm[pos:pos + k])
         pos += k
@@ -142,7 +172,9 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
     block_table = torch.randint(0, num_pages, (n, stride), generator=gen, dtype=torch.int64)
     for r in range(n):
         block_table[r, :shared_pages] = shared_ids
-        block_table[r, shared_pages:shared_pages + own_pages[r]] = own_ids[r]
+        if grp_of[r] >= 0:
+            block_table[r, shared_pages:lead[r]] = grp_ids[grp_of[r]]
+        block_table[r, lead[r]:lead[r] + own_pages[r]] = own_ids[r]
 
     nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
     caches = []
@@ -151,8 +183,14 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
         prefix_vals = _randn((w.prefix, hkv, d), gen, w.outlier_frac, w.outlier_scale)
         if shared_pages:
             cache[shared_ids] = prefix_vals[:shared_pages * ps].reshape(shared_pages, ps, hkv, d)
+        doc_vals = []
+        for g, L in enumerate(grp_len):
+            vals = _randn((L, hkv, d), gen, w.outlier_frac, w.outlier_scale)
+            if grp_pages[g]:
+                cache[grp_ids[g]] = vals[:grp_pages[g] * ps].reshape(grp_pages[g], ps, hkv, d)
+            doc_vals.append(vals)
         for r in range(n):
-            start = shared_pages * ps
+            start = lead[r] * ps
             n_tok = seq_l[r] - start
             if n_tok <= 0:
                 continue
@@ -161,6 +199,10 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
             in_prefix = t < w.prefix
             if bool(in_prefix.any()):
                 own_vals[in_prefix] = prefix_vals[t[in_prefix]]
+            if grp_of[r] >= 0:   # the partial last page of the document
+                in_doc = (t >= w.prefix) & (t < w.prefix + grp_len[grp_of[r]])
+                if bool(in_doc.any()):
+                    own_vals[in_doc] = doc_vals[grp_of[r]][t[in_doc] - w.prefix]
             pages = own_ids[r][(t - start) // ps]
             cache[pages, t % ps] = own_vals
         caches.append(cache)
