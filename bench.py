@@ -285,11 +285,20 @@ def main():
         ms_sep = time_steps(step_sep, max(10, args.steps // 2), rotate)
         spa.cascade_attn_profile_enable(False)
         prof_sep = spa.cascade_attn_profile_read()
-        suffix_visible = visible - plen * T
+        # second shared level: each group's extra positions once, its queries
+        groups = spa.cascade_attn_plan_groups(plan_sep)
+        qsl_l = b.query_start_loc.tolist()
+        g_tokens = sum(length - plen for _, _, length in groups)
+        g_q = sum(qsl_l[e] - qsl_l[a] for a, e, _ in groups)
+        g_flops = sum(4.0 * (qsl_l[e] - qsl_l[a]) * w.num_q_heads * (length - plen) * w.head_dim
+                      for a, e, length in groups)
+        suffix_visible = visible - plen * T - sum((qsl_l[e] - qsl_l[a]) * (length - plen) for a, e, length in groups)
         ph_work = {"prefix": (plen * bpt + q_bytes, 4.0 * T * w.num_q_heads * plen * w.head_dim),
-                   "suffix": ((kv_tokens - plen) * bpt + q_bytes, 4.0 * w.num_q_heads * w.head_dim * suffix_visible)}
+                   "level1": (g_tokens * bpt + g_q * w.num_q_heads * w.head_dim * 2, g_flops),
+                   "suffix": ((kv_tokens - plen - g_tokens) * bpt + q_bytes,
+                              4.0 * w.num_q_heads * w.head_dim * suffix_visible)}
         phases = {"us_per_step": round(ms_sep * 1e3, 3)}
-        for kind in ("prefix", "suffix", "merge"):
+        for kind in ("prefix", "level1", "suffix", "merge"):
             tot_ms, cnt = prof_sep[kind]
             if not cnt:
                 continue
