@@ -102,7 +102,12 @@ def cpu_baseline(b, kv_bytes, budget_s=15.0, max_runs=60):
     over the whole batch, repeated for about budget_s seconds."""
     import oracle
     from threadpoolctl import threadpool_limits
-    kc, vc = b.k_cache.float().numpy(), b.v_cache.float().numpy()
+    w = b.workload
+    if w.kv_dtype == "fp8":   # the oracle decodes the e4m3 codes itself
+        kc = oracle.fp8_e4m3_decode(b.k_cache.numpy()) * w.k_scale
+        vc = oracle.fp8_e4m3_decode(b.v_cache.numpy()) * w.v_scale
+    else:
+        kc, vc = b.k_cache.float().numpy(), b.v_cache.float().numpy()
     args = (b.q.float().numpy(), kc, vc, b.block_table.numpy(), b.query_start_loc.numpy(),
             b.seq_lens.numpy(), b.workload.page_size)
     times = []
@@ -180,13 +185,13 @@ def main():
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
     b = workloads.make_batch(w)
-    bpt = 2 * w.num_kv_heads * w.head_dim * 2
+    bpt = 2 * w.num_kv_heads * w.head_dim * (1 if w.kv_dtype == "fp8" else 2)   # K+V bytes per token
 
     def make_plan(mode, **kw):
         return spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                               k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
                               seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode,
-                              max_levels=args.max_levels, **kw)
+                              max_levels=args.max_levels, k_scale=w.k_scale, v_scale=w.v_scale, **kw)
 
     plan = make_plan(args.mode)
     info = plan.info
@@ -337,6 +342,7 @@ def main():
         "config": {"workload": args.workload, "num_reqs": w.num_reqs, "prefix": w.prefix,
                    "suffix": list(w.suffix), "q_len": list(w.q_len), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "kv_dtype": w.kv_dtype,
                    "mode": args.mode, "use_cascade": int(casc), "common_prefix_len": plen,
                    "kv_bytes_per_step": kv_bytes, "rotating_copies": rotate},
         "roofline": roof,

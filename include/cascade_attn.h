@@ -23,8 +23,8 @@
  * Conventions for every entry point:
  *   - Plain C, no allocation visible to the caller other than the plan
  *     handle; the caller owns every tensor (device memory from any allocator).
- *   - Dtypes: Q, K/V cache and output are bf16; LSE and workspace fp32;
- *     metadata int32.
+ *   - Dtypes: Q and output are bf16; the K/V caches bf16 or fp8 e4m3
+ *     (ca_kv_dtype_t); LSE and workspace fp32; metadata int32.
  *   - seq_lens[r] counts all KV positions of request r including this
  *     step's q_len_r query tokens, which are its last q_len_r positions;
  *     num_computed_tokens[r] = seq_lens[r] - q_len_r.
@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
   CA_OK = 0,
   CA_EINVAL = 1,        /* null pointer, bad handle, bad size argument */
-  CA_EUNSUPPORTED = 2,  /* head_dim not 64/128, page_size not 16, Hq % Hkv != 0 */
+  CA_EUNSUPPORTED = 2,  /* head_dim not 64/128 (fp8: not 128), page_size not 16, Hq % Hkv != 0 */
   CA_EMETA = 3,         /* inconsistent batch metadata (lengths, page ids, strides) */
   CA_EWORKSPACE = 4,    /* workspace smaller than the plan requires */
   CA_EHIP = 5           /* a HIP runtime call or kernel launch failed */
@@ -65,6 +65,14 @@ typedef enum {
   CA_MODE_FORCE_OFF = 2   /* always the non-cascade path */
 } ca_mode_t;
 
+/* Element type of the paged K/V caches. FlashInfer's cascade path was turned
+ * off for FP8 caches ([p2] section 6); here both run every phase. */
+typedef enum {
+  CA_KV_BF16 = 0,        /* bf16 */
+  CA_KV_FP8_E4M3 = 1     /* fp8 e4m3 (OCP: bias 7, max 448, NaN 0x7f / 0xff, no infinity), one byte per
+                            element, dequantised as value * k_scale (K) and value * v_scale (V); head_dim 128 */
+} ca_kv_dtype_t;
+
 typedef struct {
   int32_t num_reqs;            /* N >= 1 */
   int32_t num_q_heads;         /* Hq */
@@ -76,11 +84,12 @@ typedef struct {
   int32_t separate_phases;     /* cascade path only: 0 = prefix and suffix work-groups share one
                                   launch; 1 = two launches (prefix, then suffix) doing the same
                                   work with identical results, e.g. to time each phase */
-  /* K/V cache element strides (bf16 elements). The cache is indexed
+  /* K/V cache element strides (elements of kv_dtype). The cache is indexed
    * [page][slot][kv_head][d] with d contiguous; NHD layout
    * [num_pages, page_size, Hkv, d] has (page_size*Hkv*d, Hkv*d, d), HND
    * layout [num_pages, Hkv, page_size, d] has (Hkv*page_size*d, d, page_size*d).
-   * All three must be multiples of 8 (16-byte aligned rows), and
+   * All three must be multiples of 8 for bf16 and of 16 for fp8 (16-byte
+   * aligned rows), and
    * kv_stride_token at most 2^26 (byte offsets within one page fit 32 bits). */
   int64_t kv_stride_page;
   int64_t kv_stride_token;
@@ -94,6 +103,9 @@ typedef struct {
   int32_t max_levels;          /* shared levels of the cascade path: 0 = planner default (2);
                                   1 = the batch-wide prefix only; 2 = also groups of consecutive
                                   requests sharing more pages (see cascade_attn_plan_groups) */
+  int32_t kv_dtype;            /* ca_kv_dtype_t */
+  float k_scale;               /* fp8: K dequantisation factor (<= 0 selects 1); ignored for bf16 */
+  float v_scale;               /* fp8: V dequantisation factor (<= 0 selects 1); ignored for bf16 */
 } ca_params_t;
 
 typedef struct {
@@ -114,7 +126,7 @@ typedef struct {
   int32_t separate_phases;             /* 1 if the cascade phases run as separate launches */
   int32_t num_level1_groups;           /* request groups of the second shared level (0 = none) */
   int32_t level1_splits;               /* KV splits of every group (partial slots of that level) */
-  int32_t reserved0;
+  int32_t kv_dtype;                    /* ca_kv_dtype_t of the plan */
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
   int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */
@@ -194,7 +206,7 @@ ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* 
  * no host-to-device copy; inputs must stay alive until the stream passes
  * this call.
  *   q                [T][num_q_heads][head_dim] bf16, contiguous
- *   k_cache, v_cache paged bf16 caches with the plan's strides
+ *   k_cache, v_cache paged caches of the plan's kv_dtype and strides
  *   block_table_d, query_start_loc_d, seq_lens_d: device copies of the
  *                    same metadata given to cascade_attn_plan
  *   out              [T][num_q_heads][head_dim] bf16 (written)

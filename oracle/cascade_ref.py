@@ -261,3 +261,23 @@ def kv_tokens_multilevel(level0_len, groups, seq_lens):
         for r in range(a, b):
             start[r] = int(length)
     return int(level0_len) + extra + int(sum(int(s) - st for s, st in zip(seq_lens, start)))
+
+
+def fp8_e4m3_decode(codes):
+    """Values of fp8 e4m3 codes (uint8) as float64.
+
+    The format of the OCP 8-bit floating-point specification, E4M3 variant:
+    1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+    encodes subnormals 2^-6 * m/8; the all-ones pattern S.1111.111 is NaN and
+    there is no infinity, so the largest value is 2^8 * 1.75 = 448. The pages
+    name FP8 KV caches only as a feature FlashInfer's cascade lacked ([p2]
+    section 6); the caches here are dequantised as code value * scale.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = sign * np.ldexp(m / 8.0, -6)
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((c & 7) == 7), np.nan, out)

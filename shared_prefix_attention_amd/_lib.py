@@ -18,6 +18,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "cascade_attn.h")
 
 CA_OK, CA_EINVAL, CA_EUNSUPPORTED, CA_EMETA, CA_EWORKSPACE, CA_EHIP = range(6)
 MODE_AUTO, MODE_FORCE_ON, MODE_FORCE_OFF = 0, 1, 2
+KV_BF16, KV_FP8_E4M3 = 0, 1
+_KV_DTYPES = {"bf16": KV_BF16, "fp8": KV_FP8_E4M3, "fp8_e4m3": KV_FP8_E4M3}
 _MODES = {"auto": MODE_AUTO, "on": MODE_FORCE_ON, "off": MODE_FORCE_OFF}
 KERNEL_KINDS = ("cascade_phases", "attention", "merge", "decode", "prefix", "suffix", "level1")
 
@@ -46,6 +48,9 @@ class ca_params_t(ctypes.Structure):
         ("num_cus", ctypes.c_int32),
         ("heads_per_item", ctypes.c_int32),
         ("max_levels", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -68,7 +73,7 @@ class ca_plan_info_t(ctypes.Structure):
         ("separate_phases", ctypes.c_int32),
         ("num_level1_groups", ctypes.c_int32),
         ("level1_splits", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("kv_tokens_cascade", ctypes.c_int64),
@@ -182,7 +187,7 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
                       num_pages: int, kv_strides, block_table, query_start_loc, seq_lens,
                       num_computed_tokens=None, softmax_scale: float = 0.0, mode="auto",
                       num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
-                      max_levels: int = 0) -> Plan:
+                      max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0) -> Plan:
     """Host-only planner (see cascade_attn_plan in the header).
 
     kv_strides: (page, token-slot, head) element strides of the K/V caches.
@@ -212,6 +217,9 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
     prm.heads_per_item = int(heads_per_item)
     prm.separate_phases = int(separate_phases)
     prm.max_levels = int(max_levels)
+    prm.kv_dtype = _KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    prm.k_scale = float(k_scale)
+    prm.v_scale = float(v_scale)
     h = ctypes.c_void_p(0)
     _check(load().cascade_attn_plan(ctypes.byref(prm), bt_p, qsl_p, sl_p, nc_p, ctypes.byref(h)))
     return Plan(h.value)

@@ -75,6 +75,7 @@ struct TileArgs {
   int32_t direct;               // write the final output (no partial)
   int32_t lvl1_slot_base;       // per-request phase: first partial slot of the group level
   int32_t lvl1_slots;           //   and its slot count (rows of requests in no group get -inf there)
+  float v_scale;                // dequantisation factor of V (1 for bf16 caches)
 };
 
 // Second shared level: request groups [req_begin, req_end) whose members
@@ -106,9 +107,10 @@ __device__ __forceinline__ int group_of_request(const GroupTable& gt, int req) {
 
 constexpr int kMaxItemPages = 512;
 
-template <int D, int NS, int SK>
+// ESZ: bytes per cache element, 2 (bf16) or 1 (fp8).
+template <int D, int NS, int SK, int ESZ = 2>
 struct TileSmem {
-  static constexpr int TILE_BYTES = SK * D * 2;            // one of K or V, one stage
+  static constexpr int TILE_BYTES = SK * D * ESZ;          // one of K or V, one stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int BYTES = NS * STAGE_BYTES + kMaxItemPages * 4;
 };
@@ -125,6 +127,34 @@ __device__ __forceinline__ int chunk_swz(int key) {
 template <int D>
 __device__ __forceinline__ int chunk_swz_v(int key) {
   return D == 128 ? ((2 * key) & 15) : ((key >> 1) & 7);
+}
+
+// fp8 caches (head_dim 128: key rows of 128 bytes, 8 chunks of 16 bytes).
+// K is read one 16-byte chunk column across 16 consecutive keys; XOR with key
+// mod 8, bit 0 flipped for keys 8..15, puts those reads in 16 distinct (row
+// parity, chunk) bank groups of a 256-byte LDS cycle. V is read with the
+// 8-bit transpose load, 8 key rows x 2 halves per 16-lane group (see
+// read_v8 in attn_item); bits 1, 2 and 4 of the key pick the XOR so that a
+// group's 16 reads are distinct and the two groups of a cycle complementary.
+__device__ __forceinline__ int chunk_swz_k8(int key) { return (key & 7) ^ ((key >> 3) & 1); }
+__device__ __forceinline__ int chunk_swz_v8(int key) {
+  return ((key >> 1) & 1) | ((((key >> 4) ^ (key >> 2)) & 1) << 1) | (((key >> 2) & 1) << 2);
+}
+
+// Eight fp8 (OCP e4m3) values, bytes 0..7 of (w0, w1), as eight bf16 in
+// element order. v_cvt_pk_f32_fp8 decodes two bytes exactly (every e4m3
+// value, subnormals included, is a bf16 value too), so the bf16 rounding is
+// exact as well.
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                 pack_bf16x2(d[0], d[1])};
+}
+// Four fp8 values (bytes 0..3 of w) as four bf16.
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1])};
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes
@@ -179,6 +209,18 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
   return r;
 }
 
+// ds_read_b64_tr_b8: within each 16-lane group, lane 2*j + c supplies the
+// address of row j, bytes [8c, 8c+8) of an 8 x 16 block of bytes; lane i
+// receives column i of the eight rows (byte j = row j). Measured on the
+// device with an in-bounds probe.
+template <int OFF = 0>
+__device__ __forceinline__ u32x2_t lds_read_tr8(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
 // Pins a value in program order: code that produces it stays above, code
 // that consumes it stays below (inline asm statements keep their order).
 template <typename T>
@@ -216,14 +258,15 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
 
 // MH: the item may cover several consecutive KV heads of one request (same
 // pages and key range), run as one continuous stage pipeline.
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH>
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const int bid, uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
   constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
   constexpr int KC = D / 32;              // 32-wide d chunks per QK^T MFMA chain
   constexpr int DB = D / 16;              // 16-wide d blocks of the output
-  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  constexpr int ESZ = F8 ? 1 : 2;         // bytes per cache element
+  constexpr int CPR = D * ESZ / 16;       // 16-byte chunks per K/V row
   constexpr int KPB = 64 / CPR;           // keys per 1 KB DMA block
   constexpr int BLK = SK / KPB;           // 1 KB DMA blocks per tile (K or V)
   static_assert(BLK % W == 0, "DMA blocks must divide among the waves");
@@ -231,11 +274,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   constexpr int OPS = 2 * BLK_PER_WAVE;   // vector-memory ops per wave per stage
   constexpr int NKB = SK / 16 / KG;       // 16-key blocks per wave per stage
   static_assert((NKB == 1 || NKB == 2 || NKB == 4) && SK % (16 * KG) == 0, "each wave needs 1, 2 or 4 16-key blocks");
-  constexpr int ROWB = D * 2;             // LDS bytes per key row
+  constexpr int ROWB = D * ESZ;           // LDS bytes per key row
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
-  using SM = TileSmem<D, NS, SK>;
-  // the key-group states are combined in the stage buffer just consumed
-  static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= SM::STAGE_BYTES, "merge scratch");
+  using SM = TileSmem<D, NS, SK, ESZ>;
+  // The key-group states are combined in the stage buffer just consumed
+  // (bf16); fp8 stages are too small for that, so fp8 items run one head
+  // and combine at the item's end, when no DMA is in flight, from LDS 0.
+  static_assert(!F8 || (D == 128 && !MH), "fp8 caches: head_dim 128, one head per item");
+  static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= (F8 ? NS : 1) * SM::STAGE_BYTES, "merge scratch");
   int32_t* s_pages = reinterpret_cast<int32_t*>(smem + NS * SM::STAGE_BYTES);
 
   const int tid = threadIdx.x;
@@ -371,7 +417,10 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         if (row_ok[rb]) {
-          q[rb][kc] = load16(a.q + ((int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb]) * D + kc * 32 + lq * 8);
+          // k-slot (lq, j) of chunk kc is d = kc*32 + 8*lq + j (bf16), or,
+          // matching the fp8 K fragments, d = 16*(lq + 4*(kc/2)) + 8*(kc%2) + j
+          const int d0 = F8 ? 16 * (lq + 4 * (kc >> 1)) + 8 * (kc & 1) : kc * 32 + lq * 8;
+          q[rb][kc] = load16(a.q + ((int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb]) * D + d0);
         } else {
           q[rb][kc] = u32x4_t{0u, 0u, 0u, 0u};
         }
@@ -398,15 +447,39 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   // Lane-constant parts of the LDS operand addresses (the XOR swizzle
   // depends on key mod 16 only, so 16-key blocks differ by a constant).
   const uint32_t smem_base = lds_addr(smem);
+  auto swz_k = [](int key) { return F8 ? chunk_swz_k8(key) : chunk_swz<D>(key); };
+  auto swz_v = [](int key) { return F8 ? chunk_swz_v8(key) : chunk_swz_v<D>(key); };
   uint32_t k_off[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * ROWB + (((kc * 4 + lq) ^ chunk_swz<D>(lr)) * 16);
-  const int tr_row = 4 * lq + (lr >> 2);   // key within a 16-key block for the transpose read
   uint32_t v_off[DB];
+  if constexpr (!F8) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int d0 = db * 16 + 4 * (lr & 3);
-    v_off[db] = tr_row * ROWB + (((d0 >> 3) ^ chunk_swz_v<D>(tr_row)) * 16) + (d0 & 7) * 2;
+    for (int kc = 0; kc < KC; ++kc) k_off[kc] = lr * ROWB + (((kc * 4 + lq) ^ swz_k(lr)) * 16);
+    const int tr_row = 4 * lq + (lr >> 2);   // key within a 16-key block for the transpose read
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 16 + 4 * (lr & 3);
+      v_off[db] = tr_row * ROWB + (((d0 >> 3) ^ swz_v(tr_row)) * 16) + (d0 & 7) * 2;
+    }
+  } else {
+    // K: lane (lr, lq) reads chunks lq and lq + 4 (d = 16*chunk ..) of key lr
+#pragma unroll
+    for (int p = 0; p < KC / 2; ++p) k_off[p] = lr * ROWB + (((lq + 4 * p) ^ swz_k(lr)) * 16);
+    // V, 8-bit transpose read: lane 2j + c of group lq supplies row j, half
+    // c of a 16-byte d block. 32-key MFMA: row j is key (j < 4 ? 4*lq + j :
+    // 16 + 4*lq + j - 4) of a 32-key group (the S^T accumulators' k-slot
+    // map). 16-key MFMA: row j is key 4*lq + j%4 at d block m + 4*(j/4), so
+    // one read gives d blocks m and m + 4.
+    const int j = lr >> 1, c = lr & 1;
+    if constexpr (NKB >= 2) {
+      const int key = j < 4 ? 4 * lq + j : 16 + 4 * lq + j - 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) v_off[db] = key * ROWB + ((db ^ swz_v(key)) * 16) + 8 * c;
+    } else {
+      const int key = 4 * lq + (j & 3);
+#pragma unroll
+      for (int m = 0; m < DB / 2; ++m)
+        v_off[m] = key * ROWB + (((m + 4 * (j >> 2)) ^ swz_v(kg * 16 + key)) * 16) + 8 * c;
+    }
   }
 
   // ---------------------------------------------------- K/V DMA sources
@@ -440,15 +513,15 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 #pragma unroll
   for (int i = 0; i < BLK_PER_WAVE; ++i) {
     const int key = wave * KPW + i * KPB + lane / CPR;          // key within the stage
-    dma_koff[i] = (uint32_t)(((key & 15) * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
-    dma_voff[i] = (uint32_t)(((key & 15) * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
+    dma_koff[i] = (uint32_t)((key & 15) * a.st * ESZ + (col ^ swz_k(key)) * 16);
+    dma_voff[i] = (uint32_t)((key & 15) * a.st * ESZ + (col ^ swz_v(key)) * 16);
   }
   // Stage u of the item is tile t of head h (u = h * n_tiles + t); stages are
   // issued in order, so the issue position advances one (h, t) at a time.
   int iss_u = 0, iss_h = 0, iss_t = 0;
   auto issue_next = [&]() {
     const int t = iss_t;
-    const int64_t head_bytes = (int64_t)(g0 + iss_h) * a.sh * 2;
+    const int64_t head_bytes = (int64_t)(g0 + iss_h) * a.sh * ESZ;
     const uint32_t lds_k = smem_base + (iss_u % NS) * SM::STAGE_BYTES + wave * BLK_PER_WAVE * 1024;
     const uint32_t lds_v = lds_k + SM::TILE_BYTES;
     const int kt0 = key_begin + t * SK;
@@ -456,7 +529,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     // positions past the item re-read its last position, which lies in this
     // wave's page or, if the whole range is past it, in last_pid
     const int pid = wpos < key_end ? stage_pid(t) : last_pid;
-    const int64_t pg = (int64_t)pid * a.sp * 2 + head_bytes;
+    const int64_t pg = (int64_t)pid * a.sp * ESZ + head_bytes;
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + pg;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + pg;
     if (wpos + KPW <= key_end) {
@@ -481,8 +554,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       for (int i = 0; i < BLK_PER_WAVE; ++i) {
         const int key = wave * KPW + i * KPB + lane / CPR;
         const int slot_t = min(kt0 + key, key_end - 1) & 15;
-        const uint32_t ko = (uint32_t)((slot_t * a.st + (col ^ chunk_swz<D>(key)) * 8) * 2);
-        const uint32_t vo = (uint32_t)((slot_t * a.st + (col ^ chunk_swz_v<D>(key)) * 8) * 2);
+        const uint32_t ko = (uint32_t)(slot_t * a.st * ESZ + (col ^ swz_k(key)) * 16);
+        const uint32_t vo = (uint32_t)(slot_t * a.st * ESZ + (col ^ swz_v(key)) * 16);
         lds_dma16(kb + ko, lds_k + i * 1024);
         lds_dma16(vb + vo, lds_v + i * 1024);
       }
@@ -514,7 +587,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   auto finish_head = [&](int g, int buf) {
     if constexpr (KG > 1) {
       constexpr int SLOT_F = 16 * RB * XS_ROW;   // floats per published wave state
-      float* xs = reinterpret_cast<float*>(smem + buf * SM::STAGE_BYTES);
+      float* xs = reinterpret_cast<float*>(smem + (F8 ? 0 : buf * SM::STAGE_BYTES));
       block_barrier();                           // every wave is done with this buffer
       if (kg > 0 && wave_active) {
         float* my = xs + ((kg - 1) * RW + rw) * SLOT_F;
@@ -561,7 +634,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     for (int rb = 0; rb < RB; ++rb) {
       const float l_tot = wave_sum_across_quads(l_run[rb]);
       const bool live = l_tot > 0.f;
-      const float inv = live ? 1.f / l_tot : 0.f;
+      const float inv = live ? a.v_scale / l_tot : 0.f;
       const float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
       if (!row_ok[rb]) continue;
       const int64_t row = (int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb];
@@ -607,11 +680,30 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       // S^T = K Q^T for NKB blocks of 16 keys. All K fragments of the stage
       // are read before one wait; the MFMA chains of the blocks interleave.
       u32x4_t kf[NKB * KC];
+      if constexpr (!F8) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) kf[kb * KC + kc] = lds_read_b128_kb<ROWB>(sK + k_off[kc], kb);
-      lds_wait_regs(kf);
+          for (int kc = 0; kc < KC; ++kc) kf[kb * KC + kc] = lds_read_b128_kb<ROWB>(sK + k_off[kc], kb);
+        lds_wait_regs(kf);
+      } else {
+        // 16 fp8 of chunk lq + 4p are k-slots of chunks kc = 2p (bytes 0-7)
+        // and 2p + 1 (bytes 8-15), the order load_q gives Q
+        u32x4_t kr[NKB * KC / 2];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int p = 0; p < KC / 2; ++p) kr[kb * (KC / 2) + p] = lds_read_b128_kb<ROWB>(sK + k_off[p], kb);
+        lds_wait_regs(kr);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int p = 0; p < KC / 2; ++p) {
+            const u32x4_t r = kr[kb * (KC / 2) + p];
+            kf[kb * KC + 2 * p] = fp8x8_to_bf16(r[0], r[1]);
+            kf[kb * KC + 2 * p + 1] = fp8x8_to_bf16(r[2], r[3]);
+          }
+      }
       f32x4_t s[NKB][RB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -635,21 +727,43 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       constexpr int DBV = DB / VH;                          // d blocks per half
       u32x4_t vf[NKB >= 2 ? DBV * NKK : 1];
       u32x2_t vh[NKB == 1 ? DB : 1];
+      // fp8: raw transpose reads (8 keys of one d column per lane), converted
+      // after the softmax
+      u32x2_t vr8[F8 && NKB >= 2 ? DBV * NKK : 1];
+      u32x2_t vr1[F8 && NKB == 1 ? DB / 2 : 1];
       auto read_v = [&](int half) {
 #pragma unroll
         for (int i = 0; i < DBV; ++i) {
           const uint32_t va = sV + v_off[half * DBV + i];
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
-            const u32x2_t h0 = kk == 0 ? lds_read_tr16<0>(va) : lds_read_tr16<32 * ROWB>(va);
-            const u32x2_t h1 = kk == 0 ? lds_read_tr16<16 * ROWB>(va) : lds_read_tr16<48 * ROWB>(va);
-            vf[i * NKK + kk] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+            if constexpr (F8) {
+              vr8[i * NKK + kk] = kk == 0 ? lds_read_tr8<0>(va) : lds_read_tr8<32 * ROWB>(va);
+            } else {
+              const u32x2_t h0 = kk == 0 ? lds_read_tr16<0>(va) : lds_read_tr16<32 * ROWB>(va);
+              const u32x2_t h1 = kk == 0 ? lds_read_tr16<16 * ROWB>(va) : lds_read_tr16<48 * ROWB>(va);
+              vf[i * NKK + kk] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+            }
           }
         }
       };
-      if constexpr (NKB == 1) {
+      auto wait_v = [&]() {
+        if constexpr (F8) {
+          lds_wait_regs(vr8);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vh[db] = lds_read_tr16(sV + v_off[db]);
+          for (int i = 0; i < DBV * NKK; ++i) vf[i] = fp8x8_to_bf16(vr8[i][0], vr8[i][1]);
+        } else {
+          lds_wait_regs(vf);
+        }
+      };
+      if constexpr (NKB == 1) {
+        if constexpr (F8) {
+#pragma unroll
+          for (int m = 0; m < DB / 2; ++m) vr1[m] = lds_read_tr8(sV + v_off[m]);
+        } else {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) vh[db] = lds_read_tr16(sV + v_off[db]);
+        }
       } else {
         read_v(0);
       }
@@ -701,7 +815,16 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       for (int rb = 0; rb < RB; ++rb) reg_fence(pb[rb]);   // softmax done before the V wait
       // O^T += V^T P^T
       if constexpr (NKB == 1) {
-        lds_wait_regs(vh);
+        if constexpr (F8) {
+          lds_wait_regs(vr1);
+#pragma unroll
+          for (int m = 0; m < DB / 2; ++m) {
+            vh[m] = fp8x4_to_bf16(vr1[m][0]);
+            vh[m + DB / 2] = fp8x4_to_bf16(vr1[m][1]);
+          }
+        } else {
+          lds_wait_regs(vh);
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -710,7 +833,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 #pragma unroll
         for (int half = 0; half < VH; ++half) {
           if (half > 0) read_v(half);
-          lds_wait_regs(vf);
+          wait_v();
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -746,10 +869,10 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   }
 }
 
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH>
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
 __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK>::BYTES];
-  attn_item<D, RB, RW, KG, NS, SK, MH>(a, gt, blockIdx.x, smem);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
+  attn_item<D, RB, RW, KG, NS, SK, MH, F8>(a, gt, blockIdx.x, smem);
 }
 
 // One launch for all cascade phases: work-groups [0, n_prefix) run prefix
@@ -758,17 +881,18 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
 // bandwidth-heavy suffix share the CUs. All write partial states. Each role
 // has its own pipeline shape (stages x keys per stage) inside one LDS
 // allocation, sized so that two work-groups fit on a CU.
-template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK>
+template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK, bool F8>
 __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs ga, const TileArgs sa,
                                                              const int n_prefix, const int n_group,
                                                              const GroupTable gt) {
   static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
-  constexpr int PB = TileSmem<D, PNS, PSK>::BYTES, SB = TileSmem<D, SNS, SSK>::BYTES;
+  constexpr int ESZ = F8 ? 1 : 2;
+  constexpr int PB = TileSmem<D, PNS, PSK, ESZ>::BYTES, SB = TileSmem<D, SNS, SSK, ESZ>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false>(pa, gt, bid, smem);
-  else if (bid < n_prefix + n_group) attn_item<D, PRB, PRW, PKG, PNS, PSK, false>(ga, gt, bid - n_prefix, smem);
-  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1)>(sa, gt, bid - n_prefix - n_group, smem);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8>(pa, gt, bid, smem);
+  else if (bid < n_prefix + n_group) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8>(ga, gt, bid - n_prefix, smem);
+  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8>(sa, gt, bid - n_prefix - n_group, smem);
 }
 
 }  // namespace ca

@@ -98,7 +98,7 @@ static PhaseTile choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& 
   const int64_t mtiles = cdiv(rows, bm);
   const int64_t ntiles = cdiv(pl.prefix_len, kTileKeys);
   const int64_t max_tiles = kMaxItemTokens / kTileKeys;
-  const double bpt = 4.0 * pl.hkv * pl.d;                       // K+V bytes per token
+  const double bpt = 2.0 * pl.kv_bytes() * pl.hkv * pl.d;       // K+V bytes per token
   const double part_per_split = (double)pl.total_q * pl.hq * (pl.d + 1) * 4.0;
   double best = 1e30;
   t.mtiles = (int32_t)mtiles;
@@ -174,7 +174,7 @@ static int32_t pick_heads_per_item(const ca_plan& pl, int64_t prefix_items, int6
 // KV actually streamed, plus the MFMA work of 16-row padded query blocks.
 static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_flops, int32_t chunks, bool merge,
                             int32_t cus, const CostModel& cm, double extra_mall_bytes) {
-  const double bpt = 4.0 * pl.hkv * pl.d;
+  const double bpt = 2.0 * pl.kv_bytes() * pl.hkv * pl.d;
   const double io = (double)pl.total_q * pl.hq * pl.d * 2.0 * 2.0;
   const double t_bytes = (bpt * kv_tokens + io) / cm.hbm_bw + extra_mall_bytes / cm.reread_bw;
   const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma_rows);
@@ -300,6 +300,13 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     return fail(CA_EINVAL, "heads_per_item must be 0 or divide num_kv_heads");
   if (p.separate_phases != 0 && p.separate_phases != 1) return fail(CA_EINVAL, "separate_phases must be 0 or 1");
   if (p.max_levels < 0 || p.max_levels > 2) return fail(CA_EINVAL, "max_levels must be 0, 1 or 2");
+  if (p.kv_dtype != CA_KV_BF16 && p.kv_dtype != CA_KV_FP8_E4M3) return fail(CA_EINVAL, "unknown kv_dtype");
+  if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
+  if (p.kv_dtype == CA_KV_FP8_E4M3) {
+    if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
+    if (p.kv_stride_page % 16 || p.kv_stride_token % 16 || p.kv_stride_head % 16)
+      return fail(CA_EUNSUPPORTED, "fp8 KV strides must be multiples of 16 elements");
+  }
 
   const int32_t n = p.num_reqs, ps = p.page_size, stride = p.block_table_stride;
   if (qsl[0] != 0) return fail(CA_EMETA, "query_start_loc[0] must be 0");
@@ -340,6 +347,9 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   pl->max_q_len = max_q;
   pl->max_seq_len = max_seq;
   pl->scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)p.head_dim);
+  pl->kv_fp8 = p.kv_dtype == CA_KV_FP8_E4M3 ? 1 : 0;
+  pl->k_scale = (pl->kv_fp8 && p.k_scale > 0.f) ? p.k_scale : 1.f;
+  pl->v_scale = (pl->kv_fp8 && p.v_scale > 0.f) ? p.v_scale : 1.f;
 
   // Step 1: shared pages. Step 2: cap at min num_computed, floor to a page.
   pl->common_blocks = count_common_blocks(bt, n, stride, seq_lens, ps);
@@ -358,7 +368,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   pl->kv_tokens_cascade = plen + (sum_seq - plen * n);
 
   const CostModel cm;
-  const double bpt = 4.0 * pl->hkv * pl->d;
+  const double bpt = 2.0 * pl->kv_bytes() * pl->hkv * pl->d;
 
   // Non-cascade estimate: every request streams its whole sequence; the
   // shared pages are fetched from HBM once and re-read from cache by the
@@ -449,11 +459,14 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->prefix = pre;
     pl->suffix = suf;
     pl->lvl1 = lvl1;
-    pl->prefix.stages = 2;   // all phases share one launch (two work-groups per CU)
-    pl->suffix.stages = 2;
+    // all phases share one launch (two work-groups per CU): 2 stages of
+    // bf16 or 4 of fp8 in the same LDS; fp8 items run one KV head each
+    pl->prefix.stages = pl->kv_fp8 ? 4 : 2;
+    pl->suffix.stages = pl->kv_fp8 ? 4 : 2;
     pl->suffix.heads_per_item =
-        pick_heads_per_item(*pl, (int64_t)pre.mtiles * pl->hkv * pre.splits + group_items,
-                            std::max<int64_t>(pre.split_tokens / kTileKeys, group_stages), suf, cus);
+        pl->kv_fp8 ? 1
+                   : pick_heads_per_item(*pl, (int64_t)pre.mtiles * pl->hkv * pre.splits + group_items,
+                                         std::max<int64_t>(pre.split_tokens / kTileKeys, group_stages), suf, cus);
     pl->merge_in_suffix = 0;
     pl->separate_phases = p.separate_phases;
     pl->num_slots = pre.splits + lvl1.splits + suf.splits;
@@ -463,7 +476,8 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->max_suffix_len = max_seq;
     pl->prefix = PhaseTile{};
     pl->suffix = nc;
-    pl->suffix.heads_per_item = (nc.kernel == 1 && p.heads_per_item > 0) ? p.heads_per_item : 1;
+    if (pl->kv_fp8) pl->suffix.stages = 4;
+    pl->suffix.heads_per_item = (nc.kernel == 1 && p.heads_per_item > 0 && !pl->kv_fp8) ? p.heads_per_item : 1;
     pl->merge_in_suffix = 0;
     pl->separate_phases = 0;
     pl->num_slots = nc.splits > 1 ? nc.splits : 0;
@@ -503,6 +517,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->separate_phases = pl->separate_phases;
   out->num_level1_groups = pl->lvl1.n;
   out->level1_splits = pl->lvl1.splits;
+  out->kv_dtype = pl->kv_fp8 ? CA_KV_FP8_E4M3 : CA_KV_BF16;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

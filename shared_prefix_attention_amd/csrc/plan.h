@@ -53,6 +53,10 @@ struct ca_plan {
   int32_t max_q_len = 0;
   int32_t max_seq_len = 0;
   float scale = 0.f;
+  int32_t kv_fp8 = 0;          // K/V caches hold fp8 e4m3 (1 byte per element)
+  float k_scale = 1.f;         // dequantisation factors of the caches (1 for bf16)
+  float v_scale = 1.f;
+  int32_t kv_bytes() const { return kv_fp8 ? 1 : 2; }
 
   int32_t common_blocks = 0;
   int32_t prefix_len = 0;

@@ -37,6 +37,9 @@ class DeviceBatch:
 
 def plan(b, mode="auto", layout="NHD", k_cache=None, **kw):
     w = b.workload
+    if w.kv_dtype == "fp8":
+        kw.setdefault("k_scale", w.k_scale)
+        kw.setdefault("v_scale", w.v_scale)
     cache = b.k_cache if layout == "NHD" else b.k_cache.permute(0, 2, 1, 3).contiguous()
     if k_cache is not None:
         cache = k_cache
@@ -52,8 +55,19 @@ def run(db: DeviceBatch, mode="auto", **kw):
     return out.float().cpu().numpy(), lse.cpu().numpy(), pl.info
 
 
+def oracle_kv(b):
+    """The caches' values for the oracle: bf16 as is, fp8 codes decoded by the
+    oracle's own E4M3 decoder times the scales."""
+    w = b.workload
+    if w.kv_dtype == "fp8":
+        return (oracle.fp8_e4m3_decode(b.k_cache.numpy()) * w.k_scale,
+                oracle.fp8_e4m3_decode(b.v_cache.numpy()) * w.v_scale)
+    return b.k_cache.float().numpy(), b.v_cache.float().numpy()
+
+
 def oracle_ref(b, requests=None):
-    return oracle.attention_full(b.q.float().numpy(), b.k_cache.float().numpy(), b.v_cache.float().numpy(),
+    k, v = oracle_kv(b)
+    return oracle.attention_full(b.q.float().numpy(), k, v,
                                  b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy(),
                                  b.workload.page_size, scale=b.workload.softmax_scale, requests=requests)
 

@@ -192,6 +192,18 @@ def test_error_codes():
     with pytest.raises(spa.CascadeAttnError) as e:
         _try(max_levels=3)
     assert e.value.status == _lib.CA_EINVAL
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(kv_dtype=2)
+    assert e.value.status == _lib.CA_EINVAL
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(kv_dtype="fp8")                       # head_dim 64
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(kv_dtype="fp8", head_dim=128, kv_strides=(16 * 2 * 128, 2 * 128, 120))
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _try(kv_dtype="fp8", head_dim=128, kv_strides=(16 * 2 * 128, 2 * 128, 128), k_scale=float("nan"))
+    assert e.value.status == _lib.CA_EINVAL
 
 
 def test_plan_partition_is_consistent():
@@ -339,3 +351,19 @@ def test_level1_keeps_the_64_groups_that_save_most():
     assert len(every) == 100 and len(got) == 64
     by_saving = sorted(every, key=lambda g: -(g[2] - level0 * ps))
     assert sorted(got) == sorted(by_saving[:64]) and got == sorted(got)
+
+
+def test_fp8_plans():
+    """fp8 caches: the same decisions and partition as bf16 except the byte
+    count the cost model uses, four pipeline stages in the same LDS, and one
+    KV head per work item (an explicit heads_per_item is not applied)."""
+    b16 = workloads.make_batch(workloads.get("worked_decode"))
+    b8 = workloads.make_batch(workloads.get("worked_decode_fp8"))
+    i16, i8 = _plan(b16, mode="on").info, _plan(b8, mode="on").info
+    assert i8["kv_dtype"] == _lib.KV_FP8_E4M3 and i16["kv_dtype"] == _lib.KV_BF16
+    assert i8["prefix_stages"] == 4 and i8["suffix_stages"] == 4 and i8["suffix_heads_per_item"] == 1
+    assert i8["common_prefix_len"] == i16["common_prefix_len"] == 4096
+    assert i8["kv_tokens_cascade"] == i16["kv_tokens_cascade"]
+    assert _plan(b8, mode="on", heads_per_item=2).info["suffix_heads_per_item"] == 1
+    off = _plan(b8, mode="off").info
+    assert off["suffix_stages"] == 4 and off["suffix_heads_per_item"] == 1

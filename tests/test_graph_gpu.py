@@ -20,7 +20,8 @@ def setup_module():
 
 
 @pytest.mark.parametrize("name,mode", [("tiny_decode", "on"), ("worked_decode", "auto"),
-                                       ("mixed_prefill", "on"), ("mixed_prefill", "off")])
+                                       ("mixed_prefill", "on"), ("mixed_prefill", "off"),
+                                       ("worked_decode_fp8", "auto"), ("multi_doc", "on")])
 def test_graph_replays_match_eager(name, mode):
     log(f"[graph] {name} mode={mode}")
     b = workloads.make_batch(workloads.get(name))

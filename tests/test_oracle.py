@@ -481,6 +481,46 @@ def test_kv_tokens_multilevel_hand():
     assert oracle.kv_tokens_multilevel(16, [], [60, 70, 30]) == oracle.kv_tokens_cascade(16, [60, 70, 30])
 
 
+# ------------------------------------------------------------- fp8 caches
+
+def test_fp8_e4m3_hand_values():
+    """Codes worked by hand from the E4M3 layout (sign, 4-bit exponent with
+    bias 7, 3-bit mantissa; exponent 0 subnormal; S.1111.111 NaN)."""
+    cases = {0x00: 0.0, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+             0x07: 7 * 2.0 ** -9, 0xB8: -1.0, 0xC4: -3.0, 0x30: 0.5, 0x77: 240.0}
+    got = oracle.fp8_e4m3_decode(np.array(list(cases), dtype=np.uint8))
+    assert got.tolist() == list(cases.values())
+    nan = oracle.fp8_e4m3_decode(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.isnan(nan).all()
+    z = oracle.fp8_e4m3_decode(np.array([0x80], dtype=np.uint8))
+    assert z[0] == 0.0 and np.signbit(z[0])
+
+
+def test_fp8_e4m3_matches_torch_on_every_code():
+    """A library routine as a second reading of the format: torch's
+    float8_e4m3fn dtype, every one of the 256 codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(oracle.fp8_e4m3_decode(codes), ref, equal_nan=True)
+
+
+def test_fp8_workload_codes_dequantise_to_the_values():
+    """The fp8 batch recipe: the decoded codes times the scale are the bf16
+    batch's values rounded to the fp8 grid (within half a step, 2^-4
+    relative, or the subnormal step), and the poison stays NaN."""
+    base = dict(num_reqs=4, prefix=32, suffix=(3, 10), q_len=(1, 2), num_q_heads=4, num_kv_heads=2, head_dim=128,
+                seed=5)
+    b16 = workloads.make_batch(workloads.Workload("t", **base))
+    b8 = workloads.make_batch(workloads.Workload("t", **base, kv_dtype="fp8", k_scale=0.125, v_scale=0.0625))
+    assert torch.equal(b16.block_table, b8.block_table) and torch.equal(b16.q, b8.q)
+    for c16, c8, sc in ((b16.k_cache, b8.k_cache, 0.125), (b16.v_cache, b8.v_cache, 0.0625)):
+        x = c16.double().numpy()
+        y = oracle.fp8_e4m3_decode(c8.numpy()) * sc
+        assert np.array_equal(np.isnan(x), np.isnan(y))
+        ok = ~np.isnan(x)
+        assert (np.abs(y[ok] - x[ok]) <= np.maximum(np.abs(x[ok]) * 2.0 ** -4, sc * 2.0 ** -10) + 1e-12).all()
+
+
 # --------------------------------------------------------------- input recipe
 
 def test_workload_structure_matches_recipe():

@@ -45,6 +45,17 @@ SMALL = {
         # request 1 has computed only 601 tokens: the group's share is capped (896 -> 592)
         Workload("nested_capped", 8, 256, (10, 30), (1, 4), 8, 2, 128, seed=2016,
                  groups=((4, 640),), override=((1, 901, 300),)),
+        # fp8 e4m3 caches (head_dim 128), scales 1/8 (K) and 1/16 (V)
+        Workload("fp8_decode", 16, 512, (33, 47), (1, 1), 32, 8, 128, seed=2017,
+                 kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
+        Workload("fp8_prefill", 8, 256, (20, 100), (1, 20), 8, 2, 128, seed=2018,
+                 kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
+        Workload("fp8_gqa8_outliers", 24, 1024, (1, 100), (1, 1), 16, 2, 128, seed=2019,
+                 outlier_frac=0.01, outlier_scale=8.0, kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
+        Workload("fp8_nested", 12, 256, (1, 40), (1, 3), 8, 2, 128, seed=2020,
+                 groups=((4, 512), (3, 300)), kv_dtype="fp8", k_scale=0.25, v_scale=0.125),
+        Workload("fp8_fresh_prefill", 4, 0, (30, 50), (30, 50), 4, 1, 128, seed=2021,
+                 kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
     ]
 }
 
@@ -89,7 +100,7 @@ def test_grouped_heads(name, heads, mode):
     assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}/h{heads}")
 
 
-@pytest.mark.parametrize("name", ["decode_ragged", "prefill_mix", "d64_gqa"])
+@pytest.mark.parametrize("name", ["decode_ragged", "prefill_mix", "d64_gqa", "fp8_decode", "fp8_prefill"])
 def test_small_hnd_layout(name):
     log(f"[parity] {name} HND")
     b = workloads.make_batch(SMALL[name])
@@ -131,7 +142,8 @@ def test_full_size_sampled_parity(name):
 
 
 SEPARATE = ["tiny_decode", "prefill_mix", "prefill_capped", "gqa8_outliers", "many_rows", "d64_gqa",
-            "nested_decode", "nested_prefill", "worked_decode", "mixed_prefill", "self_consistency", "multi_doc"]
+            "nested_decode", "nested_prefill", "fp8_decode", "fp8_prefill", "fp8_nested", "worked_decode",
+            "mixed_prefill", "self_consistency", "multi_doc", "worked_decode_fp8"]
 
 
 @pytest.mark.parametrize("name", SEPARATE)

@@ -22,6 +22,9 @@ behind one shared system prompt or document, each with its own continuation):
 * block-table padding columns hold random *valid* page ids;
 * Q, K, V ~ N(0, 1) in fp32, optionally with a Bernoulli outlier mask scaled
   by a factor, then rounded to bf16.
+* fp8 caches (``kv_dtype="fp8"``): K / V are stored as fp8 e4m3 codes (uint8)
+  of value / k_scale and value / v_scale (clamped to +-448, rounded to
+  nearest by torch's float8_e4m3fn cast); the poison is the NaN code 0x7f.
 
 Nested sharing (``groups``): consecutive runs of requests additionally share
 a document of L_g tokens after the batch-wide prefix (system prompt ->
@@ -59,6 +62,9 @@ class Workload:
     # (members, shared tokens): runs of consecutive requests from request 0
     # that share a document after the prefix; remaining requests share none
     groups: Tuple[Tuple[int, int], ...] = ()
+    kv_dtype: str = "bf16"           # "bf16" or "fp8" (e4m3 codes, dequantised by the scales)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def softmax_scale(self) -> float:
@@ -74,7 +80,8 @@ def _w(name, n, p, s, q, hq, hkv, d, seed, **kw) -> Workload:
 # S=128); mixed chunked prefill; many-sample self-consistency decode; long
 # shared document (+ at the 8-request threshold, + with a 255-token prefix).
 # Then two batches with nested sharing (system prompt -> document ->
-# request): decode and chunked prefill, some requests in no group.
+# request): decode and chunked prefill, some requests in no group. Then the
+# worked example and the prefill mix with fp8 e4m3 caches.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in [
         _w("tiny_decode", 8, 256, (16, 16), (1, 1), 4, 4, 64, 1000),
@@ -93,6 +100,12 @@ WORKLOADS: Dict[str, Workload] = {
            groups=((8, 2048), (8, 2048), (6, 3072), (6, 1000))),
         _w("multi_doc_prefill", 24, 512, (32, 200), (1, 24), 32, 8, 128, 1006,
            groups=((6, 1024), (6, 768), (4, 2000))),
+        _w("worked_decode_fp8", 64, 4096, (128, 128), (1, 1), 32, 8, 128, 1007,
+           kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
+        _w("mixed_prefill_fp8", 32, 2048, (64, 512), (1, 64), 32, 8, 128, 1008,
+           kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
+        _w("self_consistency_fp8", 256, 8192, (1, 1024), (1, 1), 64, 8, 128, 1009,
+           outlier_frac=0.01, outlier_scale=8.0, kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
     ]
 }
 
@@ -101,8 +114,8 @@ WORKLOADS: Dict[str, Workload] = {
 class Batch:
     workload: Workload
     q: torch.Tensor                  # [T, Hq, d] bf16
-    k_cache: torch.Tensor            # [num_pages, page_size, Hkv, d] bf16
-    v_cache: torch.Tensor            # [num_pages, page_size, Hkv, d] bf16
+    k_cache: torch.Tensor            # [num_pages, page_size, Hkv, d] bf16, or uint8 fp8 codes
+    v_cache: torch.Tensor            # [num_pages, page_size, Hkv, d] bf16, or uint8 fp8 codes
     block_table: torch.Tensor        # [N, stride] int32
     query_start_loc: torch.Tensor    # [N+1] int32
     seq_lens: torch.Tensor           # [N] int32
@@ -178,7 +191,7 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
 
     nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
     caches = []
-    for _ in range(2):                                   # K then V
+    for _ in range(2):                                   # K then V (values; fp8 codes below)
         cache = torch.full((num_pages, ps, hkv, d), nan.item(), dtype=torch.bfloat16)
         prefix_vals = _randn((w.prefix, hkv, d), gen, w.outlier_frac, w.outlier_scale)
         if shared_pages:
@@ -207,6 +220,12 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
             cache[pages, t % ps] = own_vals
         caches.append(cache)
 
+    if w.kv_dtype == "fp8":
+        def codes(cache, scale):
+            x = cache.float() / scale
+            x = torch.where(torch.isnan(x), x, x.clamp(-448.0, 448.0))
+            return x.to(torch.float8_e4m3fn).view(torch.uint8)
+        caches = [codes(caches[0], w.k_scale), codes(caches[1], w.v_scale)]
     total_q = sum(q_l)
     q = _randn((total_q, w.num_q_heads, d), gen, w.outlier_frac, w.outlier_scale)
     qsl = torch.zeros(n + 1, dtype=torch.int32)
