@@ -106,6 +106,11 @@ typedef struct {
   int32_t kv_dtype;            /* ca_kv_dtype_t */
   float k_scale;               /* fp8: K dequantisation factor (<= 0 selects 1); ignored for bf16 */
   float v_scale;               /* fp8: V dequantisation factor (<= 0 selects 1); ignored for bf16 */
+  int32_t sliding_window;      /* 0 = none; W >= 1: a query at position p sees p - W < t <= p. Cascade
+                                  is not used when the window binds ([p2] section 3 lists sliding
+                                  window among the features cascade does not support): AUTO then
+                                  runs the non-cascade path and FORCE_ON fails with CA_EUNSUPPORTED */
+  int32_t reserved1;
 } ca_params_t;
 
 typedef struct {
@@ -127,6 +132,8 @@ typedef struct {
   int32_t num_level1_groups;           /* request groups of the second shared level (0 = none) */
   int32_t level1_splits;               /* KV splits of every group (partial slots of that level) */
   int32_t kv_dtype;                    /* ca_kv_dtype_t of the plan */
+  int32_t sliding_window;              /* window applied by the plan (0: none, or it never binds) */
+  int32_t reserved0;
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
   int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */
@@ -209,6 +216,12 @@ ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* 
  *   k_cache, v_cache paged caches of the plan's kv_dtype and strides
  *   block_table_d, query_start_loc_d, seq_lens_d: device copies of the
  *                    same metadata given to cascade_attn_plan
+ *   sinks_d          [num_q_heads] fp32 attention-sink logits, or NULL. [p2]
+ *                    section 9: every backend receives an optional sinks
+ *                    parameter. Reading: one logit z_h per query head joins
+ *                    the softmax normaliser with no value, out = sum_t
+ *                    exp(s_t) v_t / (sum_t exp(s_t) + exp(z_h)), and lse
+ *                    includes it. May change between runs of one plan.
  *   out              [T][num_q_heads][head_dim] bf16 (written)
  *   lse_out          [T][num_q_heads] fp32, natural log (written; may be NULL)
  *   workspace        device scratch of >= info.workspace_bytes bytes (may be
@@ -223,8 +236,8 @@ ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* 
  */
 ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_table_d, const int32_t* query_start_loc_d,
-                             const int32_t* seq_lens_d, void* out, float* lse_out, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             const int32_t* seq_lens_d, const float* sinks_d, void* out, float* lse_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Frees a plan (NULL is accepted). */
 void cascade_attn_plan_destroy(ca_plan_t plan);

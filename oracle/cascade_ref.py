@@ -35,7 +35,7 @@ MIN_PREFIX_TOKENS = 256
 MIN_NUM_REQS = 8
 
 
-def attend(q_rows, keys, values, scale, visible=None):
+def attend(q_rows, keys, values, scale, visible=None, sink=None):
     """Softmax attention of query rows over an explicit key set, in fp64.
 
     The plain definition ([p2] section 1: cascade is "mathematically
@@ -43,17 +43,28 @@ def attend(q_rows, keys, values, scale, visible=None):
     lse = log sum exp(s).
 
     q_rows [m, d], keys [n, d], values [n, d]; ``visible`` optional bool
-    [m, n] (True = key visible). Returns (o [m, d], lse [m]). A row that sees
-    no key gets o = 0 and lse = -inf.
+    [m, n] (True = key visible). ``sink``: optional attention-sink logit
+    ([p2] section 9 names the sinks parameter every backend receives; the
+    reading here is one logit per query head that joins the softmax
+    normaliser and carries no value): it is one more score, with value 0,
+    so lse = log(sum exp(s) + exp(sink)). Returns (o [m, d], lse [m]). A row
+    that sees no key (and has no sink) gets o = 0 and lse = -inf.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     keys = np.asarray(keys, dtype=np.float64)
     values = np.asarray(values, dtype=np.float64)
     m = q_rows.shape[0]
     d = q_rows.shape[1]
+    if sink is not None:
+        keys = np.concatenate([keys, np.zeros((1, d))])
+        values = np.concatenate([values, np.zeros((1, d))])
+        vis = np.ones((m, keys.shape[0] - 1), dtype=bool) if visible is None else np.asarray(visible, dtype=bool)
+        visible = np.concatenate([vis, np.ones((m, 1), dtype=bool)], axis=1)
     if keys.shape[0] == 0:
         return np.zeros((m, d)), np.full(m, -np.inf)
     s = (q_rows @ keys.T) * float(scale)
+    if sink is not None:
+        s[:, -1] = float(sink)
     if visible is not None:
         s = np.where(visible, s, -np.inf)
     row_max = s.max(axis=1)
@@ -112,7 +123,7 @@ def _request_kv(cache, block_table_row, seq_len, page_size, kv_head):
 
 
 def attention_full(q, k_cache, v_cache, block_table, query_start_loc, seq_lens,
-                   page_size, scale=None, requests=None):
+                   page_size, scale=None, requests=None, window=0, sinks=None):
     """Full (non-cascade) causal attention of every request over its whole KV.
 
     This is the plain definition the cascade path must reproduce ([p2]
@@ -123,7 +134,11 @@ def attention_full(q, k_cache, v_cache, block_table, query_start_loc, seq_lens,
     q [T, Hq, d]; k_cache, v_cache [num_pages, page_size, Hkv, d];
     block_table [N, stride]; query_start_loc [N+1]; seq_lens [N].
     ``requests``: optional iterable of request indices to compute (rows of
-    other requests are left NaN). Returns (out [T, Hq, d], lse [T, Hq]) fp64.
+    other requests are left NaN). ``window`` > 0: sliding-window attention, a
+    query at position p sees positions p - window < t <= p (the pages list
+    sliding window among the features cascade does not support, [p2]
+    section 3). ``sinks``: optional [Hq] attention-sink logits (see
+    ``attend``). Returns (out [T, Hq, d], lse [T, Hq]) fp64.
     """
     q = np.asarray(q)
     T, Hq, d = q.shape
@@ -150,9 +165,11 @@ def attention_full(q, k_cache, v_cache, block_table, query_start_loc, seq_lens,
             for j in range(group):
                 h = g * group + j
                 rows = np.asarray(q[q0:q1, h, :], dtype=np.float64)
-                i = np.arange(q_len)
-                visible = t[None, :] <= (num_computed + i)[:, None]
-                o_h, l_h = attend(rows, keys, vals, scale, visible)
+                pos = num_computed + np.arange(q_len)
+                visible = t[None, :] <= pos[:, None]
+                if window > 0:
+                    visible &= t[None, :] > (pos - int(window))[:, None]
+                o_h, l_h = attend(rows, keys, vals, scale, visible, None if sinks is None else sinks[h])
                 out[q0:q1, h, :] = o_h
                 lse[q0:q1, h] = l_h
     return out, lse

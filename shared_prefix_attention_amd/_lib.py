@@ -51,6 +51,8 @@ class ca_params_t(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("sliding_window", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -74,6 +76,8 @@ class ca_plan_info_t(ctypes.Structure):
         ("num_level1_groups", ctypes.c_int32),
         ("level1_splits", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("kv_tokens_cascade", ctypes.c_int64),
@@ -107,7 +111,7 @@ def load() -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_void_p)]
     lib.cascade_attn_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(ca_plan_info_t)]
     lib.cascade_attn_run.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
-        [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
     lib.cascade_attn_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.cascade_attn_plan_destroy.restype = None
@@ -187,7 +191,8 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
                       num_pages: int, kv_strides, block_table, query_start_loc, seq_lens,
                       num_computed_tokens=None, softmax_scale: float = 0.0, mode="auto",
                       num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
-                      max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0) -> Plan:
+                      max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0,
+                      sliding_window: int = 0) -> Plan:
     """Host-only planner (see cascade_attn_plan in the header).
 
     kv_strides: (page, token-slot, head) element strides of the K/V caches.
@@ -220,6 +225,7 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
     prm.kv_dtype = _KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
     prm.k_scale = float(k_scale)
     prm.v_scale = float(v_scale)
+    prm.sliding_window = int(sliding_window)
     h = ctypes.c_void_p(0)
     _check(load().cascade_attn_plan(ctypes.byref(prm), bt_p, qsl_p, sl_p, nc_p, ctypes.byref(h)))
     return Plan(h.value)
@@ -240,11 +246,11 @@ def cascade_attn_plan_groups(plan: Plan):
 
 
 def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d,
-                     out, lse_out=None, workspace=None, stream=None) -> None:
+                     out, lse_out=None, workspace=None, stream=None, sinks=None) -> None:
     """Launch one attention step on ``stream`` (default: torch's current stream).
 
     All tensors are device tensors (torch); see cascade_attn_run in the header
-    for dtypes and layouts.
+    for dtypes and layouts. ``sinks``: optional [num_q_heads] fp32 tensor.
     """
     import torch
     for name, t in (("q", q), ("out", out)):
@@ -255,9 +261,12 @@ def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start
     s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise CascadeAttnError(CA_EINVAL, "sinks must be a contiguous float32 tensor")
     _check(load().cascade_attn_run(
         plan.handle, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table_d.data_ptr(),
-        query_start_loc_d.data_ptr(), seq_lens_d.data_ptr(), out.data_ptr(),
+        query_start_loc_d.data_ptr(), seq_lens_d.data_ptr(), sinks.data_ptr() if sinks is not None else None,
+        out.data_ptr(),
         lse_out.data_ptr() if lse_out is not None else None, ws_ptr, ws_bytes, s))
 
 

@@ -76,6 +76,8 @@ struct TileArgs {
   int32_t lvl1_slot_base;       // per-request phase: first partial slot of the group level
   int32_t lvl1_slots;           //   and its slot count (rows of requests in no group get -inf there)
   float v_scale;                // dequantisation factor of V (1 for bf16 caches)
+  int32_t window;               // per-request phase: sliding window W (> 0: keys p - W < t <= p)
+  const float* sinks;           // [hq] attention-sink logits (natural log) or null; direct mode only
 };
 
 // Second shared level: request groups [req_begin, req_end) whose members
@@ -258,7 +260,9 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
 
 // MH: the item may cover several consecutive KV heads of one request (same
 // pages and key range), run as one continuous stage pipeline.
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
+// WIN: the item may apply a sliding window and attention sinks (the
+// stand-alone kernel; the cascade launch has neither).
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const int bid, uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
@@ -303,6 +307,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   const int32_t* bt_row;
   int req = 0, c = 0, mt = 0, grp = -1;
   int split_tokens = a.split_tokens;
+  int win_lo_max = 0x80000000;          // window start of the item's last row (no window: none)
+  int page_skip = 0;                    // pages of the item skipped below a sliding window
   const int H = MH ? a.heads_per_item : 1;   // KV heads g0 .. g0 + H - 1, one after another
   if (a.prefix_mode) {
     int local = bid;
@@ -370,6 +376,15 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     key_end = max(key_begin, min(key_begin + split_tokens, seq_len));
     tok_base = q0;
     q_pos_base = seq_len - q_len;        // num_computed_tokens
+    if (WIN && a.window > 0) {
+      // sliding window: stages wholly below the first row's window are
+      // skipped (the page table stays indexed from the item's first page)
+      win_lo_max = q_pos_base + (row_end - 1) / a.group - a.window + 1;
+      const int lo_min = q_pos_base + row_begin / a.group - a.window + 1;
+      const int skip = min(max(0, (lo_min - key_begin) / SK), (key_end - key_begin + SK - 1) / SK);
+      key_begin += skip * SK;
+      page_skip = skip * SK / 16;
+    }
     // rows of a request in no group have no group-level state: mark those
     // partial slots empty (weight 0 in the merge)
     if (grp < 0 && c == 0 && a.lvl1_slots > 0) {
@@ -384,7 +399,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       }
     }
   }
-  const int n_tiles = (key_end - key_begin + SK - 1) / SK;
+  const int n_tiles = max(0, (key_end - key_begin + SK - 1) / SK);
   // keys at or below this position are visible to every row of the item
   const int all_visible_to = causal ? q_pos_base + row_begin / a.group : 0x7fffffff;
 #pragma unroll
@@ -498,7 +513,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 #pragma unroll
   for (int r = 0; r < NPR; ++r) {
     const int st_i = lane + 64 * r;
-    ptab[r] = st_i < n_tiles ? s_pages[(st_i * SK + wave * KPW) >> 4] : 0;
+    ptab[r] = st_i < n_tiles ? s_pages[page_skip + ((st_i * SK + wave * KPW) >> 4)] : 0;
   }
   // page of the item's last position: the source of every clamped lane
   const int last_pid = n_tiles > 0 ? s_pages[((key_end - 1) >> 4) - first_page] : 0;
@@ -632,10 +647,22 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     if (!wave_active || (KG > 1 && kg > 0)) return;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float l_tot = wave_sum_across_quads(l_run[rb]);
+      float l_tot = wave_sum_across_quads(l_run[rb]);
+      float m_fin = m_run[rb];
+      float o_fac = 1.f;
+      if (WIN && a.direct && a.sinks && row_ok[rb]) {
+        // attention sink: one more term exp(z) of the normaliser, no value
+        const float z = a.sinks[g * a.group + row_j[rb]] * kLog2e;
+        const float mn = vmax(m_fin, z);
+        if (mn != -INFINITY) {
+          o_fac = (m_fin == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_fin - mn);
+          l_tot = l_tot * o_fac + __builtin_amdgcn_exp2f(z - mn);
+          m_fin = mn;
+        }
+      }
       const bool live = l_tot > 0.f;
-      const float inv = live ? a.v_scale / l_tot : 0.f;
-      const float lse = live ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      const float inv = live ? a.v_scale * o_fac / l_tot : 0.f;
+      const float lse = live ? (m_fin + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
       if (!row_ok[rb]) continue;
       const int64_t row = (int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb];
       if (a.direct) {
@@ -770,7 +797,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) reg_fence(s[kb]);   // softmax below the V reads
       // online softmax over this wave's keys of the stage, per row (lane lr)
-      const bool need_mask = (kt0 + NKB * 16 > key_end) || (kt0 + NKB * 16 - 1 > all_visible_to);
+      const bool need_mask =
+          (kt0 + NKB * 16 > key_end) || (kt0 + NKB * 16 - 1 > all_visible_to) || (WIN && kt0 < win_lo_max);
       u32x2_t pb[RB][NKB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -779,10 +807,13 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
           // item end and (causal) the row's position + 1
           const int lim = causal ? min(key_end, row_qpos[rb] + 1) : key_end;
           const int rem = lim - (kt0 + lq * 4);
+          // and, with a sliding window, at or above the row's window start
+          const int lo = (WIN && a.window > 0) ? row_qpos[rb] - a.window + 1 - (kt0 + lq * 4) : -0x40000000;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[kb][rb][i] = (kb * 16 + i < rem) ? s[kb][rb][i] : -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              s[kb][rb][i] = (kb * 16 + i < rem && kb * 16 + i >= lo) ? s[kb][rb][i] : -INFINITY;
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -872,7 +903,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
 __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
-  attn_item<D, RB, RW, KG, NS, SK, MH, F8>(a, gt, blockIdx.x, smem);
+  attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, blockIdx.x, smem);
 }
 
 // One launch for all cascade phases: work-groups [0, n_prefix) run prefix
@@ -890,9 +921,10 @@ __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, 
   constexpr int PB = TileSmem<D, PNS, PSK, ESZ>::BYTES, SB = TileSmem<D, SNS, SSK, ESZ>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8>(pa, gt, bid, smem);
-  else if (bid < n_prefix + n_group) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8>(ga, gt, bid - n_prefix, smem);
-  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8>(sa, gt, bid - n_prefix - n_group, smem);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(pa, gt, bid, smem);
+  else if (bid < n_prefix + n_group)
+    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(ga, gt, bid - n_prefix, smem);
+  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false>(sa, gt, bid - n_prefix - n_group, smem);
 }
 
 }  // namespace ca

@@ -5,7 +5,9 @@
 // of every (token, head) row in one pass:
 //   M = max_s lse_s, w_s = exp(lse_s - M), out = sum_s w_s o_s / sum_s w_s,
 //   lse = M + log(sum_s w_s).
-// Partials with lse = -inf have weight 0 and their o is not read.
+// Partials with lse = -inf have weight 0 and their o is not read. An
+// attention sink (one logit per query head) enters as one more state with
+// lse = sink and o = 0.
 #pragma once
 
 #include "device_common.hpp"
@@ -20,6 +22,8 @@ struct MergeArgs {
   int64_t slot_elems;      // rows * D
   uint16_t* out;           // [rows][D] bf16
   float* lse_out;          // [rows] (may be null)
+  const float* sinks;      // [hq] attention-sink logits or null: a state lse = sink, o = 0
+  int32_t hq;
 };
 
 // D/4 threads per row, each owning 4 consecutive d values.
@@ -35,6 +39,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   // use, so a row costs one memory round trip per batch.
   constexpr int B = 16;
   float m = -INFINITY, wsum = 0.f;
+  if (a.sinks) {   // the sink joins the normaliser as one more state with no value
+    m = a.sinks[row % a.hq];
+    wsum = m == -INFINITY ? 0.f : 1.f;
+  }
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < a.slots; s0 += B) {
     float l[B];

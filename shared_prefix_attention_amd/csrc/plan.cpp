@@ -301,6 +301,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.separate_phases != 0 && p.separate_phases != 1) return fail(CA_EINVAL, "separate_phases must be 0 or 1");
   if (p.max_levels < 0 || p.max_levels > 2) return fail(CA_EINVAL, "max_levels must be 0, 1 or 2");
   if (p.kv_dtype != CA_KV_BF16 && p.kv_dtype != CA_KV_FP8_E4M3) return fail(CA_EINVAL, "unknown kv_dtype");
+  if (p.sliding_window < 0) return fail(CA_EINVAL, "sliding_window must be >= 0");
   if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
   if (p.kv_dtype == CA_KV_FP8_E4M3) {
     if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
@@ -449,9 +450,21 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->kv_tokens_cascade = plen + group_tokens + suffix_tokens;
   }
 
+  // A sliding window that hides some position from some query rules the
+  // packed non-causal prefix out ([p2] section 3); one that never binds is
+  // plain causal attention and is dropped.
+  const bool window_binds = p.sliding_window > 0 && max_seq > p.sliding_window;
+  pl->window = window_binds ? p.sliding_window : 0;
   bool cascade = false;
-  if (p.mode == CA_MODE_FORCE_ON) cascade = plen > 0;
-  else if (p.mode == CA_MODE_AUTO) cascade = pl->gates_pass && pl->est_us_cascade < pl->est_us_noncascade;
+  if (p.mode == CA_MODE_FORCE_ON) {
+    if (window_binds && plen > 0) {
+      delete pl;
+      return fail(CA_EUNSUPPORTED, "cascade cannot run with a binding sliding window");
+    }
+    cascade = plen > 0;
+  } else if (p.mode == CA_MODE_AUTO) {
+    cascade = !window_binds && pl->gates_pass && pl->est_us_cascade < pl->est_us_noncascade;
+  }
   pl->use_cascade = cascade ? 1 : 0;
 
   if (cascade) {
@@ -518,6 +531,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->num_level1_groups = pl->lvl1.n;
   out->level1_splits = pl->lvl1.splits;
   out->kv_dtype = pl->kv_fp8 ? CA_KV_FP8_E4M3 : CA_KV_BF16;
+  out->sliding_window = pl->window;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

@@ -57,6 +57,7 @@ struct ca_plan {
   float k_scale = 1.f;         // dequantisation factors of the caches (1 for bf16)
   float v_scale = 1.f;
   int32_t kv_bytes() const { return kv_fp8 ? 1 : 2; }
+  int32_t window = 0;          // sliding window of the non-cascade path (0: none)
 
   int32_t common_blocks = 0;
   int32_t prefix_len = 0;

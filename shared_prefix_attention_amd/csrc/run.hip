@@ -172,7 +172,8 @@ ca_status_t run_merge(const MergeArgs& args, hipStream_t s) {
 
 template <int D>
 ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void* v, const int32_t* bt,
-                     const int32_t* qsl, const int32_t* sl, void* out, float* lse, void* ws, hipStream_t s) {
+                     const int32_t* qsl, const int32_t* sl, const float* sinks, void* out, float* lse, void* ws,
+                     hipStream_t s) {
   TileArgs base{};
   base.heads_per_item = 1;
   base.q = static_cast<const uint16_t*>(q);
@@ -190,6 +191,7 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   base.group = pl->group;
   base.scale_log2 = pl->scale * pl->k_scale * kLog2e;   // k dequantisation folded into the scores
   base.v_scale = pl->v_scale;
+  base.sinks = sinks;
   base.num_reqs = pl->num_reqs;
   base.slot_elems = pl->slot_elems;
   base.slot_rows = pl->total_q * pl->hq;
@@ -229,6 +231,7 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   sa.heads_per_item = pl->suffix.heads_per_item;
   sa.slot_base = pl->use_cascade ? pl->prefix.splits + (gt.n > 0 ? L.splits : 0) : 0;
   sa.direct = pl->direct_out ? 1 : 0;
+  sa.window = pl->use_cascade ? 0 : pl->window;
   sa.lvl1_slot_base = pl->prefix.splits;
   sa.lvl1_slots = gt.n > 0 ? L.splits : 0;
   // several KV heads per item only in the decode shape (its waves split the keys)
@@ -275,6 +278,8 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     ma.slot_elems = pl->slot_elems;
     ma.out = static_cast<uint16_t*>(out);
     ma.lse_out = lse;
+    ma.sinks = sinks;
+    ma.hq = pl->hq;
     st = run_merge<D>(ma, s);
     if (st != CA_OK) return st;
   }
@@ -294,8 +299,8 @@ extern "C" int ca_query_num_cus(int32_t* out) {
 
 extern "C" ca_status_t cascade_attn_run(ca_plan_t pl, const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* block_table_d, const int32_t* query_start_loc_d,
-                                        const int32_t* seq_lens_d, void* out, float* lse_out, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+                                        const int32_t* seq_lens_d, const float* sinks_d, void* out,
+                                        float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!pl) return fail(CA_EINVAL, "null plan");
   if (!q || !k_cache || !v_cache || !block_table_d || !query_start_loc_d || !seq_lens_d || !out)
     return fail(CA_EINVAL, "null tensor argument");
@@ -309,10 +314,10 @@ extern "C" ca_status_t cascade_attn_run(ca_plan_t pl, const void* q, const void*
     return fail(CA_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pl->d == 128)
-    return run_impl<128>(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse_out,
-                         workspace, s);
-  return run_impl<64>(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse_out, workspace,
-                      s);
+    return run_impl<128>(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, sinks_d, out,
+                         lse_out, workspace, s);
+  return run_impl<64>(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, sinks_d, out, lse_out,
+                      workspace, s);
 }
 
 extern "C" ca_status_t cascade_attn_profile_enable(int32_t enable) {

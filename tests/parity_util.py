@@ -48,9 +48,10 @@ def plan(b, mode="auto", layout="NHD", k_cache=None, **kw):
                           seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, layout=layout, mode=mode, **kw)
 
 
-def run(db: DeviceBatch, mode="auto", **kw):
+def run(db: DeviceBatch, mode="auto", sinks=None, **kw):
     pl = plan(db.b, mode=mode, layout=db.layout, k_cache=db.k, **kw)
-    out, lse = spa.run_batch(pl, db.q, db.k, db.v, db.bt, db.qsl, db.sl)
+    sinks_d = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).cuda().contiguous()
+    out, lse = spa.run_batch(pl, db.q, db.k, db.v, db.bt, db.qsl, db.sl, sinks=sinks_d)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), pl.info
 
@@ -65,11 +66,12 @@ def oracle_kv(b):
     return b.k_cache.float().numpy(), b.v_cache.float().numpy()
 
 
-def oracle_ref(b, requests=None):
+def oracle_ref(b, requests=None, window=0, sinks=None):
     k, v = oracle_kv(b)
     return oracle.attention_full(b.q.float().numpy(), k, v,
                                  b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy(),
-                                 b.workload.page_size, scale=b.workload.softmax_scale, requests=requests)
+                                 b.workload.page_size, scale=b.workload.softmax_scale, requests=requests,
+                                 window=window, sinks=None if sinks is None else np.asarray(sinks, dtype=np.float64))
 
 
 def rows_of(b, requests):

@@ -367,3 +367,21 @@ def test_fp8_plans():
     assert _plan(b8, mode="on", heads_per_item=2).info["suffix_heads_per_item"] == 1
     off = _plan(b8, mode="off").info
     assert off["suffix_stages"] == 4 and off["suffix_heads_per_item"] == 1
+
+
+def test_sliding_window_decisions():
+    """A window that hides positions from some query rules cascade out
+    (AUTO falls back, FORCE_ON refuses); one longer than every sequence
+    never binds and is dropped."""
+    wd = workloads.make_batch(workloads.get("worked_decode"))
+    assert _plan(wd, mode="auto", sliding_window=1024).info["use_cascade"] == 0
+    assert _plan(wd, mode="auto", sliding_window=1024).info["sliding_window"] == 1024
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _plan(wd, mode="on", sliding_window=1024)
+    assert e.value.status == _lib.CA_EUNSUPPORTED
+    wide = _plan(wd, mode="auto", sliding_window=4096 + 128).info
+    assert wide["sliding_window"] == 0 and wide["use_cascade"] == 1
+    assert _plan(wd, mode="off", sliding_window=100).info["sliding_window"] == 100
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _plan(wd, mode="auto", sliding_window=-1)
+    assert e.value.status == _lib.CA_EINVAL

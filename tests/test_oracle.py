@@ -481,6 +481,68 @@ def test_kv_tokens_multilevel_hand():
     assert oracle.kv_tokens_multilevel(16, [], [60, 70, 30]) == oracle.kv_tokens_cascade(16, [60, 70, 30])
 
 
+# ------------------------------------------------- sinks and sliding window
+
+def test_sink_hand_case():
+    """d=1, scale 1, one key with score 0 and value 6, sink ln 2: weights
+    1 / (1 + 2) for the key, so o = 2 and lse = ln 3."""
+    o, lse = oracle.attend([[1.0]], [[0.0]], [[6.0]], 1.0, sink=math.log(2.0))
+    assert abs(o[0, 0] - 2.0) < 1e-15 and abs(lse[0] - math.log(3.0)) < 1e-15
+    # a sink of -inf is no sink at all
+    q, k, v = np.random.default_rng(3).normal(size=(3, 4, 8))
+    a = oracle.attend(q, k, v, 0.5)
+    b = oracle.attend(q, k, v, 0.5, sink=-np.inf)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_sink_is_one_more_partial_in_the_merge():
+    """The way the merge applies a sink: an extra partial state with
+    lse = sink and o = 0, merged with the key partials, equals attention with
+    the sink over the union of the keys."""
+    rng = np.random.default_rng(4)
+    q, k, v = rng.normal(size=(5, 16)), rng.normal(size=(9, 16)), rng.normal(size=(9, 16))
+    sink = 0.7
+    full_o, full_l = oracle.attend(q, k, v, 0.25, sink=sink)
+    parts = [oracle.attend(q, k[:4], v[:4], 0.25), oracle.attend(q, k[4:], v[4:], 0.25),
+             (np.zeros((5, 16)), np.full(5, sink))]
+    o_m, l_m = oracle.merge_states([p[0] for p in parts], [p[1] for p in parts])
+    assert np.abs(o_m - full_o).max() < 1e-12 and np.abs(l_m - full_l).max() < 1e-12
+
+
+def test_window_special_cases_and_sdpa():
+    """A window of one key gives each query its own position's value; a
+    window longer than every sequence is plain causal attention; other
+    windows match torch SDPA in float64 with the explicit band mask."""
+    b = _small_batch(seed=21, n=4, prefix=24, suffix=(5, 20), q=(1, 6), ps=8)
+    w = b.workload
+    args = (b.q.float().numpy(), b.k_cache.float().numpy(), b.v_cache.float().numpy(), b.block_table.numpy(),
+            b.query_start_loc.numpy(), b.seq_lens.numpy(), w.page_size)
+    causal = oracle.attention_full(*args)
+    wide = oracle.attention_full(*args, window=int(b.seq_lens.max()))
+    assert np.array_equal(causal[0], wide[0]) and np.array_equal(causal[1], wide[1])
+    one_o, one_l = oracle.attention_full(*args, window=1)
+    G = w.num_q_heads // w.num_kv_heads
+    for r in range(w.num_reqs):
+        q0, q1 = int(b.query_start_loc[r]), int(b.query_start_loc[r + 1])
+        k, v = _dense_kv(b, r)
+        nc = int(b.num_computed[r])
+        for i in range(q1 - q0):
+            for h in range(w.num_q_heads):
+                assert np.abs(one_o[q0 + i, h] - v[nc + i, h // G].numpy()).max() < 1e-12
+        for win in (3, 11):
+            o, l = oracle.attention_full(*args, window=win, requests=[r])
+            L = k.shape[0]
+            pos = nc + torch.arange(q1 - q0)
+            t = torch.arange(L)
+            mask = (t[None, :] <= pos[:, None]) & (t[None, :] > (pos - win)[:, None])
+            for h in range(w.num_q_heads):
+                qq = b.q[q0:q1, h].double()[None, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qq, k[None, None, :, h // G], v[None, None, :, h // G], attn_mask=mask[None, None],
+                    scale=w.softmax_scale)[0, 0]
+                assert np.abs(o[q0:q1, h] - ref.numpy()).max() < 1e-12
+
+
 # ------------------------------------------------------------- fp8 caches
 
 def test_fp8_e4m3_hand_values():

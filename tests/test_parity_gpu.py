@@ -188,3 +188,54 @@ def test_second_level_against_single_level(name):
     assert_close(o2, l2, ref_o, ref_l, rows=rows, what=f"{name}/two-level")
     assert_close(o1, l1, ref_o, ref_l, rows=rows, what=f"{name}/one-level")
     assert np.all(np.abs(o2 - o1) <= 2e-2 + 1e-2 * np.abs(o1)) and np.abs(l2 - l1).max() <= 1e-3
+
+
+WINDOWS = [("decode_ragged", 1), ("decode_ragged", 37), ("prefill_mix", 17), ("prefill_mix", 200),
+           ("d64_gqa", 64), ("fresh_prefill", 9), ("fp8_prefill", 50), ("long_prefix_split", 1000),
+           ("many_rows", 130)]
+
+
+@pytest.mark.parametrize("name,window", WINDOWS)
+def test_sliding_window(name, window):
+    """Sliding window: AUTO takes the non-cascade path (the window binds),
+    stages wholly below a row's window are skipped, the rest is masked."""
+    log(f"[window] {name} W={window}")
+    b = workloads.make_batch(SMALL[name])
+    ref_o, ref_l = oracle_ref(b, window=window)
+    out, lse, info = run(DeviceBatch(b), mode="auto", sliding_window=window)
+    assert info["use_cascade"] == 0 and info["sliding_window"] == window
+    assert_close(out, lse, ref_o, ref_l, what=f"{name}/W{window}")
+
+
+def _sinks(hq, seed):
+    z = np.random.default_rng(seed).normal(0.0, 2.0, hq).astype(np.float32)
+    z[0] = -np.inf                     # a head without a sink
+    if hq > 2:
+        z[1] = 8.0                     # a sink that outweighs most keys
+    return z
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "prefill_mix", "gqa8_outliers", "nested_decode", "fp8_decode",
+                                  "long_prefix_split", "single_request"])
+@pytest.mark.parametrize("mode", ["on", "off"])
+def test_attention_sinks(name, mode):
+    """Attention sinks through the merge (cascade, split KV) and through the
+    direct epilogue (non-cascade with one chunk per request)."""
+    w = SMALL[name]
+    if mode == "on" and w.prefix == 0:
+        pytest.skip("no shared prefix")
+    log(f"[sinks] {name} mode={mode}")
+    b = workloads.make_batch(w)
+    z = _sinks(w.num_q_heads, w.seed)
+    ref_o, ref_l = oracle_ref(b, sinks=z)
+    out, lse, info = run(DeviceBatch(b), mode=mode, sinks=z)
+    log(f"  cascade={info['use_cascade']} slots={info['num_partial_slots']}")
+    assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}/sinks")
+
+
+def test_window_with_sinks():
+    b = workloads.make_batch(SMALL["prefill_mix"])
+    z = _sinks(b.workload.num_q_heads, 7)
+    ref_o, ref_l = oracle_ref(b, window=33, sinks=z)
+    out, lse, _ = run(DeviceBatch(b), mode="auto", sliding_window=33, sinks=z)
+    assert_close(out, lse, ref_o, ref_l, what="prefill_mix/W33/sinks")
