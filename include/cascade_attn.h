@@ -110,7 +110,8 @@ typedef struct {
                                   is not used when the window binds ([p2] section 3 lists sliding
                                   window among the features cascade does not support): AUTO then
                                   runs the non-cascade path and FORCE_ON fails with CA_EUNSUPPORTED */
-  int32_t reserved1;
+  int32_t prefix_splits;       /* 0 = planner's choice; else KV splits of the prefix phase (raised if an
+                                  item would exceed 8192 keys, lowered to the prefix's 64-key tiles) */
 } ca_params_t;
 
 typedef struct {
@@ -238,6 +239,40 @@ ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache,
                              const int32_t* block_table_d, const int32_t* query_start_loc_d,
                              const int32_t* seq_lens_d, const float* sinks_d, void* out, float* lse_out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-shape autotuning ([p4] "Update Cascade Attention Heuristics for FA3":
+ * the heuristic has to be re-derived for each kernel family; [p2] section 9:
+ * cascade only when it beats the plain path). Plans the batch as AUTO would,
+ * then times candidate plans on the device with the caller's data: the
+ * non-cascade path and, when a prefix is shared and no window binds, the
+ * cascade path with the planner's prefix split count, half and twice it,
+ * one or the planner's KV heads per decode item, and (if the batch has
+ * groups) one or two shared levels. Each candidate runs twice untimed and
+ * `iters` times between two HIP events on `stream`; candidates needing more
+ * than workspace_bytes are skipped. Returns the fastest plan in *out_plan
+ * (the caller destroys it) and its mean time per run in *out_us (may be
+ * NULL), and records the choice for this batch shape: later AUTO plans with
+ * no explicit overrides (prefix_splits, heads_per_item, max_levels all 0)
+ * and the same shape apply it. A shape is (num_reqs, head counts, head_dim,
+ * kv_dtype, window, and the power-of-two buckets of the shared prefix, total
+ * queries, longest query, mean remaining length and second-level group
+ * count). Synchronises the stream; not for graph capture. out, lse_out and
+ * workspace are overwritten (out / lse_out hold this batch's result).
+ * Errors: as cascade_attn_plan and cascade_attn_run; CA_EINVAL for iters
+ * outside [1, 1000]; CA_EWORKSPACE if no candidate fits the workspace.
+ */
+ca_status_t cascade_attn_autotune(const ca_params_t* params, const int32_t* block_table_h,
+                                  const int32_t* query_start_loc_h, const int32_t* seq_lens_h,
+                                  const int32_t* num_computed_tokens_h, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table_d,
+                                  const int32_t* query_start_loc_d, const int32_t* seq_lens_d,
+                                  const float* sinks_d, void* out, float* lse_out, void* workspace,
+                                  size_t workspace_bytes, void* stream, int32_t iters, ca_plan_t* out_plan,
+                                  float* out_us);
+
+/* Forgets every shape recorded by cascade_attn_autotune. */
+void cascade_attn_autotune_reset(void);
 
 /* Frees a plan (NULL is accepted). */
 void cascade_attn_plan_destroy(ca_plan_t plan);

@@ -8,6 +8,8 @@ torch provides device memory and streams.
 from ._lib import (  # noqa: F401
     CascadeAttnError,
     Plan,
+    cascade_attn_autotune,
+    cascade_attn_autotune_reset,
     cascade_attn_num_common_prefix_blocks,
     cascade_attn_plan,
     cascade_attn_plan_groups,

@@ -52,7 +52,7 @@ class ca_params_t(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("sliding_window", ctypes.c_int32),
-        ("reserved1", ctypes.c_int32),
+        ("prefix_splits", ctypes.c_int32),
     ]
 
 
@@ -113,12 +113,17 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_run.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
         [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
+    lib.cascade_attn_autotune.argtypes = [ctypes.POINTER(ca_params_t), _i32p, _i32p, _i32p, _i32p] + \
+        [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                  ctypes.POINTER(ctypes.c_float)]
+    lib.cascade_attn_autotune_reset.argtypes = []
+    lib.cascade_attn_autotune_reset.restype = None
     lib.cascade_attn_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.cascade_attn_plan_destroy.restype = None
     lib.cascade_attn_profile_enable.argtypes = [ctypes.c_int32]
     lib.cascade_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("cascade_attn_num_common_prefix_blocks", "cascade_attn_plan", "cascade_attn_plan_info",
-                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_profile_enable", "cascade_attn_profile_read"):
+                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_autotune", "cascade_attn_profile_enable", "cascade_attn_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -187,22 +192,16 @@ class Plan:
             pass
 
 
-def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
-                      num_pages: int, kv_strides, block_table, query_start_loc, seq_lens,
-                      num_computed_tokens=None, softmax_scale: float = 0.0, mode="auto",
-                      num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
-                      max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0,
-                      sliding_window: int = 0) -> Plan:
-    """Host-only planner (see cascade_attn_plan in the header).
-
-    kv_strides: (page, token-slot, head) element strides of the K/V caches.
-    block_table / query_start_loc / seq_lens / num_computed_tokens: host
-    int32 arrays or CPU tensors.
-    """
+def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int, kv_strides,
+            block_table, query_start_loc, seq_lens, num_computed_tokens=None, softmax_scale: float = 0.0,
+            mode="auto", num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
+            max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0,
+            sliding_window: int = 0, prefix_splits: int = 0):
+    """ca_params_t plus the host metadata arrays and their pointers."""
     bt, bt_p = _host_i32(block_table)
     qsl, qsl_p = _host_i32(query_start_loc)
     sl, sl_p = _host_i32(seq_lens)
-    nc_p = None
+    nc, nc_p = None, None
     if num_computed_tokens is not None:
         nc, nc_p = _host_i32(num_computed_tokens)
     if bt.ndim != 2 or qsl.shape[0] != bt.shape[0] + 1 or sl.shape[0] != bt.shape[0]:
@@ -226,9 +225,53 @@ def cascade_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, pag
     prm.k_scale = float(k_scale)
     prm.v_scale = float(v_scale)
     prm.sliding_window = int(sliding_window)
+    prm.prefix_splits = int(prefix_splits)
+    keep = (bt, qsl, sl, nc)   # the arrays behind the pointers
+    return prm, (bt_p, qsl_p, sl_p, nc_p), keep
+
+
+def cascade_attn_plan(**kw) -> Plan:
+    """Host-only planner (see cascade_attn_plan in the header).
+
+    Keywords: num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+    kv_strides ((page, token-slot, head) element strides of the caches),
+    block_table, query_start_loc, seq_lens, num_computed_tokens (host int32
+    arrays or CPU tensors), and the optional ca_params_t settings
+    softmax_scale, mode, num_cus, heads_per_item, separate_phases,
+    max_levels, kv_dtype, k_scale, v_scale, sliding_window, prefix_splits.
+    """
+    prm, ptrs, keep = _params(**kw)
     h = ctypes.c_void_p(0)
-    _check(load().cascade_attn_plan(ctypes.byref(prm), bt_p, qsl_p, sl_p, nc_p, ctypes.byref(h)))
+    _check(load().cascade_attn_plan(ctypes.byref(prm), *ptrs, ctypes.byref(h)))
+    del keep
     return Plan(h.value)
+
+
+def cascade_attn_autotune(q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse_out,
+                          workspace, iters: int = 10, stream=None, sinks=None, **kw):
+    """Times candidate plans on the device and returns (best Plan, us per run);
+    see cascade_attn_autotune in the header. ``kw`` as for cascade_attn_plan
+    (host metadata and settings); device tensors as for cascade_attn_run."""
+    import torch
+    prm, ptrs, keep = _params(**kw)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    h = ctypes.c_void_p(0)
+    us = ctypes.c_float(0.0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().cascade_attn_autotune(
+        ctypes.byref(prm), *ptrs, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table_d.data_ptr(),
+        query_start_loc_d.data_ptr(), seq_lens_d.data_ptr(), sinks.data_ptr() if sinks is not None else None,
+        out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None,
+        workspace.data_ptr() if workspace is not None else None, ws_bytes, s, int(iters), ctypes.byref(h),
+        ctypes.byref(us)))
+    del keep
+    return Plan(h.value), float(us.value)
+
+
+def cascade_attn_autotune_reset() -> None:
+    load().cascade_attn_autotune_reset()
 
 
 def cascade_attn_plan_info(plan: Plan) -> dict:

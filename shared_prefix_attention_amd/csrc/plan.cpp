@@ -10,7 +10,10 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
+#include <tuple>
 #include <string>
 #include <vector>
 
@@ -255,9 +258,43 @@ static std::vector<GroupCand> find_level1_groups(const int32_t* bt, int32_t n, i
   return out;
 }
 
+// Autotuning table: shape signature -> recorded choice.
+using ShapeKey = std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
+                            int32_t>;
+static std::mutex g_tune_mu;
+static std::map<ShapeKey, TunedChoice> g_tune;
+
+static int32_t log2_bucket(int64_t x) { return x <= 0 ? -1 : 63 - __builtin_clzll((unsigned long long)x); }
+
+static ShapeKey shape_key(const ca_plan& pl) {
+  const int64_t mean_rest = (pl.sum_seq - (int64_t)pl.prefix_len * pl.num_reqs) / std::max(1, pl.num_reqs);
+  return ShapeKey{pl.num_reqs, pl.hq, pl.hkv, pl.d, pl.kv_fp8, pl.window, log2_bucket(pl.prefix_len),
+                  log2_bucket(pl.total_q), log2_bucket(pl.max_q_len), log2_bucket(mean_rest),
+                  std::min(pl.cand_groups, 8)};
+}
+
+void tune_record(const ca_plan& pl, const TunedChoice& c) {
+  if (c.mode == CA_MODE_AUTO) return;   // a recorded choice always fixes the path
+  std::lock_guard<std::mutex> g(g_tune_mu);
+  g_tune[shape_key(pl)] = c;
+}
+
+static bool tune_lookup(const ca_plan& pl, TunedChoice* c) {
+  std::lock_guard<std::mutex> g(g_tune_mu);
+  const auto it = g_tune.find(shape_key(pl));
+  if (it == g_tune.end()) return false;
+  *c = it->second;
+  return true;
+}
+
 }  // namespace ca
 
 using namespace ca;
+
+extern "C" void cascade_attn_autotune_reset(void) {
+  std::lock_guard<std::mutex> g(g_tune_mu);
+  g_tune.clear();
+}
 
 extern "C" const char* cascade_attn_last_error(void) { return g_err.c_str(); }
 
@@ -302,6 +339,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.max_levels < 0 || p.max_levels > 2) return fail(CA_EINVAL, "max_levels must be 0, 1 or 2");
   if (p.kv_dtype != CA_KV_BF16 && p.kv_dtype != CA_KV_FP8_E4M3) return fail(CA_EINVAL, "unknown kv_dtype");
   if (p.sliding_window < 0) return fail(CA_EINVAL, "sliding_window must be >= 0");
+  if (p.prefix_splits < 0) return fail(CA_EINVAL, "prefix_splits must be >= 0");
   if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
   if (p.kv_dtype == CA_KV_FP8_E4M3) {
     if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
@@ -365,6 +403,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
 
   int64_t sum_seq = 0;
   for (int32_t r = 0; r < n; ++r) sum_seq += seq_lens[r];
+  pl->sum_seq = sum_seq;
   pl->kv_tokens_noncascade = sum_seq;
   pl->kv_tokens_cascade = plen + (sum_seq - plen * n);
 
@@ -399,8 +438,17 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->prefix_len = (int32_t)plen;
     double pre_us = 0.0;
     pre = choose_prefix(*pl, cus, cm, &pre_us);
+    if (p.prefix_splits > 0) {   // explicit split count (e.g. from the autotuner)
+      const int64_t ntiles = cdiv(plen, kTileKeys);
+      const int64_t tiles_per = std::min<int64_t>(cdiv(ntiles, std::min<int64_t>(p.prefix_splits, ntiles)),
+                                                  kMaxItemTokens / kTileKeys);
+      pre.splits = (int32_t)cdiv(ntiles, tiles_per);
+      pre.split_tokens = (int32_t)(tiles_per * kTileKeys);
+    }
     std::vector<GroupCand> groups;
-    if (p.max_levels != 1) groups = find_level1_groups(bt, n, stride, seq_lens, qsl, ps, pl->common_blocks, plen);
+    groups = find_level1_groups(bt, n, stride, seq_lens, qsl, ps, pl->common_blocks, plen);
+    pl->cand_groups = (int32_t)groups.size();   // part of the shape, whether used or not
+    if (p.max_levels == 1) groups.clear();
     double t_grp = 0.0;
     int64_t group_tokens = 0;
     if (!groups.empty()) {
@@ -505,6 +553,20 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   } else {
     pl->ws_lse_offset = 0;
     pl->workspace_bytes = 0;
+  }
+  // A choice the autotuner recorded for this shape replaces AUTO's, unless
+  // the caller fixed one of the tuned settings.
+  TunedChoice tc;
+  if (p.mode == CA_MODE_AUTO && p.prefix_splits == 0 && p.heads_per_item == 0 && p.max_levels == 0 &&
+      tune_lookup(*pl, &tc) && tc.mode != CA_MODE_AUTO) {
+    ca_params_t q2 = p;
+    q2.mode = tc.mode;
+    q2.prefix_splits = tc.prefix_splits;
+    q2.heads_per_item = tc.heads_per_item;
+    q2.max_levels = tc.max_levels;
+    q2.num_cus = cus;
+    delete pl;
+    return cascade_attn_plan(&q2, bt, qsl, seq_lens, num_computed, out_plan);
   }
   *out_plan = pl;
   return CA_OK;

@@ -77,6 +77,8 @@ struct ca_plan {
   int64_t ws_lse_offset = 0;  // byte offset of the partial LSE array
   int64_t workspace_bytes = 0;
 
+  int64_t sum_seq = 0;         // shape signature inputs (autotuning table)
+  int32_t cand_groups = 0;     // second-level groups the detector found (taken or not)
   int64_t kv_tokens_cascade = 0;
   int64_t kv_tokens_noncascade = 0;
   float est_us_cascade = 0.f, est_us_noncascade = 0.f;
@@ -84,4 +86,13 @@ struct ca_plan {
 
 namespace ca {
 void set_error(const std::string& msg);
+
+// Choice recorded by the autotuner for a batch shape (ca_params_t fields).
+struct TunedChoice {
+  int32_t mode = CA_MODE_AUTO;
+  int32_t prefix_splits = 0;
+  int32_t heads_per_item = 0;
+  int32_t max_levels = 0;
+};
+void tune_record(const ca_plan& pl, const TunedChoice& c);
 }

@@ -351,3 +351,121 @@ extern "C" ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts) {
   }
   return st;
 }
+
+// ------------------------------------------------------------ autotuning
+
+extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const int32_t* block_table_h,
+                                             const int32_t* query_start_loc_h, const int32_t* seq_lens_h,
+                                             const int32_t* num_computed_tokens_h, const void* q, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_table_d,
+                                             const int32_t* query_start_loc_d, const int32_t* seq_lens_d,
+                                             const float* sinks_d, void* out, float* lse_out, void* workspace,
+                                             size_t workspace_bytes, void* stream, int32_t iters,
+                                             ca_plan_t* out_plan, float* out_us) {
+  if (!params || !out_plan) return fail(CA_EINVAL, "null pointer argument");
+  *out_plan = nullptr;
+  if (iters < 1 || iters > 1000) return fail(CA_EINVAL, "iters must be in [1, 1000]");
+  ca_params_t base_p = *params;
+  base_p.mode = CA_MODE_AUTO;
+  base_p.prefix_splits = 0;
+  base_p.heads_per_item = 0;
+  base_p.max_levels = 0;
+  ca_plan_t base = nullptr;
+  ca_status_t st = cascade_attn_plan(&base_p, block_table_h, query_start_loc_h, seq_lens_h, num_computed_tokens_h,
+                                     &base);
+  if (st != CA_OK) return st;
+  // The shape signature is the AUTO plan's, whatever the table says: plan
+  // it once more without the table's influence.
+  std::vector<TunedChoice> cands;
+  cands.push_back({CA_MODE_FORCE_OFF, 0, 0, 0});
+  if (base->prefix_len > 0 && base->window == 0) {
+    ca_params_t pp = base_p;
+    pp.mode = CA_MODE_FORCE_ON;
+    pp.max_levels = 1;   // any explicit setting bypasses the table
+    ca_plan_t on = nullptr;
+    st = cascade_attn_plan(&pp, block_table_h, query_start_loc_h, seq_lens_h, num_computed_tokens_h, &on);
+    if (st != CA_OK) {
+      cascade_attn_plan_destroy(base);
+      return st;
+    }
+    const int32_t s0 = on->prefix.splits;
+    const int32_t h0 = on->suffix.heads_per_item;
+    cascade_attn_plan_destroy(on);
+    std::vector<int32_t> splits{s0};
+    if (s0 >= 2) splits.push_back(s0 / 2);
+    splits.push_back(s0 * 2);
+    std::vector<int32_t> heads{0};
+    if (h0 > 1) heads.push_back(1);
+    std::vector<int32_t> levels{0};
+    if (base->cand_groups > 0) levels.push_back(1);
+    for (int32_t sp : splits)
+      for (int32_t hd : heads)
+        for (int32_t lv : levels) cands.push_back({CA_MODE_FORCE_ON, sp, hd, lv});
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    cascade_attn_plan_destroy(base);
+    return fail(CA_EHIP, "event creation failed");
+  }
+  ca_plan_t best = nullptr;
+  TunedChoice best_c;
+  float best_us = 0.f;
+  for (const TunedChoice& c : cands) {
+    ca_params_t cp = base_p;
+    cp.mode = c.mode;
+    cp.prefix_splits = c.prefix_splits;
+    cp.heads_per_item = c.heads_per_item;
+    // an explicit level count keeps the table out of the candidate's plan
+    cp.max_levels = c.max_levels > 0 ? c.max_levels : 2;
+    ca_plan_t cand = nullptr;
+    if (cascade_attn_plan(&cp, block_table_h, query_start_loc_h, seq_lens_h, num_computed_tokens_h, &cand) != CA_OK)
+      continue;
+    if ((int64_t)workspace_bytes < cand->workspace_bytes) {
+      cascade_attn_plan_destroy(cand);
+      continue;
+    }
+    st = CA_OK;
+    for (int i = 0; i < 2 && st == CA_OK; ++i)
+      st = cascade_attn_run(cand, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, sinks_d, out,
+                            lse_out, workspace, workspace_bytes, stream);
+    if (st == CA_OK && hipEventRecord(e0, s) != hipSuccess) st = fail(CA_EHIP, "event record failed");
+    for (int i = 0; i < iters && st == CA_OK; ++i)
+      st = cascade_attn_run(cand, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, sinks_d, out,
+                            lse_out, workspace, workspace_bytes, stream);
+    float ms = 0.f;
+    if (st == CA_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                        hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      st = fail(CA_EHIP, "event timing failed");
+    if (st != CA_OK) {
+      cascade_attn_plan_destroy(cand);
+      cascade_attn_plan_destroy(best);
+      cascade_attn_plan_destroy(base);
+      (void)hipEventDestroy(e0);
+      (void)hipEventDestroy(e1);
+      return st;
+    }
+    const float us = ms * 1000.f / iters;
+    if (!best || us < best_us) {
+      cascade_attn_plan_destroy(best);
+      best = cand;
+      best_c = c;
+      best_c.max_levels = cp.max_levels;
+      best_us = us;
+    } else {
+      cascade_attn_plan_destroy(cand);
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (!best) {
+    cascade_attn_plan_destroy(base);
+    return fail(CA_EWORKSPACE, "no candidate plan fits the workspace");
+  }
+  tune_record(*base, best_c);
+  cascade_attn_plan_destroy(base);
+  *out_plan = best;
+  if (out_us) *out_us = best_us;
+  return CA_OK;
+}

@@ -385,3 +385,17 @@ def test_sliding_window_decisions():
     with pytest.raises(spa.CascadeAttnError) as e:
         _plan(wd, mode="auto", sliding_window=-1)
     assert e.value.status == _lib.CA_EINVAL
+
+
+def test_prefix_split_override():
+    """An explicit prefix split count is applied, limited to one 64-key tile
+    per split and raised so no item exceeds 8192 keys."""
+    wd = workloads.make_batch(workloads.get("worked_decode"))       # 4096-token prefix: 64 tiles
+    assert _plan(wd, mode="on", prefix_splits=4).info["prefix_splits"] == 4
+    assert _plan(wd, mode="on", prefix_splits=1000).info["prefix_splits"] == 64
+    ld = workloads.make_batch(workloads.get("long_doc"))            # 32768 tokens: at least 4 splits
+    assert _plan(ld, mode="on", prefix_splits=1).info["prefix_splits"] == 4
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _plan(wd, mode="on", prefix_splits=-1)
+    assert e.value.status == _lib.CA_EINVAL
+    spa.cascade_attn_autotune_reset()      # host-only: callable without a device
