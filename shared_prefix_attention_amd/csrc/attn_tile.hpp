@@ -109,6 +109,11 @@ __device__ __forceinline__ int group_of_request(const GroupTable& gt, int req) {
 
 constexpr int kMaxItemPages = 512;
 
+// Online softmax: the per-row reference max (log2 domain) is raised only when
+// a stage's max exceeds it by more than this many units, so the exponentials
+// taken against it lie in (0, 2^kRescaleSlack].
+constexpr float kRescaleSlack = 8.f;
+
 // ESZ: bytes per cache element, 2 (bf16) or 1 (fp8).
 template <int D, int NS, int SK, int ESZ = 2>
 struct TileSmem {
@@ -820,9 +825,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         for (int kb = 0; kb < NKB; ++kb)
           tmax = vmax(tmax, vmax(vmax(s[kb][rb][0], s[kb][rb][1]), vmax(s[kb][rb][2], s[kb][rb][3])));
         tmax = wave_max_across_quads(tmax) * a.scale_log2;
-        const float m_new = vmax(m_run[rb], tmax);
+        // The reference max m_run only moves when the stage's max passes it
+        // by more than kRescaleSlack (so exponentials stay <= 2^slack, exact
+        // in fp32 and bf16 alike): o and l need rescaling on few stages. The
+        // choice is per row; a skipped rescale is a product with 1.
+        const bool bump = tmax > m_run[rb] + kRescaleSlack;   // also -inf -> finite
+        const float m_new = bump ? tmax : m_run[rb];
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
+        const float alpha = bump ? __builtin_amdgcn_exp2f(m_run[rb] - m_use) : 1.f;
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -836,8 +846,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         }
         l_run[rb] = l_run[rb] * alpha + psum;
         m_run[rb] = m_new;
-        // the running max of most rows stops moving after a few stages
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+        // most stages move no row's reference max: the wave skips the product
+        if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) o[db][rb] *= alpha;
         }

@@ -239,3 +239,33 @@ def test_window_with_sinks():
     ref_o, ref_l = oracle_ref(b, window=33, sinks=z)
     out, lse, _ = run(DeviceBatch(b), mode="auto", sliding_window=33, sinks=z)
     assert_close(out, lse, ref_o, ref_l, what="prefill_mix/W33/sinks")
+
+
+def _rising_keys(b, per_token):
+    """Scales every cached key by 1 + t * per_token, t its position (shared
+    pages hold the same positions in every request), so each row's running
+    maximum keeps rising by many units of log2 along the sequence."""
+    f = torch.ones(b.k_cache.shape[0], b.k_cache.shape[1])
+    ps = b.workload.page_size
+    for r in range(b.workload.num_reqs):
+        n = int(b.seq_lens[r])
+        t = torch.arange(n)
+        pages = b.block_table[r, t // ps].long()
+        f[pages, t % ps] = 1.0 + t.float() * per_token
+    b.k_cache = (b.k_cache.float() * f[:, :, None, None]).to(torch.bfloat16)
+    return b
+
+
+@pytest.mark.parametrize("mode", ["on", "off"])
+@pytest.mark.parametrize("name,per_token", [("tiny_decode", 1 / 16), ("prefill_mix", 1 / 16),
+                                            ("long_prefix_split", 1 / 256), ("d64_gqa", 1 / 8),
+                                            ("many_rows", 1 / 32)])
+def test_rising_row_maximum(name, per_token, mode):
+    """Scores whose maximum grows by far more than the online softmax's
+    rescale slack over a row's keys: the reference maximum is raised many
+    times inside one work item and across splits."""
+    log(f"[parity] {name} rising keys x{per_token:.4f}/token mode={mode}")
+    b = _rising_keys(workloads.make_batch(SMALL[name]), per_token)
+    ref_o, ref_l = oracle_ref(b)
+    out, lse, _ = run(DeviceBatch(b), mode=mode)
+    assert_close(out, lse, ref_o, ref_l, what=f"{name}/rising/{mode}")
