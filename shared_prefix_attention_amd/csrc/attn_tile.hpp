@@ -283,6 +283,13 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   constexpr int OPS = 2 * BLK_PER_WAVE;   // vector-memory ops per wave per stage
   constexpr int NKB = SK / 16 / KG;       // 16-key blocks per wave per stage
   static_assert((NKB == 1 || NKB == 2 || NKB == 4) && SK % (16 * KG) == 0, "each wave needs 1, 2 or 4 16-key blocks");
+  // Decode shape (one row wave, the stage's keys split over the W waves):
+  // wave w reads exactly the 16 keys of each stage that its own DMA writes,
+  // so its pipeline needs no work-group barrier, and it refills a buffer as
+  // soon as it holds that stage's K and V fragments in registers (one more
+  // stage in flight than a shared buffer allows).
+  constexpr bool PRIV = RW == 1;
+  static_assert(!PRIV || (KG == W && NKB == 1 && SK / W == 16), "per-wave pipelines need one 16-key block per wave");
   constexpr int ROWB = D * ESZ;           // LDS bytes per key row
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
   using SM = TileSmem<D, NS, SK, ESZ>;
@@ -699,16 +706,54 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   for (int u = 0; u < U; ++u) {
     // stages issued after stage u so far: the prologue filled NS buffers,
     // and iteration i >= 1 issued stage i + NS - 1
-    wait_stage(u == 0 ? min(NS - 1, U - 1) : min(NS - 2, U - 1 - u));
-    block_barrier();
-    // the next stage goes into the buffer every wave finished with before
-    // this barrier
-    if (u >= 1 && u + NS - 1 < U) issue_next();
+    // Per-wave pipelines: stages u .. u + NS - 1 are in flight here, and
+    // stage u + NS goes into stage u's buffer once its fragments are read,
+    // except after a head's last tile, whose buffer holds the key-group
+    // combine (then it is issued after the combine).
+    const bool refill = PRIV && u + NS < U;
+    const bool refill_now = refill && t != n_tiles - 1;
+    if constexpr (PRIV) {
+      wait_stage(min(NS - 1, U - 1 - u));
+      if (refill_now && !wave_active) issue_next();
+    } else {
+      wait_stage(u == 0 ? min(NS - 1, U - 1) : min(NS - 2, U - 1 - u));
+      block_barrier();
+      // the next stage goes into the buffer every wave finished with before
+      // this barrier
+      if (u >= 1 && u + NS - 1 < U) issue_next();
+    }
     const uint32_t stage = smem_base + (u % NS) * SM::STAGE_BYTES;
     if (wave_active) {
       const uint32_t sK = stage + kg * NKB * 16 * ROWB;
       const uint32_t sV = stage + SM::TILE_BYTES + kg * NKB * 16 * ROWB;
       const int kt0 = key_begin + t * SK + kg * NKB * 16;   // first key of this wave's group
+      constexpr int NKK = NKB >= 2 ? NKB / 2 : 1;
+      constexpr int VH = (RB >= 2 && NKB >= 2) ? 2 : 1;   // d halves
+      constexpr int DBV = DB / VH;                          // d blocks per half
+      u32x4_t vf[NKB >= 2 ? DBV * NKK : 1];
+      u32x2_t vh[NKB == 1 ? DB : 1];
+      // fp8: raw transpose reads (8 keys of one d column per lane), converted
+      // after the softmax
+      u32x2_t vr8[F8 && NKB >= 2 ? DBV * NKK : 1];
+      u32x2_t vr1[F8 && NKB == 1 ? DB / 2 : 1];
+      // one 16-key block: V^T of the block with the transpose load
+      auto read_v1 = [&]() {
+        if constexpr (F8) {
+#pragma unroll
+          for (int m = 0; m < DB / 2; ++m) vr1[m] = lds_read_tr8(sV + v_off[m]);
+        } else {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) vh[db] = lds_read_tr16(sV + v_off[db]);
+        }
+      };
+      // per-wave pipelines: with K and V in registers the buffer is free
+      auto release = [&]() {
+        if constexpr (PRIV) {
+          if constexpr (F8) reg_fence(vr1);
+          else reg_fence(vh);
+          if (refill_now) issue_next();
+        }
+      };
       // S^T = K Q^T for NKB blocks of 16 keys. All K fragments of the stage
       // are read before one wait; the MFMA chains of the blocks interleave.
       u32x4_t kf[NKB * KC];
@@ -717,7 +762,9 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) kf[kb * KC + kc] = lds_read_b128_kb<ROWB>(sK + k_off[kc], kb);
+        if constexpr (PRIV) read_v1();
         lds_wait_regs(kf);
+        release();
       } else {
         // 16 fp8 of chunk lq + 4p are k-slots of chunks kc = 2p (bytes 0-7)
         // and 2p + 1 (bytes 8-15), the order load_q gives Q
@@ -726,7 +773,9 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int p = 0; p < KC / 2; ++p) kr[kb * (KC / 2) + p] = lds_read_b128_kb<ROWB>(sK + k_off[p], kb);
+        if constexpr (PRIV) read_v1();
         lds_wait_regs(kr);
+        release();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -754,15 +803,6 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       // 16 + 4*lq + j - 4), the map the S^T accumulators give P^T.
       // With two row blocks the fragments are read in two halves of d (the
       // second after the first is consumed) to stay within 256 VGPRs.
-      constexpr int NKK = NKB >= 2 ? NKB / 2 : 1;
-      constexpr int VH = (RB >= 2 && NKB >= 2) ? 2 : 1;   // d halves
-      constexpr int DBV = DB / VH;                          // d blocks per half
-      u32x4_t vf[NKB >= 2 ? DBV * NKK : 1];
-      u32x2_t vh[NKB == 1 ? DB : 1];
-      // fp8: raw transpose reads (8 keys of one d column per lane), converted
-      // after the softmax
-      u32x2_t vr8[F8 && NKB >= 2 ? DBV * NKK : 1];
-      u32x2_t vr1[F8 && NKB == 1 ? DB / 2 : 1];
       auto read_v = [&](int half) {
 #pragma unroll
         for (int i = 0; i < DBV; ++i) {
@@ -789,13 +829,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         }
       };
       if constexpr (NKB == 1) {
-        if constexpr (F8) {
-#pragma unroll
-          for (int m = 0; m < DB / 2; ++m) vr1[m] = lds_read_tr8(sV + v_off[m]);
-        } else {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) vh[db] = lds_read_tr16(sV + v_off[db]);
-        }
+        if constexpr (!PRIV) read_v1();
       } else {
         read_v(0);
       }
@@ -895,6 +929,10 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       const bool more = MH && h + 1 < H;
       if (more) load_q(g0 + h + 1, qn);
       finish_head(g0 + h, u % NS);
+      if (refill) {
+        block_barrier();   // every wave is past the combine in this buffer
+        issue_next();
+      }
       if (more) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
