@@ -112,6 +112,9 @@ typedef struct {
                                   runs the non-cascade path and FORCE_ON fails with CA_EUNSUPPORTED */
   int32_t prefix_splits;       /* 0 = planner's choice; else KV splits of the prefix phase (raised if an
                                   item would exceed 8192 keys, lowered to the prefix's 64-key tiles) */
+  int32_t suffix_order;        /* 0 = per-request work items start longest key range first (batches of
+                                  at most 512 requests; results are identical, only the dispatch
+                                  order changes); 1 = batch order */
 } ca_params_t;
 
 typedef struct {
@@ -134,7 +137,7 @@ typedef struct {
   int32_t level1_splits;               /* KV splits of every group (partial slots of that level) */
   int32_t kv_dtype;                    /* ca_kv_dtype_t of the plan */
   int32_t sliding_window;              /* window applied by the plan (0: none, or it never binds) */
-  int32_t reserved0;
+  int32_t suffix_longest_first;        /* 1 if per-request items start longest key range first */
   int64_t total_q;                     /* T = query_start_loc[N] */
   int64_t workspace_bytes;             /* bytes run() needs (0 = none) */
   int64_t kv_tokens_cascade;           /* prefix + sum of suffixes (positions read by cascade) */

@@ -107,6 +107,15 @@ __device__ __forceinline__ int group_of_request(const GroupTable& gt, int req) {
   return (lo > 0 && req < gt.req_end[lo - 1]) ? lo - 1 : -1;
 }
 
+// Dispatch order of the per-request work items: request slot j runs request
+// req[j] (n = 0: batch order, else n = num_reqs). The planner starts the
+// longest key ranges first, so a launch ends on short items. Kernel argument.
+constexpr int kMaxOrderedReqs = 512;
+struct ReqOrder {
+  int32_t n;
+  uint16_t req[kMaxOrderedReqs];
+};
+
 constexpr int kMaxItemPages = 512;
 
 // Online softmax: the per-row reference max (log2 domain) is raised only when
@@ -268,7 +277,8 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
 // WIN: the item may apply a sliding window and attention sinks (the
 // stand-alone kernel; the cascade launch has neither).
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN>
-__device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const int bid, uint8_t* smem) {
+__device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const ReqOrder& ro, const int bid,
+                                          uint8_t* smem) {
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
   constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
@@ -352,7 +362,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     rest /= a.mtiles;
     const int groups = a.hkv / H;
     g0 = (rest % groups) * H;
-    req = rest / groups;
+    req = ro.n > 0 ? ro.req[rest / groups] : rest / groups;
     // a request in a group starts after the group's shared positions
     grp = gt.n > 0 ? group_of_request(gt, req) : -1;
     key_begin = (grp >= 0 ? gt.key_end[grp] : a.key_start) + c * split_tokens;
@@ -949,9 +959,10 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 }
 
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
-__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt) {
+__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt,
+                                                                  const ReqOrder ro) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
-  attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, blockIdx.x, smem);
+  attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, ro, blockIdx.x, smem);
 }
 
 // One launch for all cascade phases: work-groups [0, n_prefix) run prefix
@@ -963,16 +974,17 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
 template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK, bool F8>
 __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs ga, const TileArgs sa,
                                                              const int n_prefix, const int n_group,
-                                                             const GroupTable gt) {
+                                                             const GroupTable gt, const ReqOrder ro) {
   static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
   constexpr int ESZ = F8 ? 1 : 2;
   constexpr int PB = TileSmem<D, PNS, PSK, ESZ>::BYTES, SB = TileSmem<D, SNS, SSK, ESZ>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(pa, gt, bid, smem);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(pa, gt, ro, bid, smem);
   else if (bid < n_prefix + n_group)
-    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(ga, gt, bid - n_prefix, smem);
-  else attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false>(sa, gt, bid - n_prefix - n_group, smem);
+    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(ga, gt, ro, bid - n_prefix, smem);
+  else
+    attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false>(sa, gt, ro, bid - n_prefix - n_group, smem);
 }
 
 }  // namespace ca

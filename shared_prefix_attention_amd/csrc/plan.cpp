@@ -152,6 +152,26 @@ static PhaseTile choose_suffix(const ca_plan& pl, int32_t cus, bool fill) {
   return t;
 }
 
+// Per-request work items start with the longest key ranges (in 64-key
+// tiles; ties keep batch order): greedy list scheduling that leaves the short
+// items for the end of the launch, where they fill the CUs freed by the long
+// ones. Only the dispatch order changes, never an item's work.
+static void order_requests(ca_plan& pl, const ca_params_t& p, const int32_t* seq_lens, const int64_t* kstart) {
+  pl.order_n = 0;
+  const int32_t n = pl.num_reqs;
+  if (p.suffix_order != 0 || n > kOrderCapacity) return;
+  std::vector<int64_t> tiles(n);
+  for (int32_t r = 0; r < n; ++r) tiles[r] = cdiv(std::max<int64_t>(0, seq_lens[r] - kstart[r]), kTileKeys);
+  std::vector<int32_t> idx(n);
+  for (int32_t r = 0; r < n; ++r) idx[r] = r;
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return tiles[a] > tiles[b]; });
+  bool identity = true;
+  for (int32_t r = 0; r < n; ++r) identity = identity && idx[r] == r;
+  if (identity) return;
+  pl.order_n = n;
+  for (int32_t r = 0; r < n; ++r) pl.order[r] = (uint16_t)idx[r];
+}
+
 // Decode-shaped items may run several consecutive KV heads of one request as
 // one stage pipeline (same pages and key range). Worth it when that keeps the
 // whole cascade launch within two resident work-groups per CU (no item waits
@@ -340,6 +360,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.kv_dtype != CA_KV_BF16 && p.kv_dtype != CA_KV_FP8_E4M3) return fail(CA_EINVAL, "unknown kv_dtype");
   if (p.sliding_window < 0) return fail(CA_EINVAL, "sliding_window must be >= 0");
   if (p.prefix_splits < 0) return fail(CA_EINVAL, "prefix_splits must be >= 0");
+  if (p.suffix_order != 0 && p.suffix_order != 1) return fail(CA_EINVAL, "suffix_order must be 0 or 1");
   if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
   if (p.kv_dtype == CA_KV_FP8_E4M3) {
     if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
@@ -532,6 +553,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->separate_phases = p.separate_phases;
     pl->num_slots = pre.splits + lvl1.splits + suf.splits;
     pl->direct_out = false;
+    order_requests(*pl, p, seq_lens, kstart.data());
   } else {
     pl->key_start = 0;
     pl->max_suffix_len = max_seq;
@@ -543,6 +565,8 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->separate_phases = 0;
     pl->num_slots = nc.splits > 1 ? nc.splits : 0;
     pl->direct_out = nc.splits == 1;
+    const std::vector<int64_t> zero(n, 0);
+    order_requests(*pl, p, seq_lens, zero.data());
   }
   pl->slot_elems = total_q * pl->hq * pl->d;
   if (pl->num_slots > 0) {
@@ -594,6 +618,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->level1_splits = pl->lvl1.splits;
   out->kv_dtype = pl->kv_fp8 ? CA_KV_FP8_E4M3 : CA_KV_BF16;
   out->sliding_window = pl->window;
+  out->suffix_longest_first = pl->order_n > 0 ? 1 : 0;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

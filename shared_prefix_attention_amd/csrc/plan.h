@@ -34,6 +34,9 @@ constexpr int kMaxItemTokens = 512 * 16;
 // beyond the batch-wide prefix. At most kMaxLevel1Groups (they travel to the
 // kernels as launch arguments).
 constexpr int kMaxLevel1Groups = 64;
+// Requests whose work-item order a plan can set (kernel-argument table).
+constexpr int kOrderCapacity = 512;
+
 struct Level1 {
   int32_t n = 0;                               // groups in use
   int32_t splits = 0;                          // KV splits of every group
@@ -79,6 +82,10 @@ struct ca_plan {
 
   int64_t sum_seq = 0;         // shape signature inputs (autotuning table)
   int32_t cand_groups = 0;     // second-level groups the detector found (taken or not)
+  // dispatch order of the per-request work items: the j-th request slot runs
+  // request order[j] (order_n = 0: batch order; else order_n = num_reqs)
+  int32_t order_n = 0;
+  uint16_t order[ca::kOrderCapacity] = {};
   int64_t kv_tokens_cascade = 0;
   int64_t kv_tokens_noncascade = 0;
   float est_us_cascade = 0.f, est_us_noncascade = 0.f;

@@ -24,6 +24,7 @@ namespace {
 
 enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_PREFIX = 4, K_SUFFIX = 5, K_LEVEL1 = 6, K_KINDS = 7 };
 static_assert(kMaxGroups == kMaxLevel1Groups, "group table size");
+static_assert(kOrderCapacity == kMaxOrderedReqs, "request order table size");
 static_assert(K_KINDS == CA_PROFILE_KINDS, "profile kinds");
 
 struct Profiler {
@@ -70,23 +71,23 @@ ca_status_t check_launch(const char* what) {
 }
 
 template <int D, int RB, int RW, int KG, int NS, bool F8>
-void launch_tile(const TileArgs& args, const GroupTable& gt, int grid, hipStream_t s, int kind) {
+void launch_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, int grid, hipStream_t s, int kind) {
   launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, (KG > 1) && !F8, F8>, dim3(grid), dim3(64 * RW * KG), s, args,
-         gt);
+         gt, ro);
 }
 
 // bf16 caches: 2 or 4 stages of 64 keys; fp8 caches (head_dim 128 only):
 // 4 stages, the same 64 KB of LDS.
 template <int D, int RB, int RW, int KG>
-void launch_tile_ns(const TileArgs& args, const GroupTable& gt, int ns, bool f8, int grid, hipStream_t s, int kind) {
+void launch_tile_ns(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, int ns, bool f8, int grid, hipStream_t s, int kind) {
   if constexpr (D == 128) {
     if (f8) {
-      launch_tile<D, RB, RW, KG, 4, true>(args, gt, grid, s, kind);
+      launch_tile<D, RB, RW, KG, 4, true>(args, gt, ro, grid, s, kind);
       return;
     }
   }
-  if (ns == 4) launch_tile<D, RB, RW, KG, 4, false>(args, gt, grid, s, kind);
-  else launch_tile<D, RB, RW, KG, 2, false>(args, gt, grid, s, kind);
+  if (ns == 4) launch_tile<D, RB, RW, KG, 4, false>(args, gt, ro, grid, s, kind);
+  else launch_tile<D, RB, RW, KG, 2, false>(args, gt, ro, grid, s, kind);
 }
 
 bool item_ok(const PhaseTile& ph) { return ph.split_tokens > 0 && ph.split_tokens <= kMaxItemTokens && ph.split_tokens % kTileKeys == 0; }
@@ -101,16 +102,16 @@ int shape_id(const PhaseTile& ph) {
 }
 
 template <int D>
-ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const PhaseTile& ph, int64_t grid, bool f8,
+ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const PhaseTile& ph, int64_t grid, bool f8,
                      hipStream_t s, int kind) {
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(ph)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   if (f8 && (D != 128 || ph.stages != 4)) return fail(CA_EINVAL, "fp8 plan needs head_dim 128 and 4 stages");
   switch (shape_id(ph)) {
-    case 0: launch_tile_ns<D, 1, 4, 1>(args, gt, ph.stages, f8, (int)grid, s, kind); break;
-    case 1: launch_tile_ns<D, 2, 4, 1>(args, gt, ph.stages, f8, (int)grid, s, kind); break;
-    case 2: launch_tile_ns<D, 1, 1, 4>(args, gt, ph.stages, f8, (int)grid, s, kind); break;
+    case 0: launch_tile_ns<D, 1, 4, 1>(args, gt, ro, ph.stages, f8, (int)grid, s, kind); break;
+    case 1: launch_tile_ns<D, 2, 4, 1>(args, gt, ro, ph.stages, f8, (int)grid, s, kind); break;
+    case 2: launch_tile_ns<D, 1, 1, 4>(args, gt, ro, ph.stages, f8, (int)grid, s, kind); break;
     default: return fail(CA_EINVAL, "unsupported work-group shape in plan");
   }
   return check_launch("attention kernel launch");
@@ -120,29 +121,29 @@ ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const PhaseTile
 // of bf16, or 4 of fp8.
 template <int D, int P, int S, bool F8>
 void launch_phases(const TileArgs& pa, const TileArgs& ga, const TileArgs& sa, int n_prefix, int n_group,
-                   const GroupTable& gt, int grid, hipStream_t s) {
+                   const GroupTable& gt, const ReqOrder& ro, int grid, hipStream_t s) {
   constexpr int PRB = P == 1 ? 2 : 1;
   constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
   constexpr int NS = F8 ? 4 : 2;
   launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, NS, 64, 1, SRW, SKG, NS, 64, F8>, dim3(grid), dim3(256), s,
-         pa, ga, sa, n_prefix, n_group, gt);
+         pa, ga, sa, n_prefix, n_group, gt, ro);
 }
 
 template <int D, bool F8>
 void launch_phases_shapes(int pid, int sid, const TileArgs& pa, const TileArgs& ga, const TileArgs& sa, int np,
-                          int ng, const GroupTable& gt, int grid, hipStream_t s) {
+                          int ng, const GroupTable& gt, const ReqOrder& ro, int grid, hipStream_t s) {
   if (sid == 0) {
-    if (pid == 0) launch_phases<D, 0, 0, F8>(pa, ga, sa, np, ng, gt, grid, s);
-    else launch_phases<D, 1, 0, F8>(pa, ga, sa, np, ng, gt, grid, s);
+    if (pid == 0) launch_phases<D, 0, 0, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
+    else launch_phases<D, 1, 0, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
   } else {
-    if (pid == 0) launch_phases<D, 0, 2, F8>(pa, ga, sa, np, ng, gt, grid, s);
-    else launch_phases<D, 1, 2, F8>(pa, ga, sa, np, ng, gt, grid, s);
+    if (pid == 0) launch_phases<D, 0, 2, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
+    else launch_phases<D, 1, 2, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
   }
 }
 
 template <int D>
 ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix, const TileArgs& ga,
-                       int64_t n_group, const GroupTable& gt, const TileArgs& sa, const PhaseTile& sp,
+                       int64_t n_group, const GroupTable& gt, const ReqOrder& ro, const TileArgs& sa, const PhaseTile& sp,
                        int64_t n_suffix, bool f8, hipStream_t s) {
   if (n_prefix + n_group + n_suffix > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(pp) || !item_ok(sp)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
@@ -153,10 +154,10 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
   const int grid = (int)(n_prefix + n_group + n_suffix);
   const int np = (int)n_prefix, ng = (int)n_group;
   if constexpr (D == 128) {
-    if (f8) launch_phases_shapes<D, true>(pid, sid, pa, ga, sa, np, ng, gt, grid, s);
-    else launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, grid, s);
+    if (f8) launch_phases_shapes<D, true>(pid, sid, pa, ga, sa, np, ng, gt, ro, grid, s);
+    else launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, ro, grid, s);
   } else {
-    launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, grid, s);
+    launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, ro, grid, s);
   }
   return check_launch("cascade phases kernel launch");
 }
@@ -218,6 +219,12 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     if (L.split_tokens[j] <= 0 || L.split_tokens[j] > kMaxItemTokens || L.split_tokens[j] % kTileKeys)
       return fail(CA_EINVAL, "group work item exceeds the per-item KV limit");
 
+  // dispatch order of the per-request items (n = 0: batch order)
+  ReqOrder ro{};
+  ro.n = pl->order_n;
+  if (ro.n != 0 && ro.n != pl->num_reqs) return fail(CA_EINVAL, "request order does not cover the batch");
+  for (int j = 0; j < ro.n; ++j) ro.req[j] = pl->order[j];
+
   const bool f8 = pl->kv_fp8 != 0;
   if (f8 && pl->suffix.heads_per_item != 1) return fail(CA_EINVAL, "fp8 plans run one KV head per item");
 
@@ -259,14 +266,14 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     ga.direct = 0;
     const int64_t n_group = gt.n > 0 ? gt.item_begin[gt.n] : 0;
     if (pl->separate_phases) {
-      st = run_tile<D>(pa, gt, pl->prefix, n_prefix, f8, s, K_PREFIX);
-      if (st == CA_OK) st = run_tile<D>(ga, gt, pl->prefix, n_group, f8, s, K_LEVEL1);
-      if (st == CA_OK) st = run_tile<D>(sa, gt, pl->suffix, n_suffix, f8, s, K_SUFFIX);
+      st = run_tile<D>(pa, gt, ro, pl->prefix, n_prefix, f8, s, K_PREFIX);
+      if (st == CA_OK) st = run_tile<D>(ga, gt, ro, pl->prefix, n_group, f8, s, K_LEVEL1);
+      if (st == CA_OK) st = run_tile<D>(sa, gt, ro, pl->suffix, n_suffix, f8, s, K_SUFFIX);
     } else {
-      st = run_phases<D>(pa, pl->prefix, n_prefix, ga, n_group, gt, sa, pl->suffix, n_suffix, f8, s);
+      st = run_phases<D>(pa, pl->prefix, n_prefix, ga, n_group, gt, ro, sa, pl->suffix, n_suffix, f8, s);
     }
   } else {
-    st = run_tile<D>(sa, gt, pl->suffix, n_suffix, f8, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
+    st = run_tile<D>(sa, gt, ro, pl->suffix, n_suffix, f8, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
   }
   if (st != CA_OK) return st;
   if (!pl->direct_out) {

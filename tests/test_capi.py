@@ -399,3 +399,20 @@ def test_prefix_split_override():
         _plan(wd, mode="on", prefix_splits=-1)
     assert e.value.status == _lib.CA_EINVAL
     spa.cascade_attn_autotune_reset()      # host-only: callable without a device
+
+
+def test_suffix_order():
+    """Per-request work items of a ragged batch start with the longest key
+    range; batches whose requests already come longest first, suffix_order=1
+    and batches of more than 512 requests keep batch order."""
+    sc = workloads.make_batch(workloads.get("self_consistency"))   # suffixes U[1, 1024]
+    assert _plan(sc, mode="on").info["suffix_longest_first"] == 1
+    assert _plan(sc, mode="off").info["suffix_longest_first"] == 1
+    assert _plan(sc, mode="on", suffix_order=1).info["suffix_longest_first"] == 0
+    wd = workloads.make_batch(workloads.get("worked_decode"))      # every suffix 128 tokens
+    assert _plan(wd, mode="on").info["suffix_longest_first"] == 0
+    big = workloads.make_batch(workloads.Workload("many_requests", 600, 256, (1, 200), (1, 1), 1, 1, 64, seed=77))
+    assert _plan(big, mode="on").info["suffix_longest_first"] == 0
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _plan(wd, mode="on", suffix_order=2)
+    assert e.value.status == _lib.CA_EINVAL

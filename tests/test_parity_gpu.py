@@ -269,3 +269,20 @@ def test_rising_row_maximum(name, per_token, mode):
     ref_o, ref_l = oracle_ref(b)
     out, lse, _ = run(DeviceBatch(b), mode=mode)
     assert_close(out, lse, ref_o, ref_l, what=f"{name}/rising/{mode}")
+
+
+@pytest.mark.parametrize("name,mode", [("prefill_mix", "on"), ("prefill_mix", "off"), ("gqa8_outliers", "on"),
+                                       ("gqa8_outliers", "off"), ("nested_decode", "off"), ("nested_capped", "on"),
+                                       ("fp8_gqa8_outliers", "on"), ("fp8_prefill", "off")])
+def test_longest_first_order_changes_no_result(name, mode):
+    """Starting per-request items longest first only reorders the dispatch:
+    outputs and LSE are bitwise those of batch order."""
+    log(f"[order] {name} mode={mode}")
+    b = workloads.make_batch(SMALL[name])
+    db = DeviceBatch(b)
+    o1, l1, i1 = run(db, mode=mode)
+    o2, l2, i2 = run(db, mode=mode, suffix_order=1)
+    assert i1["suffix_longest_first"] == 1 and i2["suffix_longest_first"] == 0
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ref_o, ref_l = oracle_ref(b)
+    assert_close(o1, l1, ref_o, ref_l, what=f"{name}/{mode}/longest-first")
