@@ -115,6 +115,9 @@ typedef struct {
   int32_t suffix_order;        /* 0 = per-request work items start longest key range first (batches of
                                   at most 512 requests; results are identical, only the dispatch
                                   order changes); 1 = batch order */
+  int32_t partials_fp32;       /* partial outputs of the phases before the merge: 0 = bf16 (the
+                                  attention dtype, as [p2] section 8 Step 5 merges the two phases'
+                                  outputs), 1 = fp32; partial LSEs are fp32 either way */
 } ca_params_t;
 
 typedef struct {
@@ -127,7 +130,7 @@ typedef struct {
   int32_t suffix_chunks;               /* KV chunks per request of the suffix (or only) phase */
   int32_t suffix_chunk_tokens;         /* tokens per chunk */
   int32_t suffix_kernel;               /* 0 = tiled kernel, 1 = decode kernel */
-  int32_t num_partial_slots;           /* fp32 partial states per (token, head) */
+  int32_t num_partial_slots;           /* partial states per (token, head) */
   int32_t prefix_stages;               /* LDS pipeline depth of the prefix kernel */
   int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
   int32_t merge_in_suffix;             /* 1: the suffix kernel merges and writes the output */
@@ -144,6 +147,8 @@ typedef struct {
   int64_t kv_tokens_noncascade;        /* sum of seq_lens (positions read without cascade) */
   float est_us_cascade;                /* cost-model estimates used by AUTO */
   float est_us_noncascade;
+  int32_t partials_fp32;               /* 1 if partial outputs are fp32, 0 if bf16 */
+  int32_t reserved1;
 } ca_plan_info_t;
 
 typedef struct ca_plan* ca_plan_t;

@@ -54,6 +54,7 @@ class ca_params_t(ctypes.Structure):
         ("sliding_window", ctypes.c_int32),
         ("prefix_splits", ctypes.c_int32),
         ("suffix_order", ctypes.c_int32),
+        ("partials_fp32", ctypes.c_int32),
     ]
 
 
@@ -85,6 +86,8 @@ class ca_plan_info_t(ctypes.Structure):
         ("kv_tokens_noncascade", ctypes.c_int64),
         ("est_us_cascade", ctypes.c_float),
         ("est_us_noncascade", ctypes.c_float),
+        ("partials_fp32", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -197,7 +200,8 @@ def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: in
             block_table, query_start_loc, seq_lens, num_computed_tokens=None, softmax_scale: float = 0.0,
             mode="auto", num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
             max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0,
-            sliding_window: int = 0, prefix_splits: int = 0, suffix_order: int = 0):
+            sliding_window: int = 0, prefix_splits: int = 0, suffix_order: int = 0,
+            partials_fp32: bool = False):
     """ca_params_t plus the host metadata arrays and their pointers."""
     bt, bt_p = _host_i32(block_table)
     qsl, qsl_p = _host_i32(query_start_loc)
@@ -228,6 +232,7 @@ def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: in
     prm.sliding_window = int(sliding_window)
     prm.prefix_splits = int(prefix_splits)
     prm.suffix_order = int(suffix_order)
+    prm.partials_fp32 = int(partials_fp32)
     keep = (bt, qsl, sl, nc)   # the arrays behind the pointers
     return prm, (bt_p, qsl_p, sl_p, nc_p), keep
 
@@ -241,7 +246,7 @@ def cascade_attn_plan(**kw) -> Plan:
     arrays or CPU tensors), and the optional ca_params_t settings
     softmax_scale, mode, num_cus, heads_per_item, separate_phases,
     max_levels, kv_dtype, k_scale, v_scale, sliding_window, prefix_splits,
-    suffix_order.
+    suffix_order, partials_fp32.
     """
     prm, ptrs, keep = _params(**kw)
     h = ctypes.c_void_p(0)

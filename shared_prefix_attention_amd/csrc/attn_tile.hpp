@@ -65,7 +65,8 @@ struct TileArgs {
   int32_t splits;               // KV splits (prefix) / chunks per request
   int32_t heads_per_item;       // per-request phase: consecutive KV heads one item runs (divides hkv)
   int32_t split_tokens;         // multiple of 64, <= kMaxItemPages * 16
-  float* part_o;                // [slots][T][hq][D] fp32 (partial mode)
+  void* part_o;                 // [slots][T][hq][D] bf16 or fp32 (partial mode)
+  int32_t part_fp32;            // partial outputs in fp32 (else bf16)
   float* part_lse;              // [slots][T][hq] fp32, natural log
   int32_t slot_base;
   int64_t slot_elems;           // T * hq * D
@@ -697,9 +698,19 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
               u32x2_t{pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
         if (lq == 0 && a.lse_out) a.lse_out[row] = lse;
       } else {
-        float* dst = a.part_o + (int64_t)slot * a.slot_elems + row * D;
+        const int64_t e0 = (int64_t)slot * a.slot_elems + row * D;
+        if (a.part_fp32) {
+          float* dst = static_cast<float*>(a.part_o) + e0;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(dst + db * 16 + lq * 4) = o[db][rb] * inv;
+          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(dst + db * 16 + lq * 4) = o[db][rb] * inv;
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(a.part_o) + e0;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const f32x4_t r = o[db][rb] * inv;
+            *reinterpret_cast<u32x2_t*>(dst + db * 16 + lq * 4) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+          }
+        }
         if (lq == 0) a.part_lse[(int64_t)slot * a.slot_rows + row] = lse;
       }
     }

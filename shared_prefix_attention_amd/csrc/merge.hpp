@@ -15,7 +15,7 @@
 namespace ca {
 
 struct MergeArgs {
-  const float* part_o;     // [slots][rows][D]
+  const void* part_o;      // [slots][rows][D] bf16 or fp32
   const float* part_lse;   // [slots][rows]
   int32_t slots;
   int64_t rows;            // T * hq
@@ -26,8 +26,9 @@ struct MergeArgs {
   int32_t hq;
 };
 
-// D/4 threads per row, each owning 4 consecutive d values.
-template <int D>
+// D/4 threads per row, each owning 4 consecutive d values. F32: partial
+// outputs in fp32, else bf16 (widened exactly).
+template <int D, bool F32>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
@@ -47,11 +48,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   for (int s0 = 0; s0 < a.slots; s0 += B) {
     float l[B];
     f32x4_t x[B][1];
+    u32x2_t w[F32 ? 1 : B];   // bf16 partials: raw words, widened once all loads are out
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int sl = min(s0 + k, a.slots - 1);
       l[k] = (s0 + k < a.slots) ? a.part_lse[(int64_t)sl * a.rows + row] : -INFINITY;
-      x[k][0] = *reinterpret_cast<const f32x4_t*>(a.part_o + (int64_t)sl * a.slot_elems + row * D + part * 4);
+      const int64_t e = (int64_t)sl * a.slot_elems + row * D + part * 4;
+      if constexpr (F32) x[k][0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part_o) + e);
+      else w[k] = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(a.part_o) + e);
+    }
+    if constexpr (!F32) {
+#pragma unroll
+      for (int k = 0; k < B; ++k)
+        x[k][0] = f32x4_t{__builtin_bit_cast(float, w[k][0] << 16), __builtin_bit_cast(float, w[k][0] & 0xffff0000u),
+                          __builtin_bit_cast(float, w[k][1] << 16), __builtin_bit_cast(float, w[k][1] & 0xffff0000u)};
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) merge_step(m, wsum, acc, l[k], x[k]);

@@ -102,7 +102,7 @@ static PhaseTile choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& 
   const int64_t ntiles = cdiv(pl.prefix_len, kTileKeys);
   const int64_t max_tiles = kMaxItemTokens / kTileKeys;
   const double bpt = 2.0 * pl.kv_bytes() * pl.hkv * pl.d;       // K+V bytes per token
-  const double part_per_split = (double)pl.total_q * pl.hq * (pl.d + 1) * 4.0;
+  const double part_per_split = (double)pl.total_q * pl.hq * pl.part_row_bytes();
   double best = 1e30;
   t.mtiles = (int32_t)mtiles;
   t.splits = 1;
@@ -110,6 +110,8 @@ static PhaseTile choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& 
   for (int64_t s = 1; s <= ntiles; s *= 2) {
     const int64_t tiles_per = cdiv(ntiles, s);
     if (tiles_per > max_tiles) continue;
+    // an item of one stage has nothing to overlap its start-up with
+    if (s > 1 && tiles_per < 2) break;
     const int64_t splits = cdiv(ntiles, tiles_per);
     const int64_t items = mtiles * pl.hkv * splits;
     const double active = (double)std::min<int64_t>(items, cus);
@@ -118,7 +120,9 @@ static PhaseTile choose_prefix(const ca_plan& pl, int32_t cus, const CostModel& 
     const double t_mfma = waves_of_items * item_flops / (t.row_blocks > 1 ? cm.cu_mfma : cm.cu_mfma_rows);
     const double hbm = bpt * pl.prefix_len + part_per_split * splits + (double)pl.total_q * pl.hq * pl.d * 2.0;
     const double t_hbm = hbm / std::min(cm.hbm_bw, active * cm.cu_bw);
-    const double est = (std::max(t_mfma, t_hbm) + part_per_split * splits / cm.mall_bw) * 1e6 + cm.item_latency_us;
+    // every round of items on the CUs pays the start / drain latency again
+    const double est =
+        (std::max(t_mfma, t_hbm) + part_per_split * splits / cm.mall_bw) * 1e6 + waves_of_items * cm.item_latency_us;
     if (est < best) {
       best = est;
       t.splits = (int32_t)splits;
@@ -203,7 +207,7 @@ static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_
   const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma_rows);
   double us = std::max(t_bytes, t_mfma) * 1e6 + cm.launch_us;
   if (merge) {
-    const double part = (double)chunks * pl.total_q * pl.hq * (pl.d + 1) * 4.0;
+    const double part = (double)chunks * pl.total_q * pl.hq * pl.part_row_bytes();
     us += 2.0 * part / cm.mall_bw * 1e6 + cm.launch_us;
   }
   return us;
@@ -361,6 +365,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.sliding_window < 0) return fail(CA_EINVAL, "sliding_window must be >= 0");
   if (p.prefix_splits < 0) return fail(CA_EINVAL, "prefix_splits must be >= 0");
   if (p.suffix_order != 0 && p.suffix_order != 1) return fail(CA_EINVAL, "suffix_order must be 0 or 1");
+  if (p.partials_fp32 != 0 && p.partials_fp32 != 1) return fail(CA_EINVAL, "partials_fp32 must be 0 or 1");
   if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
   if (p.kv_dtype == CA_KV_FP8_E4M3) {
     if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
@@ -408,6 +413,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   pl->max_seq_len = max_seq;
   pl->scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)p.head_dim);
   pl->kv_fp8 = p.kv_dtype == CA_KV_FP8_E4M3 ? 1 : 0;
+  pl->part_fp32 = p.partials_fp32;
   pl->k_scale = (pl->kv_fp8 && p.k_scale > 0.f) ? p.k_scale : 1.f;
   pl->v_scale = (pl->kv_fp8 && p.v_scale > 0.f) ? p.v_scale : 1.f;
 
@@ -512,7 +518,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     suf = choose_suffix(*pl, cus, true);
     const double t_suf = est_suffix_us(*pl, suffix_tokens, suffix_padded_flops(*pl, qsl, seq_lens, kstart.data()),
                                        suf.splits, false, cus, cm, 0.0);
-    const double merge_bytes = (double)(pre.splits + lvl1.splits + suf.splits) * total_q * pl->hq * (pl->d + 1) * 4.0 +
+    const double merge_bytes = (double)(pre.splits + lvl1.splits + suf.splits) * total_q * pl->hq * pl->part_row_bytes() +
                                (double)total_q * pl->hq * pl->d * 2.0;
     pl->est_us_cascade = (float)(pre_us + t_grp + cm.launch_us + t_suf +
                                  (merge_bytes / cm.mall_bw) * 1e6 + cm.launch_us);
@@ -570,7 +576,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   }
   pl->slot_elems = total_q * pl->hq * pl->d;
   if (pl->num_slots > 0) {
-    const int64_t o_bytes = round_up((int64_t)pl->num_slots * pl->slot_elems * 4, 256);
+    const int64_t o_bytes = round_up((int64_t)pl->num_slots * pl->slot_elems * (pl->part_fp32 ? 4 : 2), 256);
     const int64_t l_bytes = round_up((int64_t)pl->num_slots * total_q * pl->hq * 4, 256);
     pl->ws_lse_offset = o_bytes;
     pl->workspace_bytes = o_bytes + l_bytes;
@@ -619,6 +625,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->kv_dtype = pl->kv_fp8 ? CA_KV_FP8_E4M3 : CA_KV_BF16;
   out->sliding_window = pl->window;
   out->suffix_longest_first = pl->order_n > 0 ? 1 : 0;
+  out->partials_fp32 = pl->part_fp32;
   out->total_q = pl->total_q;
   out->workspace_bytes = pl->workspace_bytes;
   out->kv_tokens_cascade = pl->kv_tokens_cascade;

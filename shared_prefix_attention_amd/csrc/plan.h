@@ -60,6 +60,9 @@ struct ca_plan {
   float k_scale = 1.f;         // dequantisation factors of the caches (1 for bf16)
   float v_scale = 1.f;
   int32_t kv_bytes() const { return kv_fp8 ? 1 : 2; }
+  int32_t part_fp32 = 0;       // partial outputs in fp32 (else bf16); partial LSEs are fp32
+  // bytes of one (token, head) partial state: output and LSE
+  double part_row_bytes() const { return part_fp32 ? (d + 1) * 4.0 : d * 2.0 + 4.0; }
   int32_t window = 0;          // sliding window of the non-cascade path (0: none)
 
   int32_t common_blocks = 0;

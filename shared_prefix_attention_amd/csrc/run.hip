@@ -163,11 +163,12 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
 }
 
 template <int D>
-ca_status_t run_merge(const MergeArgs& args, hipStream_t s) {
+ca_status_t run_merge(const MergeArgs& args, bool f32, hipStream_t s) {
   constexpr int RPB = 256 / (D / 4);
   const int64_t grid = (args.rows + RPB - 1) / RPB;
   if (grid <= 0) return CA_OK;
-  launch(K_MERGE, merge_kernel<D>, dim3((unsigned)grid), dim3(256), s, args);
+  if (f32) launch(K_MERGE, merge_kernel<D, true>, dim3((unsigned)grid), dim3(256), s, args);
+  else launch(K_MERGE, merge_kernel<D, false>, dim3((unsigned)grid), dim3(256), s, args);
   return check_launch("merge kernel launch");
 }
 
@@ -198,9 +199,10 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   base.slot_rows = pl->total_q * pl->hq;
   base.out = static_cast<uint16_t*>(out);
   base.lse_out = lse;
-  float* part_o = static_cast<float*>(ws);
+  void* part_o = ws;
   float* part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl->ws_lse_offset) : nullptr;
   base.part_o = part_o;
+  base.part_fp32 = pl->part_fp32;
   base.part_lse = part_lse;
 
   // second shared level (none: n = 0)
@@ -287,7 +289,7 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     ma.lse_out = lse;
     ma.sinks = sinks;
     ma.hq = pl->hq;
-    st = run_merge<D>(ma, s);
+    st = run_merge<D>(ma, pl->part_fp32 != 0, s);
     if (st != CA_OK) return st;
   }
   return CA_OK;

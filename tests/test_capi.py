@@ -213,7 +213,12 @@ def test_plan_partition_is_consistent():
             info = _plan(b, mode=mode).info
             T, hq, d = b.q.shape
             slots = info["num_partial_slots"]
-            assert info["workspace_bytes"] >= slots * T * hq * (d + 1) * 4
+            assert info["partials_fp32"] == 0
+            assert info["workspace_bytes"] >= slots * T * hq * (d * 2 + 4)
+            # fp32 partials (the cost model prices their bytes, so the split count may differ)
+            wide = _plan(b, mode=mode, partials_fp32=True).info
+            assert wide["partials_fp32"] == 1
+            assert wide["workspace_bytes"] >= wide["num_partial_slots"] * T * hq * (d + 1) * 4
             if info["use_cascade"]:
                 assert info["merge_in_suffix"] == 0
                 assert slots == info["prefix_splits"] + info["level1_splits"] + info["suffix_chunks"]

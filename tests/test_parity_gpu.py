@@ -286,3 +286,17 @@ def test_longest_first_order_changes_no_result(name, mode):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     ref_o, ref_l = oracle_ref(b)
     assert_close(o1, l1, ref_o, ref_l, what=f"{name}/{mode}/longest-first")
+
+
+@pytest.mark.parametrize("name,mode", [("prefill_mix", "on"), ("gqa8_outliers", "on"), ("nested_prefill", "on"),
+                                       ("long_prefix_split", "off"), ("fp8_prefill", "on"), ("d64_gqa", "on")])
+def test_fp32_partials(name, mode):
+    """Partial outputs kept in fp32 (partials_fp32): the same plan shape,
+    the merge reading fp32 states; parity with the oracle."""
+    log(f"[parity] {name} mode={mode} fp32 partials")
+    b = workloads.make_batch(SMALL[name])
+    db = DeviceBatch(b)
+    o32, l32, i32 = run(db, mode=mode, partials_fp32=True)
+    assert i32["partials_fp32"] == 1 and i32["num_partial_slots"] > 0
+    ref_o, ref_l = oracle_ref(b)
+    assert_close(o32, l32, ref_o, ref_l, what=f"{name}/{mode}/fp32-partials")
