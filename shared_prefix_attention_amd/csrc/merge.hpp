@@ -26,33 +26,53 @@ struct MergeArgs {
   int32_t hq;
 };
 
-// D/4 threads per row, each owning 4 consecutive d values. F32: partial
-// outputs in fp32, else bf16 (widened exactly).
-template <int D, bool F32>
+// Folds an unnormalised state (m2, w2, acc2) into (m, w, acc): acc / w is
+// the merged output and m + log(w) its LSE.
+__device__ __forceinline__ void fold_state(float& m, float& w, f32x4_t& acc, float m2, float w2, const f32x4_t& acc2) {
+  if (m2 == -INFINITY) return;
+  const float mn = fmaxf(m, m2);
+  const float a1 = (m == -INFINITY) ? 0.f : exp2f((m - mn) * kLog2e);
+  const float a2 = exp2f((m2 - mn) * kLog2e);
+  w = w * a1 + w2 * a2;
+  acc = acc * a1 + acc2 * a2;
+  m = mn;
+}
+
+// D/4 threads per row and slot group, each owning 4 consecutive d values.
+// F32: partial outputs in fp32, else bf16 (widened exactly). SG slot groups
+// share a row's slots (contiguous ranges) when there are many slots and few
+// rows: each group merges its range, and group 0 folds the others in, in
+// group order, through LDS (so the result is fixed by the slot count).
+template <int D, bool F32, int SG>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  constexpr int RPB = 256 / (TPR * SG);
   const int part = threadIdx.x % TPR;
-  if (row >= a.rows) return;
-  // Online merge over slots in batches whose loads (LSE and o, the latter
-  // unconditionally: every slot is in bounds) are all issued before the first
-  // use, so a row costs one memory round trip per batch.
+  const int rl = (threadIdx.x / TPR) % RPB;
+  const int g = threadIdx.x / (TPR * RPB);
+  const int64_t row = (int64_t)blockIdx.x * RPB + rl;
+  const bool live = row < a.rows;
+  if (SG == 1 && !live) return;
+  const int per = (a.slots + SG - 1) / SG;
+  const int s_begin = g * per, s_end = min(a.slots, s_begin + per);
+  // Online merge over the group's slots in batches whose loads (LSE and o,
+  // the latter unconditionally: every slot is in bounds) are all issued
+  // before the first use, so a row costs one memory round trip per batch.
   constexpr int B = 16;
   float m = -INFINITY, wsum = 0.f;
-  if (a.sinks) {   // the sink joins the normaliser as one more state with no value
+  if (a.sinks && g == 0 && live) {   // the sink joins the normaliser as one more state with no value
     m = a.sinks[row % a.hq];
     wsum = m == -INFINITY ? 0.f : 1.f;
   }
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  for (int s0 = 0; s0 < a.slots; s0 += B) {
+  for (int s0 = s_begin; live && s0 < s_end; s0 += B) {
     float l[B];
     f32x4_t x[B][1];
     u32x2_t w[F32 ? 1 : B];   // bf16 partials: raw words, widened once all loads are out
 #pragma unroll
     for (int k = 0; k < B; ++k) {
-      const int sl = min(s0 + k, a.slots - 1);
-      l[k] = (s0 + k < a.slots) ? a.part_lse[(int64_t)sl * a.rows + row] : -INFINITY;
+      const int sl = min(s0 + k, s_end - 1);
+      l[k] = (s0 + k < s_end) ? a.part_lse[(int64_t)sl * a.rows + row] : -INFINITY;
       const int64_t e = (int64_t)sl * a.slot_elems + row * D + part * 4;
       if constexpr (F32) x[k][0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part_o) + e);
       else w[k] = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(a.part_o) + e);
@@ -65,6 +85,25 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) merge_step(m, wsum, acc, l[k], x[k]);
+  }
+  if constexpr (SG > 1) {
+    __shared__ float xs[SG - 1][RPB][TPR][6];
+    if (g > 0) {
+      float* r = xs[g - 1][rl][part];
+      r[0] = acc[0][0];
+      r[1] = acc[0][1];
+      r[2] = acc[0][2];
+      r[3] = acc[0][3];
+      r[4] = m;
+      r[5] = wsum;
+    }
+    __syncthreads();
+    if (g > 0 || !live) return;
+#pragma unroll
+    for (int g2 = 1; g2 < SG; ++g2) {
+      const float* r = xs[g2 - 1][rl][part];
+      fold_state(m, wsum, acc[0], r[4], r[5], f32x4_t{r[0], r[1], r[2], r[3]});
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const f32x4_t r = acc[0] * inv;

@@ -164,11 +164,20 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
 
 template <int D>
 ca_status_t run_merge(const MergeArgs& args, bool f32, hipStream_t s) {
-  constexpr int RPB = 256 / (D / 4);
-  const int64_t grid = (args.rows + RPB - 1) / RPB;
+  // more than 16 slots: four slot groups per row, each one batch of loads
+  const int sg = args.slots > 16 ? 4 : 1;
+  const int rpb = 256 / (D / 4) / sg;
+  const int64_t grid = (args.rows + rpb - 1) / rpb;
   if (grid <= 0) return CA_OK;
-  if (f32) launch(K_MERGE, merge_kernel<D, true>, dim3((unsigned)grid), dim3(256), s, args);
-  else launch(K_MERGE, merge_kernel<D, false>, dim3((unsigned)grid), dim3(256), s, args);
+  if (grid > 0x7fffffff) return fail(CA_EINVAL, "merge grid too large");
+  const dim3 gr((unsigned)grid), bl(256);
+  if (sg == 4) {
+    if (f32) launch(K_MERGE, merge_kernel<D, true, 4>, gr, bl, s, args);
+    else launch(K_MERGE, merge_kernel<D, false, 4>, gr, bl, s, args);
+  } else {
+    if (f32) launch(K_MERGE, merge_kernel<D, true, 1>, gr, bl, s, args);
+    else launch(K_MERGE, merge_kernel<D, false, 1>, gr, bl, s, args);
+  }
   return check_launch("merge kernel launch");
 }
 
