@@ -133,7 +133,7 @@ typedef struct {
   int32_t num_partial_slots;           /* partial states per (token, head) */
   int32_t prefix_stages;               /* LDS pipeline depth of the prefix kernel */
   int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
-  int32_t merge_in_suffix;             /* 1: the suffix kernel merges and writes the output */
+  int32_t reserved2;                   /* 0 */
   int32_t suffix_heads_per_item;       /* consecutive KV heads one suffix (or only) work item runs */
   int32_t separate_phases;             /* 1 if the cascade phases run as separate launches */
   int32_t num_level1_groups;           /* request groups of the second shared level (0 = none) */

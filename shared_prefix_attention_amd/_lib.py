@@ -72,7 +72,7 @@ class ca_plan_info_t(ctypes.Structure):
         ("num_partial_slots", ctypes.c_int32),
         ("prefix_stages", ctypes.c_int32),
         ("suffix_stages", ctypes.c_int32),
-        ("merge_in_suffix", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
         ("suffix_heads_per_item", ctypes.c_int32),
         ("separate_phases", ctypes.c_int32),
         ("num_level1_groups", ctypes.c_int32),

@@ -555,7 +555,6 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
         pl->kv_fp8 ? 1
                    : pick_heads_per_item(*pl, (int64_t)pre.mtiles * pl->hkv * pre.splits + group_items,
                                          std::max<int64_t>(pre.split_tokens / kTileKeys, group_stages), suf, cus);
-    pl->merge_in_suffix = 0;
     pl->separate_phases = p.separate_phases;
     pl->num_slots = pre.splits + lvl1.splits + suf.splits;
     pl->direct_out = false;
@@ -567,7 +566,6 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->suffix = nc;
     if (pl->kv_fp8) pl->suffix.stages = 4;
     pl->suffix.heads_per_item = (nc.kernel == 1 && p.heads_per_item > 0 && !pl->kv_fp8) ? p.heads_per_item : 1;
-    pl->merge_in_suffix = 0;
     pl->separate_phases = 0;
     pl->num_slots = nc.splits > 1 ? nc.splits : 0;
     pl->direct_out = nc.splits == 1;
@@ -617,7 +615,6 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->num_partial_slots = pl->num_slots;
   out->prefix_stages = pl->use_cascade ? pl->prefix.stages : 0;
   out->suffix_stages = pl->suffix.stages;
-  out->merge_in_suffix = pl->merge_in_suffix;
   out->suffix_heads_per_item = pl->suffix.heads_per_item;
   out->separate_phases = pl->separate_phases;
   out->num_level1_groups = pl->lvl1.n;

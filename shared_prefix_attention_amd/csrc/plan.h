@@ -76,7 +76,6 @@ struct ca_plan {
   int32_t max_suffix_len = 0; // max over requests of seq_len - key_start
   int32_t num_slots = 0;      // fp32 partial states per (token, head)
   bool direct_out = false;    // the last attention launch writes the bf16 output directly
-  int32_t merge_in_suffix = 0;// cascade: the suffix kernel folds in the prefix partials
   int32_t separate_phases = 0;// cascade: prefix and suffix as two launches
   ca::Level1 lvl1;            // cascade: second shared level (n = 0: none)
   int64_t slot_elems = 0;     // T * Hq * d
