@@ -182,7 +182,8 @@ static void order_requests(ca_plan& pl, const ca_params_t& p, const int32_t* seq
 // for a slot, and each item's first round trips are paid once for all its
 // heads) and the grouped item stays at most half as long as a prefix item: a
 // decode stage costs about one memory round trip, so longer chains become the
-// launch's critical path. Otherwise one head per item.
+// launch's critical path. Failing that, two heads per item when the suffix
+// items alone need more than two rounds; otherwise one head per item.
 static int32_t pick_heads_per_item(const ca_plan& pl, int64_t prefix_items, int64_t prefix_stages,
                                    const PhaseTile& suf, int32_t cus) {
   if (suf.kernel != 1) return 1;
@@ -191,9 +192,15 @@ static int32_t pick_heads_per_item(const ca_plan& pl, int64_t prefix_items, int6
   const int64_t suffix_stages = suf.split_tokens / kTileKeys;
   for (int32_t h = 1; h <= pl.hkv && h <= 8; ++h) {
     if (pl.hkv % h) continue;
-    if (prefix_items + per_head * (pl.hkv / h) <= 2 * (int64_t)cus)
-      return h * suffix_stages <= std::max<int64_t>(1, prefix_stages / 2) ? h : 1;
+    if (prefix_items + per_head * (pl.hkv / h) <= 2 * (int64_t)cus) {
+      if (h * suffix_stages <= std::max<int64_t>(1, prefix_stages / 2)) return h;
+      break;
+    }
   }
+  // Suffix items alone fill more than two rounds of two work-groups per CU:
+  // two heads per item halve the item start-ups (the second head's first
+  // stages are already in flight when the first head finishes).
+  if (per_head * pl.hkv > 4 * (int64_t)cus && pl.hkv % 2 == 0) return 2;
   return 1;
 }
 
