@@ -242,6 +242,15 @@ def test_heads_per_item_choice_and_override():
     assert _plan(wd, mode="on", heads_per_item=8).info["suffix_heads_per_item"] == 8
     mp = workloads.make_batch(workloads.get("mixed_prefill"))
     assert _plan(mp, mode="on", heads_per_item=2).info["suffix_heads_per_item"] == 1
+    # 2,048 one-head decode items need four rounds of two work-groups per CU:
+    # two heads per item; fp8 plans keep one
+    sc = workloads.make_batch(workloads.get("self_consistency"))
+    assert _plan(sc, mode="on").info["suffix_heads_per_item"] == 2
+    sc8 = workloads.make_batch(workloads.get("self_consistency_fp8"))
+    assert _plan(sc8, mode="on").info["suffix_heads_per_item"] == 1
+    # the long document's 64 items per head fit one round with two heads per item
+    ld = workloads.make_batch(workloads.get("long_doc"))
+    assert _plan(ld, mode="on").info["suffix_heads_per_item"] == 2
 
 
 def test_separate_phases_changes_only_the_launch_count():
