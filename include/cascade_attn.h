@@ -24,7 +24,8 @@
  *   - Plain C, no allocation visible to the caller other than the plan
  *     handle; the caller owns every tensor (device memory from any allocator).
  *   - Dtypes: Q and output are bf16; the K/V caches bf16 or fp8 e4m3
- *     (ca_kv_dtype_t); LSE and workspace fp32; metadata int32.
+ *     (ca_kv_dtype_t); LSE fp32; workspace partial states bf16 or fp32
+ *     (partials_fp32) with fp32 LSEs; metadata int32.
  *   - seq_lens[r] counts all KV positions of request r including this
  *     step's q_len_r query tokens, which are its last q_len_r positions;
  *     num_computed_tokens[r] = seq_lens[r] - q_len_r.

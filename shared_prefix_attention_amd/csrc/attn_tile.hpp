@@ -611,8 +611,10 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     else wait_vmcnt<0>();
   };
 
-  // All NS buffers are filled up front; afterwards stage u + NS - 1 goes into
-  // the buffer that stage u - 1 used, once every wave is past stage u's barrier.
+  // All NS buffers are filled up front. Afterwards, with shared buffers, stage
+  // u + NS - 1 goes into the buffer that stage u - 1 used, once every wave is
+  // past stage u's barrier; per-wave pipelines refill a buffer themselves (in
+  // the stage loop).
   const int U = H * n_tiles;
   const int pro = min(NS, U);
   for (int p = 0; p < pro; ++p) issue_next();
@@ -725,8 +727,9 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 
   int h = 0, t = 0;   // head and tile of stage u
   for (int u = 0; u < U; ++u) {
-    // stages issued after stage u so far: the prologue filled NS buffers,
-    // and iteration i >= 1 issued stage i + NS - 1
+    // Shared buffers: the prologue filled NS buffers and iteration i >= 1
+    // issued stage i + NS - 1, so stage u is followed by min(NS - 2, ...)
+    // issued stages here (NS - 1 at u = 0).
     // Per-wave pipelines: stages u .. u + NS - 1 are in flight here, and
     // stage u + NS goes into stage u's buffer once its fragments are read,
     // except after a head's last tile, whose buffer holds the key-group

@@ -74,7 +74,7 @@ struct ca_plan {
   ca::PhaseTile suffix;       // suffix phase (cascade) or the only phase
   int32_t key_start = 0;      // first KV position of the suffix phase (prefix_len or 0)
   int32_t max_suffix_len = 0; // max over requests of seq_len - key_start
-  int32_t num_slots = 0;      // fp32 partial states per (token, head)
+  int32_t num_slots = 0;      // partial states per (token, head)
   bool direct_out = false;    // the last attention launch writes the bf16 output directly
   int32_t separate_phases = 0;// cascade: prefix and suffix as two launches
   ca::Level1 lvl1;            // cascade: second shared level (n = 0: none)
