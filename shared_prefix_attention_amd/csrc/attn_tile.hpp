@@ -158,20 +158,23 @@ __device__ __forceinline__ int chunk_swz_v8(int key) {
   return ((key >> 1) & 1) | ((((key >> 4) ^ (key >> 2)) & 1) << 1) | (((key >> 2) & 1) << 2);
 }
 
-// Eight fp8 (OCP e4m3) values, bytes 0..7 of (w0, w1), as eight bf16 in
-// element order. v_cvt_pk_f32_fp8 decodes two bytes exactly (every e4m3
-// value, subnormals included, is a bf16 value too), so the bf16 rounding is
-// exact as well.
+// Two fp8 (OCP e4m3) values, bytes 0-1 (high: 2-3) of w, as two bf16 in one
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1. Every e4m3 value, subnormals
+// included, is a bf16 value, so the conversion is exact (checked on the device
+// against v_cvt_pk_f32_fp8 + v_cvt_pk_bf16_f32 for all 256 codes in both
+// halves of both words).
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+}
+// Eight fp8 values, bytes 0..7 of (w0, w1), as eight bf16 in element order.
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
-  return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
-                 pack_bf16x2(d[0], d[1])};
+  return u32x4_t{fp8x2_to_bf16<false>(w0), fp8x2_to_bf16<true>(w0), fp8x2_to_bf16<false>(w1),
+                 fp8x2_to_bf16<true>(w1)};
 }
 // Four fp8 values (bytes 0..3 of w) as four bf16.
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1])};
+  return u32x2_t{fp8x2_to_bf16<false>(w), fp8x2_to_bf16<true>(w)};
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes
