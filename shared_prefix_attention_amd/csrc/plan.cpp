@@ -66,6 +66,9 @@ struct CostModel {
   double cu_mfma_rows = 1.8e12;   // flop/s of one CU, 64-row tiles and prefill suffixes (causal, ragged)
   double reread_bw = 14.0e12;     // bytes/s of the non-cascade path's shared-prefix re-reads (L2 / MALL)
   double launch_us = 2.5;         // per kernel launch on one stream
+  double merge_trip_us = 1.5;     // the merge's one memory round trip
+  double decode_stage_us = 0.5;   // one 64-key stage of a decode-shaped item
+  double rows_stage_us = 1.4;     // one 64-key stage of a 64-row item
   double mall_bytes = 256.0e6;    // Infinity Cache capacity
 };
 
@@ -451,6 +454,19 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   pl->max_suffix_len = max_seq;
   PhaseTile nc = choose_suffix(*pl, cus, true);
   {
+    // Chunking a request's KV range fills the chip but adds the merge
+    // launch: keep one chunk per request (the attention writes the output)
+    // when the chunked plan does not save that launch's cost.
+    const PhaseTile direct = choose_suffix(*pl, cus, false);
+    if (direct.splits < nc.splits) {
+      const double t_stage = nc.kernel == 1 ? cm.decode_stage_us : cm.rows_stage_us;
+      const int64_t base = (int64_t)pl->num_reqs * nc.mtiles * pl->hkv;
+      auto items_us = [&](const PhaseTile& t) {
+        const double rounds = std::ceil((double)(base * t.splits) / (2.0 * cus));
+        return rounds * (cm.item_latency_us + (double)(t.split_tokens / kTileKeys) * t_stage);
+      };
+      if (items_us(direct) <= items_us(nc) + cm.launch_us + cm.merge_trip_us) nc = direct;
+    }
     const double shared_bytes = bpt * plen;
     const double reread = shared_bytes * (n - 1);
     int64_t hbm_tokens = pl->kv_tokens_cascade;
