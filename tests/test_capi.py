@@ -429,3 +429,14 @@ def test_suffix_order():
     with pytest.raises(spa.CascadeAttnError) as e:
         _plan(wd, mode="on", suffix_order=2)
     assert e.value.status == _lib.CA_EINVAL
+
+
+def test_noncascade_chunking_pays_for_the_merge():
+    """The non-cascade path splits a request's KV range only when that saves
+    more than the merge launch it adds: small batches run one direct launch
+    (no partial slots); 8 requests of 33k tokens keep their chunks."""
+    for name in ("tiny_decode", "long_doc_p255", "multi_doc_prefill"):
+        info = _plan(workloads.make_batch(workloads.get(name)), mode="off").info
+        assert info["suffix_chunks"] == 1 and info["num_partial_slots"] == 0, name
+    info = _plan(workloads.make_batch(workloads.get("long_doc_n8")), mode="off").info
+    assert info["suffix_chunks"] > 1 and info["num_partial_slots"] == info["suffix_chunks"]
