@@ -256,7 +256,7 @@ ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache,
  * then times candidate plans on the device with the caller's data: the
  * non-cascade path and, when a prefix is shared and no window binds, the
  * cascade path with the planner's prefix split count, half and twice it,
- * one or the planner's KV heads per decode item, and (if the batch has
+ * one, two or the planner's KV heads per decode item, and (if the batch has
  * groups) one or two shared levels. Each candidate runs twice untimed and
  * `iters` times between two HIP events on `stream`; candidates needing more
  * than workspace_bytes are skipped. Returns the fastest plan in *out_plan

@@ -408,12 +408,16 @@ extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const in
     }
     const int32_t s0 = on->prefix.splits;
     const int32_t h0 = on->suffix.heads_per_item;
+    // two heads per decode item is a candidate whenever the plan's items are
+    // decode-shaped bf16 ones (fp8 plans run one head per item)
+    const bool two_heads = on->suffix.kernel == 1 && !on->kv_fp8 && on->hkv % 2 == 0 && h0 != 2;
     cascade_attn_plan_destroy(on);
     std::vector<int32_t> splits{s0};
     if (s0 >= 2) splits.push_back(s0 / 2);
     splits.push_back(s0 * 2);
     std::vector<int32_t> heads{0};
     if (h0 > 1) heads.push_back(1);
+    if (two_heads) heads.push_back(2);
     std::vector<int32_t> levels{0};
     if (base->cand_groups > 0) levels.push_back(1);
     for (int32_t sp : splits)
