@@ -300,3 +300,21 @@ def test_fp32_partials(name, mode):
     assert i32["partials_fp32"] == 1 and i32["num_partial_slots"] > 0
     ref_o, ref_l = oracle_ref(b)
     assert_close(o32, l32, ref_o, ref_l, what=f"{name}/{mode}/fp32-partials")
+
+
+@pytest.mark.parametrize("num_reqs,ordered", [(512, 1), (600, 0)])
+def test_request_order_table_limits(num_reqs, ordered):
+    """Decode batches at the request-order table's size: 512 requests fill
+    it (longest first), 600 run in batch order; sampled requests against the
+    oracle, cascade and non-cascade."""
+    w = Workload(f"many_requests_{num_reqs}", num_reqs, 256, (1, 200), (1, 1), 8, 2, 64, seed=3000 + num_reqs)
+    b = workloads.make_batch(w)
+    reqs = [0, 1, num_reqs // 2, num_reqs - 2, num_reqs - 1]
+    ref_o, ref_l = oracle_ref(b, requests=reqs)
+    rows = rows_of(b, reqs)
+    db = DeviceBatch(b)
+    for mode in ("on", "off"):
+        out, lse, info = run(db, mode=mode)
+        log(f"[order] N={num_reqs} mode={mode} longest_first={info['suffix_longest_first']}")
+        assert info["suffix_longest_first"] == ordered
+        assert_close(out, lse, ref_o, ref_l, rows=rows, what=f"N={num_reqs}/{mode}")
