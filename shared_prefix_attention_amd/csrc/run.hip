@@ -166,7 +166,7 @@ template <int D>
 ca_status_t run_merge(const MergeArgs& args, bool f32, hipStream_t s) {
   // more than 16 slots: four slot groups per row, each one batch of loads
   const int sg = args.slots > 16 ? 4 : 1;
-  const int rpb = 256 / (D / 4) / sg;
+  const int rpb = 256 / (D / (f32 ? 4 : 8)) / sg;   // a thread owns 4 fp32 or 8 bf16 values
   const int64_t grid = (args.rows + rpb - 1) / rpb;
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "merge grid too large");
