@@ -318,3 +318,19 @@ def test_request_order_table_limits(num_reqs, ordered):
         log(f"[order] N={num_reqs} mode={mode} longest_first={info['suffix_longest_first']}")
         assert info["suffix_longest_first"] == ordered
         assert_close(out, lse, ref_o, ref_l, rows=rows, what=f"N={num_reqs}/{mode}")
+
+
+@pytest.mark.parametrize("mode", ["on", "off"])
+def test_long_prefill_chunks(mode):
+    """Four requests with 1,100-1,600 query tokens each over a 2,048-token
+    shared prefix (5,833 tokens, 23,332 packed prefix rows per KV head): many
+    row tiles per request on the per-request phase, a large prefix phase.
+    Request 2 against the oracle."""
+    w = Workload("long_prefill", 4, 2048, (1500, 2500), (1000, 2000), 32, 8, 128, seed=4242)
+    b = workloads.make_batch(w)
+    ref_o, ref_l = oracle_ref(b, requests=[2])
+    out, lse, info = run(DeviceBatch(b), mode=mode)
+    log(f"[long prefill] mode={mode} cascade={info['use_cascade']} psplit={info['prefix_splits']} "
+        f"row tile={info['prefix_row_tile']} schunks={info['suffix_chunks']}")
+    assert info["use_cascade"] == (1 if mode == "on" else 0)
+    assert_close(out, lse, ref_o, ref_l, rows=rows_of(b, [2]), what=f"long_prefill/{mode}")
