@@ -18,6 +18,8 @@ non-cascade path, a warm-cache number and the oracle's CPU rate.
 Other modes (measurement plumbing, used under rocprofv3):
   --traffic-probe       one device copy of known size, then --steps steps
                         (no timing; for `rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE`)
+  --probe-separate      with --traffic-probe: the cascade phases as separate
+                        launches (per-phase counters, e.g. the prefix's MFMA)
   --summarize-pmc F W   read the counter CSVs of those two runs and write the
                         HBM-traffic summary profiles/traffic_<workload>.json
 """
@@ -164,6 +166,7 @@ def main():
     ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--max-levels", type=int, default=0, help="shared levels of the cascade plan (0 = default)")
     ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--probe-separate", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.gpus != 1:
@@ -219,6 +222,9 @@ def main():
         return f
 
     step = step_with(plan, ws)
+    if args.traffic_probe and args.probe_separate and casc:
+        plan = make_plan(args.mode, separate_phases=True)
+        step = step_with(plan, workspace_for(plan))
     if args.traffic_probe:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
