@@ -215,15 +215,16 @@ def _sinks(hq, seed):
     return z
 
 
-@pytest.mark.parametrize("name", ["tiny_decode", "prefill_mix", "gqa8_outliers", "nested_decode", "fp8_decode",
-                                  "long_prefix_split", "single_request"])
-@pytest.mark.parametrize("mode", ["on", "off"])
+SINKS = [(name, mode) for name in ["tiny_decode", "prefill_mix", "gqa8_outliers", "nested_decode", "fp8_decode",
+                                   "long_prefix_split", "single_request"]
+         for mode in ("on", "off") if mode == "off" or SMALL[name].prefix > 0]   # single_request shares nothing
+
+
+@pytest.mark.parametrize("name,mode", SINKS)
 def test_attention_sinks(name, mode):
     """Attention sinks through the merge (cascade, split KV) and through the
     direct epilogue (non-cascade with one chunk per request)."""
     w = SMALL[name]
-    if mode == "on" and w.prefix == 0:
-        pytest.skip("no shared prefix")
     log(f"[sinks] {name} mode={mode}")
     b = workloads.make_batch(w)
     z = _sinks(w.num_q_heads, w.seed)
