@@ -18,7 +18,10 @@
 //
 // Work-group: RW * KG wave64s owning one (KV head, row tile, KV range) item.
 // K/V are streamed SK keys (SK/16 pages) per stage straight from HBM into
-// LDS with global_load_lds_dwordx4 (no register staging), NS stages in flight.
+// LDS with global_load_lds_dwordx4 (no register staging), NS stage buffers.
+// Shapes with several row waves share each stage (one barrier per stage);
+// the decode shape (one row wave, KG key groups) runs one pipeline per wave,
+// since each wave reads only the keys its own DMA wrote.
 // Each LDS row (one key, d contiguous) has its 16-byte chunks XOR-swizzled
 // by the key index so the MFMA operand reads are bank-conflict free.
 // Wave (rw, kg) owns query rows [rw*16*RB, +16*RB) of the tile and keys
@@ -27,13 +30,20 @@
 // stage:
 //   S^T[key][row] = K Q^T   (v_mfma_f32_16x16x32_bf16: A = K from LDS,
 //                            B = Q^T kept in registers)
-//   online softmax on S^T (exp2 domain, fp32), P^T rounded to bf16
+//   online softmax on S^T (exp2 domain, fp32; the per-row reference max
+//                          moves only past a slack, so rescales are rare),
+//                          P^T rounded to bf16
 //   O^T[d][row] += V^T P^T (A = V^T read with the LDS transpose load
 //                            ds_read_b64_tr_b16, B = P^T taken straight from
 //                            the S^T accumulators; 16x16x32 MFMA for 32-key
 //                            groups, 16x16x16 for 16-key groups)
 // Computing the transposed products leaves P in the lane layout the second
 // product needs, so P never moves between lanes.
+//
+// Partial states (normalised o, bf16 or fp32, and the natural-log LSE) go
+// to the workspace for the merge kernel; an item covering a request's whole
+// range on the non-cascade path writes the final bf16 output instead.
+// Per-request items run in the plan's order (longest key range first).
 //
 // Masking: positions past the item's range are loaded from the item's last
 // valid position (so no unused page or NaN tail slot is ever read) and their
