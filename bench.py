@@ -22,6 +22,9 @@ Other modes (measurement plumbing, used under rocprofv3):
                         launches (per-phase counters, e.g. the prefix's MFMA)
   --summarize-pmc F W   read the counter CSVs of those two runs and write the
                         HBM-traffic summary profiles/traffic_<workload>.json
+  --decision-sweep      time the cascade and non-cascade paths over a grid of
+                        batch shapes and print, per shape, AUTO's choice, both
+                        times and the time AUTO loses against the faster path
 """
 
 import argparse
@@ -154,6 +157,82 @@ def summarize_pmc(fetch_dir, write_dir, workload, steps):
     return out
 
 
+# Batch shapes of the decision sweep: decode batches (one query token) over
+# request counts, shared-prefix lengths and suffix lengths around the gates
+# (256 tokens, 8 requests) and far from them, plus chunked-prefill batches.
+SWEEP_DECODE = [(n, p, s) for n in (4, 8, 16, 64, 256) for p in (256, 1024, 4096, 16384) for s in (16, 512)]
+SWEEP_PREFILL = [(n, p) for n in (8, 32, 128) for p in (256, 2048)]
+
+
+def decision_sweep(steps, warmup):
+    """AUTO's use_cascade choice against both forced paths, per batch shape
+    (GQA 32/8, head_dim 128, bf16, page 16; rotating input copies as in the
+    main measurement; each path's time is the median of per-step events).
+    Prints one JSON line per shape, with the planner's estimates, and a
+    summary line."""
+    import torch
+    import workloads
+    import shared_prefix_attention_amd as spa
+
+    dev = torch.device("cuda:0")
+    cases = [workloads.Workload(name=f"decode_n{n}_p{p}_s{sl}", num_reqs=n, prefix=p, suffix=(sl, sl), q_len=(1, 1),
+                                num_q_heads=32, num_kv_heads=8, head_dim=128, seed=7)
+             for n, p, sl in SWEEP_DECODE]
+    cases += [workloads.Workload(name=f"prefill_n{n}_p{p}", num_reqs=n, prefix=p, suffix=(64, 512), q_len=(1, 64),
+                                 num_q_heads=32, num_kv_heads=8, head_dim=128, seed=7)
+              for n, p in SWEEP_PREFILL]
+    recs = []
+    for w in cases:
+        b = workloads.make_batch(w)
+        touched = (b.k_cache.numel() + b.v_cache.numel() + b.q.numel()) * 2
+        rotate = int(min(32, max(2, math.ceil((1 << 30) / max(touched, 1)))))
+        copies = [(b.q.to(dev), b.k_cache.to(dev), b.v_cache.to(dev)) for _ in range(rotate)]
+        bt, qsl, sl = b.block_table.to(dev), b.query_start_loc.to(dev), b.seq_lens.to(dev)
+        out = torch.empty_like(copies[0][0])
+        lse = torch.empty(b.total_q, w.num_q_heads, dtype=torch.float32, device=dev)
+        times, infos, kern = {}, {}, {}
+        for mode in ("auto", "on", "off"):
+            pl = spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
+                                seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode)
+            ws = torch.empty(max(pl.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+
+            def f(i, pl=pl, ws=ws):
+                q, k, v = copies[i]
+                spa.cascade_attn_run(pl, q, k, v, bt, qsl, sl, out, lse, ws)
+            for i in range(warmup):
+                f(i % rotate)
+            times[mode] = step_distribution(f, steps, rotate)["p50"]   # median, robust to stray slow steps
+            infos[mode] = pl.info
+            if mode != "auto":
+                spa.cascade_attn_profile_enable(True)
+                time_steps(f, steps, rotate)
+                spa.cascade_attn_profile_enable(False)
+                kern[mode] = {k: round(t * 1e3 / c, 2) for k, (t, c) in spa.cascade_attn_profile_read().items() if c}
+        casc = bool(infos["auto"]["use_cascade"])
+        best = min(times["on"], times["off"])
+        chosen = times["on"] if casc else times["off"]
+        rec = {"case": w.name, "num_reqs": w.num_reqs, "prefix": w.prefix, "suffix": list(w.suffix),
+               "q_len": list(w.q_len), "gates_pass": infos["auto"]["gates_pass"], "auto_cascade": int(casc),
+               "cascade_us": round(times["on"], 2), "noncascade_us": round(times["off"], 2),
+               "auto_us": round(times["auto"], 2), "chosen_over_best": round(chosen / best, 3),
+               "faster": "cascade" if times["on"] < times["off"] else "non-cascade",
+               "est_cascade_us": round(infos["auto"]["est_us_cascade"], 1),
+               "est_noncascade_us": round(infos["auto"]["est_us_noncascade"], 1),
+               "noncascade_chunks": infos["off"]["suffix_chunks"], "prefix_splits": infos["on"]["prefix_splits"],
+               "kernels_cascade_us": kern["on"], "kernels_noncascade_us": kern["off"]}
+        recs.append(rec)
+        print(json.dumps(rec), flush=True)
+        del copies
+        torch.cuda.empty_cache()
+    right = sum(1 for r in recs if (r["auto_cascade"] == 1) == (r["faster"] == "cascade"))
+    lost = [r["chosen_over_best"] for r in recs]
+    print(json.dumps({"decision_sweep": len(recs), "auto_picked_faster": right,
+                      "worst_chosen_over_best": max(lost),
+                      "mean_chosen_over_best": round(sum(lost) / len(lost), 4),
+                      "steps": steps, "warmup": warmup}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,11 +247,15 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--probe-separate", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--decision-sweep", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.decision_sweep:
+        decision_sweep(args.steps, args.warmup)
+        return
     if args.summarize_pmc:
         rec = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.steps)
         os.makedirs(os.path.dirname(traffic_path(args.workload)), exist_ok=True)

@@ -69,6 +69,17 @@ struct CostModel {
   double merge_trip_us = 1.5;     // the merge's one memory round trip
   double decode_stage_us = 0.5;   // one 64-key stage of a decode-shaped item
   double rows_stage_us = 1.4;     // one 64-key stage of a 64-row item
+  // CU time of work items, for launches bound by their items' stage chains
+  // rather than by bytes (two work-groups per CU overlap, so these are per
+  // CU, not per work-group): a fixed part per item (start-up, combine,
+  // store) and a part per 64-key stage by work-group shape.
+  double item_cu_us = 5.2;        // 64- / 128-row items; decode-shaped items half of it
+  double rows_stage_cu_us = 0.94; // 64-row stage
+  double mfma_stage_cu_us = 0.91; // 128-row stage
+  double decode_stage_cu_us = 0.25;
+  double kernel_floor_us = 7.5;   // shortest attention launch: dispatch, page-table and first-stage round trips, store
+  double chunked_floor_us = 11.0; // shortest launch of KV-chunked decode items (partial states out)
+  double merge_floor_us = 3.5;    // shortest merge launch (its bytes move at hbm_bw on top)
   double mall_bytes = 256.0e6;    // Infinity Cache capacity
 };
 
@@ -207,18 +218,41 @@ static int32_t pick_heads_per_item(const ca_plan& pl, int64_t prefix_items, int6
   return 1;
 }
 
+// CU time (µs) of a per-request phase's items: request r runs
+// ceil(q_len_r * G / rows) row tiles per KV head, each split in `chunks`
+// items that together walk its positions [start_r, seq_len_r).
+static double items_cu_us(const ca_plan& pl, const PhaseTile& t, const int32_t* qsl, const int32_t* seq_lens,
+                          const int64_t* start, const CostModel& cm, int32_t heads_per_item = 1) {
+  const bool dec = t.kernel == 1;
+  const double a = (dec ? 0.5 * cm.item_cu_us : cm.item_cu_us) / heads_per_item;
+  const double x = dec ? cm.decode_stage_cu_us : (t.row_blocks > 1 ? cm.mfma_stage_cu_us : cm.rows_stage_cu_us);
+  double us = 0.0;
+  for (int32_t r = 0; r < pl.num_reqs; ++r) {
+    const int64_t mt = cdiv((int64_t)(qsl[r + 1] - qsl[r]) * pl.group, t.rows_per_wg());
+    const int64_t tiles = cdiv(std::max<int64_t>(0, seq_lens[r] - (start ? start[r] : 0)), kTileKeys);
+    us += (double)(mt * pl.hkv) * ((double)t.splits * a + (double)tiles * x);
+  }
+  return us;
+}
+
+// One merge launch that reads and writes `bytes` (partial states in, output
+// out): a fixed floor plus the bytes at the streaming rate.
+static double est_merge_us(double bytes, const CostModel& cm) { return cm.merge_floor_us + bytes / cm.hbm_bw * 1e6; }
+
 // Per-request phase over KV positions [key_start, seq_len): HBM bytes for the
-// KV actually streamed, plus the MFMA work of 16-row padded query blocks.
+// KV actually streamed, plus the MFMA work of 16-row padded query blocks, but
+// no less than `floor_us` (the launch's item rounds; 0 when the phase overlaps
+// another in one launch).
 static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_flops, int32_t chunks, bool merge,
-                            int32_t cus, const CostModel& cm, double extra_mall_bytes) {
+                            int32_t cus, const CostModel& cm, double extra_mall_bytes, double floor_us) {
   const double bpt = 2.0 * pl.kv_bytes() * pl.hkv * pl.d;
   const double io = (double)pl.total_q * pl.hq * pl.d * 2.0 * 2.0;
   const double t_bytes = (bpt * kv_tokens + io) / cm.hbm_bw + extra_mall_bytes / cm.reread_bw;
   const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma_rows);
-  double us = std::max(t_bytes, t_mfma) * 1e6 + cm.launch_us;
+  double us = std::max(std::max(t_bytes, t_mfma) * 1e6, floor_us) + cm.launch_us;
   if (merge) {
     const double part = (double)chunks * pl.total_q * pl.hq * pl.part_row_bytes();
-    us += 2.0 * part / cm.mall_bw * 1e6 + cm.launch_us;
+    us += est_merge_us(part + (double)pl.total_q * pl.hq * pl.d * 2.0, cm) + cm.launch_us;
   }
   return us;
 }
@@ -473,8 +507,15 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     double extra = 0.0;
     if (shared_bytes <= cm.mall_bytes) extra = reread;
     else hbm_tokens = sum_seq;
+    // however few bytes, the launch takes its floor, its items' CU time, or
+    // its longest item
+    const double t_stage = nc.kernel == 1 ? cm.decode_stage_us : cm.rows_stage_us;
+    const double t_longest = cm.item_latency_us + (double)(nc.split_tokens / kTileKeys) * t_stage;
+    const double floor_us = nc.splits > 1 && nc.kernel == 1 ? cm.chunked_floor_us : cm.kernel_floor_us;
+    const double t_items =
+        std::max(std::max(floor_us, t_longest), items_cu_us(*pl, nc, qsl, seq_lens, nullptr, cm) / cus);
     pl->est_us_noncascade = (float)est_suffix_us(*pl, hbm_tokens, suffix_padded_flops(*pl, qsl, seq_lens, nullptr),
-                                                 nc.splits, nc.splits > 1, cus, cm, extra);
+                                                 nc.splits, nc.splits > 1, cus, cm, extra, t_items);
   }
 
   // Cascade estimate (only meaningful when something is shared): the
@@ -540,11 +581,23 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->max_suffix_len = (int32_t)max_suffix;
     suf = choose_suffix(*pl, cus, true);
     const double t_suf = est_suffix_us(*pl, suffix_tokens, suffix_padded_flops(*pl, qsl, seq_lens, kstart.data()),
-                                       suf.splits, false, cus, cm, 0.0);
+                                       suf.splits, false, cus, cm, 0.0, 0.0);
     const double merge_bytes = (double)(pre.splits + lvl1.splits + suf.splits) * total_q * pl->hq * pl->part_row_bytes() +
                                (double)total_q * pl->hq * pl->d * 2.0;
-    pl->est_us_cascade = (float)(pre_us + t_grp + cm.launch_us + t_suf +
-                                 (merge_bytes / cm.mall_bw) * 1e6 + cm.launch_us);
+    // The single launch also takes no less than its items' CU time (decode
+    // items running several KV heads pay their start-up once).
+    const double x_pre = pre.row_blocks > 1 ? cm.mfma_stage_cu_us : cm.rows_stage_cu_us;
+    const int64_t pre_items = (int64_t)pre.mtiles * pl->hkv * pre.splits;
+    const int32_t heads = pl->kv_fp8 ? 1
+                                     : pick_heads_per_item(*pl, pre_items + group_items,
+                                                           std::max<int64_t>(pre.split_tokens / kTileKeys, group_stages),
+                                                           suf, cus);
+    const double cu_us = (double)pre_items * (cm.item_cu_us + (double)(pre.split_tokens / kTileKeys) * x_pre) +
+                         (double)group_items * (cm.item_cu_us + (double)group_stages * x_pre) +
+                         items_cu_us(*pl, suf, qsl, seq_lens, kstart.data(), cm, heads);
+    const double t_launch = std::max(cm.kernel_floor_us, cu_us / cus) + cm.launch_us;
+    // one launch runs the phases (t_suf carries its launch cost), one the merge
+    pl->est_us_cascade = (float)(std::max(pre_us + t_grp + t_suf, t_launch) + est_merge_us(merge_bytes, cm) + cm.launch_us);
     pl->kv_tokens_cascade = plen + group_tokens + suffix_tokens;
   }
 
