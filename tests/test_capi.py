@@ -278,6 +278,34 @@ def test_auto_takes_the_measured_faster_path():
         assert _plan(b, mode="auto").info["use_cascade"] == casc, name
 
 
+# Shapes of the device decision sweep (32 / 8 heads, head_dim 128, seed 7)
+# where one path measured clearly faster (by 15 % or more; µs per step,
+# cascade / non-cascade): (name, N, P, suffix range, query range, cascade?)
+SWEEP_CLEAR = [
+    ("decode_n8_p256_s16", 8, 256, (16, 16), (1, 1), 0),          # 15.1 / 11.1
+    ("decode_n8_p1024_s16", 8, 1024, (16, 16), (1, 1), 1),        # 15.7 / 18.4
+    ("decode_n16_p4096_s16", 16, 4096, (16, 16), (1, 1), 1),      # 17.2 / 28.2
+    ("decode_n64_p256_s16", 64, 256, (16, 16), (1, 1), 0),        # 15.8 / 12.4
+    ("decode_n64_p1024_s512", 64, 1024, (512, 512), (1, 1), 1),   # 38.0 / 43.7
+    ("decode_n256_p1024_s16", 256, 1024, (16, 16), (1, 1), 1),    # 35.2 / 76.5
+    ("prefill_n8_p2048", 8, 2048, (64, 512), (1, 64), 1),         # 34.6 / 43.9
+    ("prefill_n32_p256", 32, 256, (64, 512), (1, 64), 0),         # 50.1 / 42.6
+    ("prefill_n128_p256", 128, 256, (64, 512), (1, 64), 0),       # 166.6 / 140.5
+]
+
+
+@pytest.mark.parametrize("name,n,p,s,q,casc", SWEEP_CLEAR, ids=[c[0] for c in SWEEP_CLEAR])
+def test_auto_matches_the_decision_sweep(name, n, p, s, q, casc):
+    """Where the device sweep found one path clearly faster, AUTO picks it
+    (host-only plan; the cost model is fitted to the kernels' measured
+    per-item, per-stage and per-launch costs)."""
+    w = workloads.Workload(name=name, num_reqs=n, prefix=p, suffix=s, q_len=q, num_q_heads=32, num_kv_heads=8,
+                           head_dim=128, seed=7)
+    info = _plan(workloads.make_batch(w), mode="auto").info
+    assert info["gates_pass"] == 1
+    assert info["use_cascade"] == casc, (info["est_us_cascade"], info["est_us_noncascade"])
+
+
 def _nested_tables(rng, n, ps=16):
     """Random block tables with a level-0 prefix, runs of requests sharing
     extra pages (sometimes only some of a run), and random lengths."""
