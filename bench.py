@@ -160,7 +160,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, steps):
 # Batch shapes of the decision sweep: decode batches (one query token) over
 # request counts, shared-prefix lengths and suffix lengths around the gates
 # (256 tokens, 8 requests) and far from them, plus chunked-prefill batches.
-SWEEP_DECODE = [(n, p, s) for n in (4, 8, 16, 64, 256) for p in (256, 1024, 4096, 16384) for s in (16, 512)]
+SWEEP_DECODE = [(n, p, s) for n in (2, 4, 8, 16, 64, 256) for p in (256, 1024, 4096, 16384) for s in (16, 512)]
 SWEEP_PREFILL = [(n, p) for n in (8, 32, 128) for p in (256, 2048)]
 
 

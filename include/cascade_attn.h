@@ -61,7 +61,7 @@ typedef enum {
  * attention": the disable_cascade_attn option; [p2] section 3: cascade is
  * only used when the heuristic says it pays). */
 typedef enum {
-  CA_MODE_AUTO = 0,       /* gates + cost model decide */
+  CA_MODE_AUTO = 0,       /* prefix and request gates + cost model decide */
   CA_MODE_FORCE_ON = 1,   /* cascade whenever the capped shared prefix is > 0 */
   CA_MODE_FORCE_OFF = 2   /* always the non-cascade path */
 } ca_mode_t;
@@ -125,7 +125,9 @@ typedef struct {
   int32_t use_cascade;                 /* 1 if run() takes the three-phase path */
   int32_t num_common_prefix_blocks;    /* pages shared by every request */
   int32_t common_prefix_len;           /* capped, page-floored shared prefix (tokens) */
-  int32_t gates_pass;                  /* prefix >= 256 tokens and >= 8 requests */
+  int32_t gates_pass;                  /* the pages' gates: prefix >= 256 tokens and >= 8 requests
+                                          (reported; AUTO's own gate is prefix >= 256 tokens and
+                                          >= 2 requests, see cascade_attn_plan) */
   int32_t prefix_splits;               /* KV splits of the prefix phase */
   int32_t prefix_row_tile;             /* packed query rows per prefix work-group */
   int32_t suffix_chunks;               /* KV chunks per request of the suffix (or only) phase */
@@ -180,9 +182,11 @@ ca_status_t cascade_attn_num_common_prefix_blocks(const int32_t* block_table_h, 
  *   num_computed_tokens_h int32 [num_reqs] (may be NULL: derived as
  *                        seq_lens - q_len; if given it must equal that)
  * and computes: the shared-page count, the capped/floored prefix length,
- * the gates (prefix >= 256 tokens, >= 8 requests; [p2] section 3), the
- * cascade/non-cascade decision (mode, then a cost model of this library's
- * kernels on params->num_cus compute units), the work partition of each
+ * the pages' gates (prefix >= 256 tokens, >= 8 requests; [p2] section 3,
+ * reported in gates_pass), the cascade/non-cascade decision (mode; in AUTO,
+ * a prefix of >= 256 tokens shared by >= 2 requests, the request gate
+ * re-derived for these kernels, then a cost model of this library's kernels
+ * on params->num_cus compute units), the work partition of each
  * phase and the workspace size. Copies nothing but derived scalars; the
  * plan is valid for every layer of the step (same metadata, any Q/KV).
  * Device is touched only when params->num_cus == 0 (to read the CU count).
