@@ -321,6 +321,21 @@ def test_request_order_table_limits(num_reqs, ordered):
         assert_close(out, lse, ref_o, ref_l, rows=rows, what=f"N={num_reqs}/{mode}")
 
 
+@pytest.mark.parametrize("num_reqs", [2, 3])
+def test_few_requests_take_the_cascade_under_auto(num_reqs):
+    """Two or three decode requests behind a 4,096-token prefix: AUTO's
+    request gate (two or more) lets the cost model pick the cascade path,
+    which matches the oracle."""
+    w = Workload(f"few{num_reqs}", num_reqs, 4096, (16, 40), (1, 1), 32, 8, 128, seed=77 + num_reqs)
+    b = workloads.make_batch(w)
+    ref_o, ref_l = oracle_ref(b)
+    out, lse, info = run(DeviceBatch(b), mode="auto")
+    log(f"[few requests] N={num_reqs} cascade={info['use_cascade']} gates_pass={info['gates_pass']} "
+        f"psplit={info['prefix_splits']}")
+    assert info["gates_pass"] == 0 and info["use_cascade"] == 1
+    assert_close(out, lse, ref_o, ref_l, what=f"few{num_reqs}/auto")
+
+
 @pytest.mark.parametrize("mode", ["on", "off"])
 def test_long_prefill_chunks(mode):
     """Four requests with 1,100-1,600 query tokens each over a 2,048-token
