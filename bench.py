@@ -102,11 +102,34 @@ def step_distribution(fn, steps, rotate):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
-def cpu_baseline(b, kv_bytes, budget_s=15.0, max_runs=60):
-    """The fp64 oracle (test infrastructure) on this host, one BLAS thread,
-    over the whole batch, repeated for about budget_s seconds."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Threads the host gives this process: the affinity mask, capped by
+    OMP_NUM_THREADS when that is set (the GPU machine sets it to its CPU share)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(b, kv_bytes, budget_s=12.0, max_runs=60):
+    """The fp64 oracle (test infrastructure) on this host over the whole
+    batch, repeated for about budget_s seconds per thread count: with every
+    host thread given to numpy's BLAS, and with one. The oracle is the plain
+    definition, untuned; it loops over requests and heads in Python, so
+    extra BLAS threads help it little."""
     import oracle
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
     w = b.workload
     if w.kv_dtype == "fp8":   # the oracle decodes the e4m3 codes itself
         kc = oracle.fp8_e4m3_decode(b.k_cache.numpy()) * w.k_scale
@@ -115,17 +138,33 @@ def cpu_baseline(b, kv_bytes, budget_s=15.0, max_runs=60):
         kc, vc = b.k_cache.float().numpy(), b.v_cache.float().numpy()
     args = (b.q.float().numpy(), kc, vc, b.block_table.numpy(), b.query_start_loc.numpy(),
             b.seq_lens.numpy(), b.workload.page_size)
-    times = []
-    t_start = time.perf_counter()
-    with threadpool_limits(1):
-        while len(times) < max_runs and (time.perf_counter() - t_start) < budget_s:
-            t0 = time.perf_counter()
-            oracle.attention_full(*args)
-            times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole batch ({b.workload.num_reqs} requests) x {len(times)} runs "
-                      f"({sum(times):.1f} s), median {t:.3f} s per batch; fp64 numpy, 1 BLAS thread"}
+
+    def run(threads):
+        times = []
+        t_start = time.perf_counter()
+        with threadpool_limits(threads):
+            blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+            while len(times) < max_runs and (time.perf_counter() - t_start) < budget_s:
+                t0 = time.perf_counter()
+                oracle.attention_full(*args)
+                times.append(time.perf_counter() - t0)
+        return statistics.median(times), len(times), sum(times), (blas[0] if blas else None)
+
+    n = host_threads()
+    t_all, runs_all, tot_all, blas_all = run(n)
+    t_one, runs_one, tot_one, _ = run(1)
+    legs = {"all_threads": {"value": round(kv_bytes / t_all / 1e9, 4), "unit": "GB/s", "cores": n,
+                            "sample": f"{runs_all} runs ({tot_all:.1f} s), median {t_all:.3f} s per batch, "
+                                      f"{blas_all} BLAS threads"},
+            "one_thread": {"value": round(kv_bytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"{runs_one} runs ({tot_one:.1f} s), median {t_one:.3f} s per batch"}}
+    # the headline figure is the faster configuration; both are recorded
+    best = "all_threads" if t_all <= t_one else "one_thread"
+    t_best = min(t_all, t_one)
+    return {"value": legs[best]["value"], "unit": "GB/s", "cores": legs[best]["cores"], "kind": "oracle",
+            "sample": f"whole batch ({w.num_reqs} requests, every row), median {t_best:.3f} s per batch; fp64 "
+                      f"numpy ({best.replace('_', ' ')}: the faster of {n} BLAS threads and 1)",
+            "cpu_model": cpu_model(), "host_threads": n, **legs}
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, steps):
@@ -205,10 +244,10 @@ def decision_sweep(steps, warmup):
             times[mode] = step_distribution(f, steps, rotate)["p50"]   # median, robust to stray slow steps
             infos[mode] = pl.info
             if mode != "auto":
-                spa.cascade_attn_profile_enable(True)
+                spa.cascade_attn_profile_enable(4 * steps)
                 time_steps(f, steps, rotate)
-                spa.cascade_attn_profile_enable(False)
                 kern[mode] = {k: round(t * 1e3 / c, 2) for k, (t, c) in spa.cascade_attn_profile_read().items() if c}
+                spa.cascade_attn_profile_enable(0)
         casc = bool(infos["auto"]["use_cascade"])
         best = min(times["on"], times["off"])
         chosen = times["on"] if casc else times["off"]
@@ -320,14 +359,16 @@ def main():
 
     for i in range(args.warmup):
         step(i % rotate)
+    # The timed loop: each kernel launch carries a start / stop event pair
+    # from a pool created before the loop (no host work is added between
+    # launches), so the per-kernel durations come from the timed steps
+    # themselves; a second loop without the events shows what they cost.
+    spa.cascade_attn_profile_enable(4 * args.steps)
     ms = time_steps(step, args.steps, rotate)
-    dist = step_distribution(step, args.steps, rotate)
-
-    # per-kernel durations: HIP events around every launch, on the run's stream
-    spa.cascade_attn_profile_enable(True)
-    ms_prof = time_steps(step, args.steps, rotate)
-    spa.cascade_attn_profile_enable(False)
     prof = spa.cascade_attn_profile_read()
+    spa.cascade_attn_profile_enable(0)
+    ms_plain = time_steps(step, args.steps, rotate)
+    dist = step_distribution(step, args.steps, rotate)
     kern = {}
     for kind, (tot_ms, cnt) in prof.items():
         if cnt:
@@ -375,10 +416,10 @@ def main():
         step_sep = step_with(plan_sep, workspace_for(plan_sep))
         for i in range(args.warmup):
             step_sep(i % rotate)
-        spa.cascade_attn_profile_enable(True)
+        spa.cascade_attn_profile_enable(4 * max(10, args.steps // 2))
         ms_sep = time_steps(step_sep, max(10, args.steps // 2), rotate)
-        spa.cascade_attn_profile_enable(False)
         prof_sep = spa.cascade_attn_profile_read()
+        spa.cascade_attn_profile_enable(0)
         # second shared level: each group's extra positions once, its queries
         groups = spa.cascade_attn_plan_groups(plan_sep)
         qsl_l = b.query_start_loc.tolist()
@@ -436,7 +477,7 @@ def main():
                    "kv_bytes_per_step": kv_bytes, "rotating_copies": rotate},
         "roofline": roof,
         "kernels": kern,
-        "profiled_us_per_step": round(ms_prof * 1e3, 3),
+        "us_per_step_without_kernel_events": round(ms_plain * 1e3, 3),
         "warm_us_per_step": round(ms_warm * 1e3, 3),
         "plan": {k: info[k] for k in ("prefix_splits", "prefix_row_tile", "num_level1_groups", "level1_splits",
                                        "suffix_chunks", "suffix_chunk_tokens", "suffix_kernel", "num_partial_slots",

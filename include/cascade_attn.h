@@ -119,6 +119,12 @@ typedef struct {
   int32_t partials_fp32;       /* partial outputs of the phases before the merge: 0 = bf16 (the
                                   attention dtype, as [p2] section 8 Step 5 merges the two phases'
                                   outputs), 1 = fp32; partial LSEs are fp32 either way */
+  int32_t use_tuned;           /* 0 (default) = AUTO is a pure function of the batch and these
+                                  params; 1 = an AUTO plan whose batch shape has a choice recorded
+                                  by cascade_attn_autotune / cascade_attn_autotune_record takes
+                                  that choice. Off by default so that a request's output bits never
+                                  depend on what the process tuned before ([p1]: output that
+                                  changes with batch composition is the failure to avoid) */
 } ca_params_t;
 
 typedef struct {
@@ -198,7 +204,10 @@ ca_status_t cascade_attn_plan(const ca_params_t* params, const int32_t* block_ta
                               const int32_t* query_start_loc_h, const int32_t* seq_lens_h,
                               const int32_t* num_computed_tokens_h, ca_plan_t* out_plan);
 
-/* Copies the plan's decisions and sizes into *out. */
+/* Copies the plan's decisions and sizes (the quantities of [p2] section 8
+ * Steps 1-3: shared pages, capped prefix length, gates and decision, and
+ * the per-phase partition) into *out. Errors: CA_EINVAL for a null plan or
+ * output. */
 ca_status_t cascade_attn_plan_info(ca_plan_t plan, ca_plan_info_t* out);
 
 /*
@@ -266,8 +275,8 @@ ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache,
  * than workspace_bytes are skipped. Returns the fastest plan in *out_plan
  * (the caller destroys it) and its mean time per run in *out_us (may be
  * NULL), and records the choice for this batch shape: later AUTO plans with
- * no explicit overrides (prefix_splits, heads_per_item, max_levels all 0)
- * and the same shape apply it. A shape is (num_reqs, head counts, head_dim,
+ * params->use_tuned = 1, no explicit overrides (prefix_splits,
+ * heads_per_item, max_levels all 0) and the same shape apply it. A shape is (num_reqs, head counts, head_dim,
  * kv_dtype, window, and the power-of-two buckets of the shared prefix, total
  * queries, longest query, mean remaining length and second-level group
  * count). Synchronises the stream; not for graph capture. out, lse_out and
@@ -284,7 +293,23 @@ ca_status_t cascade_attn_autotune(const ca_params_t* params, const int32_t* bloc
                                   size_t workspace_bytes, void* stream, int32_t iters, ca_plan_t* out_plan,
                                   float* out_us);
 
-/* Forgets every shape recorded by cascade_attn_autotune. */
+/*
+ * Records a choice for the batch's shape without timing anything (host only;
+ * e.g. to restore choices a previous process tuned). The shape is that of
+ * the AUTO plan of (params, metadata), as cascade_attn_autotune records it;
+ * the choice is the mode (CA_MODE_FORCE_ON or CA_MODE_FORCE_OFF) and the
+ * ca_params_t settings prefix_splits, heads_per_item and max_levels (0 =
+ * planner's choice). Only plans made with params->use_tuned = 1 consult it.
+ * Errors: as cascade_attn_plan; CA_EINVAL for a mode other than FORCE_ON /
+ * FORCE_OFF or a negative setting.
+ */
+ca_status_t cascade_attn_autotune_record(const ca_params_t* params, const int32_t* block_table_h,
+                                         const int32_t* query_start_loc_h, const int32_t* seq_lens_h,
+                                         const int32_t* num_computed_tokens_h, int32_t mode,
+                                         int32_t prefix_splits, int32_t heads_per_item, int32_t max_levels);
+
+/* Forgets every shape recorded by cascade_attn_autotune or
+ * cascade_attn_autotune_record. */
 void cascade_attn_autotune_reset(void);
 
 /* Frees a plan (NULL is accepted). */
@@ -294,20 +319,26 @@ void cascade_attn_plan_destroy(ca_plan_t plan);
 const char* cascade_attn_last_error(void);
 
 /*
- * Kernel timing for measurement. While enabled, run() records a HIP event
- * pair around every kernel it launches, on the launch stream.
- * cascade_attn_profile_read() waits for the recorded events, writes the
- * summed milliseconds and launch counts per kernel kind into
- * ms[CA_PROFILE_KINDS] and counts[CA_PROFILE_KINDS], and clears the record.
+ * Kernel timing for measurement. cascade_attn_profile_enable(capacity)
+ * creates a pool of 2 * capacity HIP events (call it outside any timed
+ * region; 0 disables timing and frees the pool). While enabled, each kernel
+ * run() launches takes the next start / stop pair of the pool and carries it
+ * on its own dispatch (the events bracket that kernel's execution on the
+ * launch stream; no event is created during run()); launches past the
+ * pool's capacity run untimed. cascade_attn_profile_read() waits for the
+ * recorded events, writes the summed milliseconds and launch counts per
+ * kernel kind into ms[CA_PROFILE_KINDS] and counts[CA_PROFILE_KINDS], and
+ * makes the whole pool available again.
  * Kinds: 0 = cascade phases (prefix and suffix work-groups of the cascade
  * path in one launch), 1 = tiled attention of the non-cascade path,
  * 2 = merge, 3 = decode attention of the non-cascade path, 4 = prefix phase,
  * 5 = suffix phase and 6 = group level when a plan runs the phases as
  * separate launches.
- * Errors: CA_EHIP if an event call fails, CA_EINVAL for null outputs.
+ * Errors: CA_EINVAL (capacity outside [0, 2^20], null outputs), CA_EHIP if
+ * an event call fails.
  */
 #define CA_PROFILE_KINDS 7
-ca_status_t cascade_attn_profile_enable(int32_t enable);
+ca_status_t cascade_attn_profile_enable(int32_t capacity);
 ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts);
 
 #ifdef __cplusplus

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     CascadeAttnError,
     Plan,
     cascade_attn_autotune,
+    cascade_attn_autotune_record,
     cascade_attn_autotune_reset,
     cascade_attn_num_common_prefix_blocks,
     cascade_attn_plan,

@@ -55,6 +55,7 @@ class ca_params_t(ctypes.Structure):
         ("prefix_splits", ctypes.c_int32),
         ("suffix_order", ctypes.c_int32),
         ("partials_fp32", ctypes.c_int32),
+        ("use_tuned", ctypes.c_int32),
     ]
 
 
@@ -120,6 +121,8 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_autotune.argtypes = [ctypes.POINTER(ca_params_t), _i32p, _i32p, _i32p, _i32p] + \
         [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.POINTER(ctypes.c_float)]
+    lib.cascade_attn_autotune_record.argtypes = [ctypes.POINTER(ca_params_t), _i32p, _i32p, _i32p, _i32p] + \
+        [ctypes.c_int32] * 4
     lib.cascade_attn_autotune_reset.argtypes = []
     lib.cascade_attn_autotune_reset.restype = None
     lib.cascade_attn_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -127,7 +130,8 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_profile_enable.argtypes = [ctypes.c_int32]
     lib.cascade_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("cascade_attn_num_common_prefix_blocks", "cascade_attn_plan", "cascade_attn_plan_info",
-                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_autotune", "cascade_attn_profile_enable", "cascade_attn_profile_read"):
+                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_autotune", "cascade_attn_autotune_record",
+                 "cascade_attn_profile_enable", "cascade_attn_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -201,7 +205,7 @@ def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: in
             mode="auto", num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
             max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0,
             sliding_window: int = 0, prefix_splits: int = 0, suffix_order: int = 0,
-            partials_fp32: bool = False):
+            partials_fp32: bool = False, use_tuned: bool = False):
     """ca_params_t plus the host metadata arrays and their pointers."""
     bt, bt_p = _host_i32(block_table)
     qsl, qsl_p = _host_i32(query_start_loc)
@@ -233,6 +237,7 @@ def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: in
     prm.prefix_splits = int(prefix_splits)
     prm.suffix_order = int(suffix_order)
     prm.partials_fp32 = int(partials_fp32)
+    prm.use_tuned = int(use_tuned)
     keep = (bt, qsl, sl, nc)   # the arrays behind the pointers
     return prm, (bt_p, qsl_p, sl_p, nc_p), keep
 
@@ -246,7 +251,7 @@ def cascade_attn_plan(**kw) -> Plan:
     arrays or CPU tensors), and the optional ca_params_t settings
     softmax_scale, mode, num_cus, heads_per_item, separate_phases,
     max_levels, kv_dtype, k_scale, v_scale, sliding_window, prefix_splits,
-    suffix_order, partials_fp32.
+    suffix_order, partials_fp32, use_tuned.
     """
     prm, ptrs, keep = _params(**kw)
     h = ctypes.c_void_p(0)
@@ -276,6 +281,17 @@ def cascade_attn_autotune(q, k_cache, v_cache, block_table_d, query_start_loc_d,
         ctypes.byref(us)))
     del keep
     return Plan(h.value), float(us.value)
+
+
+def cascade_attn_autotune_record(mode="on", prefix_splits: int = 0, heads_per_item: int = 0, max_levels: int = 0,
+                                 **kw) -> None:
+    """Records a choice for the batch shape of ``kw`` (as for
+    cascade_attn_plan) without timing; see the header."""
+    prm, ptrs, keep = _params(**kw)
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(load().cascade_attn_autotune_record(ctypes.byref(prm), *ptrs, m, int(prefix_splits), int(heads_per_item),
+                                               int(max_levels)))
+    del keep
 
 
 def cascade_attn_autotune_reset() -> None:
@@ -321,8 +337,10 @@ def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start
         lse_out.data_ptr() if lse_out is not None else None, ws_ptr, ws_bytes, s))
 
 
-def cascade_attn_profile_enable(enable: bool = True) -> None:
-    _check(load().cascade_attn_profile_enable(1 if enable else 0))
+def cascade_attn_profile_enable(capacity: int = 4096) -> None:
+    """Creates a pool of timing events for ``capacity`` kernel launches (0:
+    timing off, pool freed); see the header."""
+    _check(load().cascade_attn_profile_enable(int(capacity)))
 
 
 def cascade_attn_profile_read():

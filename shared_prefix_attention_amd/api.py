@@ -28,7 +28,8 @@ def plan_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, k_cache: t
                layout: str = "NHD", mode="auto", softmax_scale: float = 0.0, num_cus: int = 0,
                heads_per_item: int = 0, separate_phases: bool = False, max_levels: int = 0,
                kv_dtype=None, k_scale: float = 0.0, v_scale: float = 0.0, sliding_window: int = 0,
-               prefix_splits: int = 0, suffix_order: int = 0, partials_fp32: bool = False) -> Plan:
+               prefix_splits: int = 0, suffix_order: int = 0, partials_fp32: bool = False,
+               use_tuned: bool = False) -> Plan:
     """Plan from host metadata; strides and pool size are read off ``k_cache``.
 
     kv_dtype: "bf16" or "fp8"; by default taken from ``k_cache`` (bf16, or a
@@ -43,7 +44,7 @@ def plan_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, k_cache: t
         softmax_scale=softmax_scale, mode=mode, num_cus=num_cus, heads_per_item=heads_per_item,
         separate_phases=separate_phases, max_levels=max_levels, kv_dtype=kv_dtype, k_scale=k_scale,
         v_scale=v_scale, sliding_window=sliding_window, prefix_splits=prefix_splits, suffix_order=suffix_order,
-        partials_fp32=partials_fp32)
+        partials_fp32=partials_fp32, use_tuned=use_tuned)
 
 
 def run_batch(plan: Plan, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

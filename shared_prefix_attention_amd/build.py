@@ -8,6 +8,7 @@ it travels with the source tree.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -37,6 +38,35 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
+def check_resource_usage(remarks: str) -> list:
+    """Parses hipcc's kernel-resource-usage remarks and returns one record per
+    kernel. The LDS reads of the attention kernels are inline asm whose
+    results the code waits for by hand (an explicit lgkmcnt wait that names
+    the destination registers); that is only sound while the compiler keeps
+    every such register in place, i.e. never spills or moves it through
+    scratch memory. So any kernel with scratch or spills fails the build."""
+    kernels = []
+    cur = None
+    for line in remarks.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            kernels.append(cur)
+            continue
+        m = re.search(r"remark:\s+(ScratchSize \[bytes/lane\]|SGPRs Spill|VGPRs Spill|VGPRs|AGPRs|"
+                      r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]|Dynamic Stack): (\S+)", line)
+        if m and cur is not None:
+            cur[m.group(1)] = m.group(2)
+    bad = [k for k in kernels if k.get("ScratchSize [bytes/lane]", "0") != "0" or k.get("SGPRs Spill", "0") != "0"
+           or k.get("VGPRs Spill", "0") != "0" or k.get("Dynamic Stack", "False") != "False"]
+    if not kernels:
+        raise RuntimeError("no kernel-resource-usage remarks found in the HIP compile output")
+    if bad:
+        raise RuntimeError("kernels use scratch memory or spill registers (the inline-asm LDS reads rely on "
+                           "neither): " + "; ".join(f"{k['name']}: {k}" for k in bad))
+    return kernels
+
+
 def build(verbose: bool = True) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objdir = os.path.join(PKG, "_build")
@@ -47,10 +77,37 @@ def build(verbose: bool = True) -> str:
         _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
               "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    usage = []
     for src in HIP_SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        _run([hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmd = [hipcc, *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        print("+", " ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise subprocess.CalledProcessError(r.returncode, cmd)
+        usage += check_resource_usage(r.stderr)
         objs.append(obj)
+        # the compiler's own gfx950 assembly of the same source: every
+        # inline-asm LDS read is waited for before any use of its registers
+        asm_path = os.path.join(objdir, src + ".s")
+        _run([hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC,
+              os.path.join(CSRC, src), "-o", asm_path])
+        from shared_prefix_attention_amd import lds_wait_check
+        nfun, nreads, problems = lds_wait_check.check(open(asm_path).read())
+        if problems:
+            raise RuntimeError(f"{len(problems)} uses of inline-asm LDS read results before their wait:\n" +
+                               "\n".join(problems[:20]))
+        if verbose:
+            print(f"  {nfun} kernels, {nreads} inline-asm LDS reads: every result waited for before use",
+                  flush=True)
+    with open(os.path.join(objdir, "kernel_resource_usage.txt"), "w") as f:
+        for k in usage:
+            f.write(" ".join(f"{key}={val}" for key, val in k.items()) + "\n")
+    if verbose:
+        print(f"  {len(usage)} kernels: no scratch, no spills; max VGPRs "
+              f"{max(int(k.get('VGPRs', 0)) for k in usage)}", flush=True)
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

@@ -386,8 +386,8 @@ extern "C" int ca_query_num_cus(int32_t* out);
 extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* bt, const int32_t* qsl,
                                          const int32_t* seq_lens, const int32_t* num_computed,
                                          ca_plan_t* out_plan) {
+  if (out_plan) *out_plan = nullptr;   // no plan on any error
   if (!prm || !bt || !qsl || !seq_lens || !out_plan) return fail(CA_EINVAL, "null pointer argument");
-  *out_plan = nullptr;
   const ca_params_t& p = *prm;
   if (p.num_reqs <= 0) return fail(CA_EINVAL, "num_reqs must be >= 1");
   if (p.num_q_heads <= 0 || p.num_kv_heads <= 0) return fail(CA_EINVAL, "head counts must be >= 1");
@@ -410,6 +410,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.prefix_splits < 0) return fail(CA_EINVAL, "prefix_splits must be >= 0");
   if (p.suffix_order != 0 && p.suffix_order != 1) return fail(CA_EINVAL, "suffix_order must be 0 or 1");
   if (p.partials_fp32 != 0 && p.partials_fp32 != 1) return fail(CA_EINVAL, "partials_fp32 must be 0 or 1");
+  if (p.use_tuned != 0 && p.use_tuned != 1) return fail(CA_EINVAL, "use_tuned must be 0 or 1");
   if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
   if (p.kv_dtype == CA_KV_FP8_E4M3) {
     if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
@@ -663,11 +664,13 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->ws_lse_offset = 0;
     pl->workspace_bytes = 0;
   }
-  // A choice the autotuner recorded for this shape replaces AUTO's, unless
-  // the caller fixed one of the tuned settings.
+  // With use_tuned, a choice recorded for this shape replaces AUTO's, unless
+  // the caller fixed one of the tuned settings. Without it (the default) the
+  // plan depends on the batch and the params only.
   TunedChoice tc;
-  if (p.mode == CA_MODE_AUTO && p.prefix_splits == 0 && p.heads_per_item == 0 && p.max_levels == 0 &&
-      tune_lookup(*pl, &tc) && tc.mode != CA_MODE_AUTO) {
+  if (p.use_tuned == 1 && p.mode == CA_MODE_AUTO && p.prefix_splits == 0 && p.heads_per_item == 0 &&
+      p.max_levels == 0 && tune_lookup(*pl, &tc) && tc.mode != CA_MODE_AUTO &&
+      !(tc.mode == CA_MODE_FORCE_ON && pl->window > 0)) {
     ca_params_t q2 = p;
     q2.mode = tc.mode;
     q2.prefix_splits = tc.prefix_splits;
@@ -727,3 +730,35 @@ extern "C" ca_status_t cascade_attn_plan_groups(ca_plan_t pl, int32_t capacity, 
 }
 
 extern "C" void cascade_attn_plan_destroy(ca_plan_t pl) { delete pl; }
+
+extern "C" ca_status_t cascade_attn_autotune_record(const ca_params_t* params, const int32_t* bt, const int32_t* qsl,
+                                                    const int32_t* seq_lens, const int32_t* num_computed,
+                                                    int32_t mode, int32_t prefix_splits, int32_t heads_per_item,
+                                                    int32_t max_levels) {
+  if (!params) return fail(CA_EINVAL, "null pointer argument");
+  if (mode != CA_MODE_FORCE_ON && mode != CA_MODE_FORCE_OFF) return fail(CA_EINVAL, "mode must be FORCE_ON or FORCE_OFF");
+  if (prefix_splits < 0 || heads_per_item < 0 || max_levels < 0 || max_levels > 2)
+    return fail(CA_EINVAL, "prefix_splits, heads_per_item must be >= 0 and max_levels in [0, 2]");
+  // the shape key is that of the AUTO plan, made without the table
+  ca_params_t p = *params;
+  p.mode = CA_MODE_AUTO;
+  p.use_tuned = 0;
+  p.prefix_splits = 0;
+  p.heads_per_item = 0;
+  p.max_levels = 0;
+  ca_plan_t base = nullptr;
+  const ca_status_t st = cascade_attn_plan(&p, bt, qsl, seq_lens, num_computed, &base);
+  if (st != CA_OK) return st;
+  if (mode == CA_MODE_FORCE_ON && base->window > 0) {
+    cascade_attn_plan_destroy(base);
+    return fail(CA_EUNSUPPORTED, "cascade cannot run with a binding sliding window");
+  }
+  TunedChoice c;
+  c.mode = mode;
+  c.prefix_splits = prefix_splits;
+  c.heads_per_item = heads_per_item;
+  c.max_levels = max_levels;
+  tune_record(*base, c);
+  cascade_attn_plan_destroy(base);
+  return CA_OK;
+}

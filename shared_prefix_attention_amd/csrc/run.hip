@@ -27,35 +27,53 @@ static_assert(kMaxGroups == kMaxLevel1Groups, "group table size");
 static_assert(kOrderCapacity == kMaxOrderedReqs, "request order table size");
 static_assert(K_KINDS == CA_PROFILE_KINDS, "profile kinds");
 
+// Kernel timing for measurement: a pool of HIP events created when timing
+// is enabled (outside any timed region); each launch takes the next start /
+// stop pair and carries it on its own dispatch (hipExtLaunchKernelGGL), so
+// the recorded time is the kernel's execution, with no event creation or
+// other host work added between launches. When the pool is used up, further
+// launches run untimed.
 struct Profiler {
   std::mutex mu;
   bool enabled = false;
+  std::vector<hipEvent_t> pool;   // 2 * capacity events
   struct Rec {
     int kind;
-    hipEvent_t a, b;
+    int slot;                     // events pool[2 slot], pool[2 slot + 1]
   };
   std::vector<Rec> recs;
+  size_t next = 0;
+  int64_t dropped = 0;            // launches past the pool's capacity
+  void release() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    pool.clear();
+    recs.clear();
+    next = 0;
+    dropped = 0;
+  }
 };
 Profiler g_prof;
 
-// Launches `kernel`; while timing is enabled the launch carries a start /
-// stop event pair on its own dispatch (hipExtLaunchKernelGGL), so the
-// recorded time is the kernel's execution only.
 template <typename K, typename... Args>
 void launch(int kind, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
-  bool timed = false;
   hipEvent_t a = nullptr, b = nullptr;
   {
     std::lock_guard<std::mutex> g(g_prof.mu);
-    timed = g_prof.enabled;
+    if (g_prof.enabled) {
+      if (2 * g_prof.next + 1 < g_prof.pool.size()) {
+        a = g_prof.pool[2 * g_prof.next];
+        b = g_prof.pool[2 * g_prof.next + 1];
+        g_prof.recs.push_back({kind, (int)g_prof.next});
+        ++g_prof.next;
+      } else {
+        ++g_prof.dropped;
+      }
+    }
   }
-  if (timed && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess) {
+  if (a) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
-    std::lock_guard<std::mutex> g(g_prof.mu);
-    g_prof.recs.push_back({kind, a, b});
     return;
   }
-  if (a) (void)hipEventDestroy(a);
   hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
@@ -338,35 +356,48 @@ extern "C" ca_status_t cascade_attn_run(ca_plan_t pl, const void* q, const void*
                       workspace, s);
 }
 
-extern "C" ca_status_t cascade_attn_profile_enable(int32_t enable) {
+extern "C" ca_status_t cascade_attn_profile_enable(int32_t capacity) {
+  if (capacity < 0 || capacity > (1 << 20)) return fail(CA_EINVAL, "capacity must be in [0, 2^20]");
   std::lock_guard<std::mutex> g(g_prof.mu);
-  g_prof.enabled = enable != 0;
+  g_prof.release();
+  g_prof.enabled = false;
+  if (capacity == 0) return CA_OK;
+  g_prof.pool.reserve(2 * (size_t)capacity);
+  for (int32_t i = 0; i < 2 * capacity; ++i) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+      g_prof.release();
+      return fail(CA_EHIP, "event creation failed");
+    }
+    g_prof.pool.push_back(e);
+  }
+  g_prof.recs.reserve(capacity);
+  g_prof.enabled = true;
   return CA_OK;
 }
 
 extern "C" ca_status_t cascade_attn_profile_read(double* ms, int64_t* counts) {
   if (!ms || !counts) return fail(CA_EINVAL, "null output");
-  std::vector<Profiler::Rec> recs;
-  {
-    std::lock_guard<std::mutex> g(g_prof.mu);
-    recs.swap(g_prof.recs);
-  }
+  std::lock_guard<std::mutex> g(g_prof.mu);
   for (int i = 0; i < K_KINDS; ++i) {
     ms[i] = 0.0;
     counts[i] = 0;
   }
   ca_status_t st = CA_OK;
-  for (auto& r : recs) {
+  for (const auto& r : g_prof.recs) {
     float t = 0.f;
-    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+    hipEvent_t a = g_prof.pool[2 * r.slot], b = g_prof.pool[2 * r.slot + 1];
+    if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&t, a, b) != hipSuccess) {
       st = fail(CA_EHIP, "event timing failed");
     } else {
       ms[r.kind] += t;
       counts[r.kind] += 1;
     }
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
   }
+  // the pool is reused from its start; launches past its capacity were untimed
+  g_prof.recs.clear();
+  g_prof.next = 0;
+  g_prof.dropped = 0;
   return st;
 }
 
@@ -388,6 +419,7 @@ extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const in
   base_p.prefix_splits = 0;
   base_p.heads_per_item = 0;
   base_p.max_levels = 0;
+  base_p.use_tuned = 0;
   ca_plan_t base = nullptr;
   ca_status_t st = cascade_attn_plan(&base_p, block_table_h, query_start_loc_h, seq_lens_h, num_computed_tokens_h,
                                      &base);

@@ -1,8 +1,9 @@
 """On-device autotuning: cascade_attn_autotune times candidate plans with the
 caller's data and returns the fastest; the choice is recorded for the batch
-shape, so a later AUTO plan of that shape takes it. Every candidate computes
-the same attention, so the tuned plan is checked against the oracle like any
-other."""
+shape, so a later AUTO plan of that shape that opts in (use_tuned) takes it,
+while default AUTO plans stay a function of the batch alone. Every candidate
+computes the same attention, so the tuned plan is checked against the oracle
+like any other."""
 
 import numpy as np
 import pytest
@@ -10,7 +11,7 @@ import torch
 
 import workloads
 import shared_prefix_attention_amd as spa
-from parity_util import DeviceBatch, assert_close, log, oracle_ref, plan, rows_of
+from parity_util import DeviceBatch, assert_close, log, oracle_ref, plan
 
 pytestmark = pytest.mark.gpu
 
@@ -18,6 +19,14 @@ pytestmark = pytest.mark.gpu
 def setup_module():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+
+
+@pytest.fixture(autouse=True)
+def _clean_tuning_table():
+    """Every test starts and ends with an empty tuning table, pass or fail."""
+    spa.cascade_attn_autotune_reset()
+    yield
+    spa.cascade_attn_autotune_reset()
 
 
 def _plan_kw(b):
@@ -34,7 +43,6 @@ def _plan_kw(b):
 @pytest.mark.parametrize("name", ["tiny_decode", "worked_decode", "mixed_prefill", "multi_doc", "worked_decode_fp8"])
 def test_autotune_picks_a_valid_plan_and_records_it(name):
     log(f"[autotune] {name}")
-    spa.cascade_attn_autotune_reset()
     b = workloads.make_batch(workloads.get(name))
     db = DeviceBatch(b)
     auto = plan(b, mode="auto")
@@ -51,24 +59,23 @@ def test_autotune_picks_a_valid_plan_and_records_it(name):
     # the tuned plan computes the batch's attention
     spa.cascade_attn_run(tuned, db.q, db.k, db.v, db.bt, db.qsl, db.sl, out, lse, ws)
     torch.cuda.synchronize()
-    reqs = list(range(b.workload.num_reqs)) if b.workload.num_reqs <= 8 else [0, b.workload.num_reqs // 2,
-                                                                             b.workload.num_reqs - 1]
-    ref_o, ref_l = oracle_ref(b, requests=reqs)
-    rows = rows_of(b, reqs)
-    assert_close(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, rows=rows, what=f"{name}/tuned")
-    # a later AUTO plan of the same shape takes the recorded choice
-    again = plan(b, mode="auto").info
+    ref_o, ref_l = oracle_ref(b)
+    assert_close(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, what=f"{name}/tuned")
+    # a later AUTO plan of the same shape that opts in takes the recorded choice
+    again = plan(b, mode="auto", use_tuned=True).info
     for k in ("use_cascade", "prefix_splits", "suffix_heads_per_item", "num_level1_groups", "num_partial_slots"):
         assert again[k] == info[k], k
+    # a default AUTO plan ignores the record
+    default = plan(b, mode="auto").info
+    assert default == auto.info
     spa.cascade_attn_autotune_reset()
-    fresh = plan(b, mode="auto").info
-    assert fresh["use_cascade"] == auto.info["use_cascade"] and fresh["prefix_splits"] == auto.info["prefix_splits"]
+    fresh = plan(b, mode="auto", use_tuned=True).info
+    assert fresh == auto.info
 
 
 def test_autotune_skips_candidates_that_do_not_fit_the_workspace():
     """Without a workspace only plans that need none can run; the worked
     example's cascade plans all need one."""
-    spa.cascade_attn_autotune_reset()
     b = workloads.make_batch(workloads.get("tiny_decode"))
     db = DeviceBatch(b)
     out = torch.empty_like(db.q)
@@ -80,4 +87,3 @@ def test_autotune_skips_candidates_that_do_not_fit_the_workspace():
         assert e.status == 4   # CA_EWORKSPACE: nothing fits
     else:
         assert tuned.workspace_bytes == 0
-    spa.cascade_attn_autotune_reset()

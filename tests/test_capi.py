@@ -14,7 +14,14 @@ import workloads
 import shared_prefix_attention_amd as spa
 from shared_prefix_attention_amd import _lib
 
-pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+@pytest.fixture(scope="module", autouse=True)
+def _library_built():
+    """A checkout without the built library builds it here (host compile
+    only) rather than skipping the boundary and planner tests."""
+    if not os.path.exists(_lib.LIB_PATH):
+        from shared_prefix_attention_amd.build import build
+        build()
 
 
 def test_library_exports_every_header_symbol():
@@ -486,3 +493,43 @@ def test_noncascade_chunking_pays_for_the_merge():
         assert info["suffix_chunks"] == 1 and info["num_partial_slots"] == 0, name
     info = _plan(workloads.make_batch(workloads.get("long_doc_n8")), mode="off").info
     assert info["suffix_chunks"] > 1 and info["num_partial_slots"] == info["suffix_chunks"]
+
+
+def test_auto_is_a_function_of_the_batch_unless_tuning_is_asked_for():
+    """A recorded tuning choice never changes a default AUTO plan: the same
+    batch planned before and after the record gets identical plans. Only a
+    plan that opts in (use_tuned) takes the record, and a reset forgets it.
+    ("Diary - vLLM's cascade attention": output that depends on what else
+    happened in the process is the failure to avoid.)"""
+    wd = workloads.make_batch(workloads.get("worked_decode"))
+    w = wd.workload
+    kw = dict(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size,
+              num_pages=wd.num_pages, kv_strides=spa.kv_strides(wd.k_cache), block_table=wd.block_table,
+              query_start_loc=wd.query_start_loc, seq_lens=wd.seq_lens, num_computed_tokens=wd.num_computed,
+              num_cus=256)
+    try:
+        spa.cascade_attn_autotune_reset()
+        before = _plan(wd, mode="auto").info
+        before_opt_in = _plan(wd, mode="auto", use_tuned=True).info
+        assert before_opt_in == before and before["use_cascade"] == 1
+        spa.cascade_attn_autotune_record(mode="off", **kw)
+        assert _plan(wd, mode="auto").info == before
+        tuned = _plan(wd, mode="auto", use_tuned=True).info
+        assert tuned["use_cascade"] == 0
+        # an explicit setting keeps the record out even when opted in
+        assert _plan(wd, mode="auto", use_tuned=True, max_levels=1).info["use_cascade"] == 1
+        spa.cascade_attn_autotune_record(mode="on", prefix_splits=4, **kw)
+        tuned = _plan(wd, mode="auto", use_tuned=True).info
+        assert tuned["use_cascade"] == 1 and tuned["prefix_splits"] == 4
+        assert _plan(wd, mode="auto").info == before
+        spa.cascade_attn_autotune_reset()
+        assert _plan(wd, mode="auto", use_tuned=True).info == before
+        for bad in (dict(mode="auto"), dict(mode="on", prefix_splits=-1), dict(mode="on", max_levels=3)):
+            with pytest.raises(spa.CascadeAttnError) as e:
+                spa.cascade_attn_autotune_record(**bad, **kw)
+            assert e.value.status == _lib.CA_EINVAL
+        with pytest.raises(spa.CascadeAttnError) as e:
+            _plan(wd, mode="auto", use_tuned=2)
+        assert e.value.status == _lib.CA_EINVAL
+    finally:
+        spa.cascade_attn_autotune_reset()

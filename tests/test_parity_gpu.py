@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small batches are compared element by element over every output; the full
-workloads are compared on sampled requests (the oracle evaluates those rows
-only). Tolerances: |out - ref| <= 2e-2 + 1e-2 |ref| elementwise, |lse - ref|
+Every test compares every output row and LSE with the oracle: the small
+batches, and the full-size workloads at the sizes and launch configurations
+the benchmark times (the oracle runs once per full workload). Tolerances: |out - ref| <= 2e-2 + 1e-2 |ref| elementwise, |lse - ref|
 <= 1e-3. Inputs carry NaN in unused pages and in the tail slots of each
 request's last page, so any out-of-range read shows up as a non-finite output.
 """
@@ -13,7 +13,7 @@ import torch
 
 import workloads
 from workloads import Workload
-from parity_util import DeviceBatch, assert_close, log, oracle_ref, rows_of, run
+from parity_util import DeviceBatch, assert_close, log, oracle_ref, run
 
 pytestmark = pytest.mark.gpu
 
@@ -110,35 +110,51 @@ def test_small_hnd_layout(name):
         assert_close(out, lse, ref_o, ref_l, what=f"{name}/HND/{mode}")
 
 
-def _sample_requests(n, seed):
-    rng = np.random.default_rng(seed)
-    pick = {0, n - 1, n // 2}
-    pick.update(int(x) for x in rng.integers(0, n, 3))
-    return sorted(pick)
+_ORACLE = {}
+
+
+def oracle_cached(name, b):
+    """The fp64 oracle over every request of a named workload, computed once
+    per test session and shared by the tests that compare against it."""
+    if name not in _ORACLE:
+        log(f"  oracle: {name} ({b.workload.num_reqs} requests, every row)")
+        _ORACLE[name] = oracle_ref(b)
+    return _ORACLE[name]
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
-def test_full_size_sampled_parity(name):
+def test_full_size_every_row_parity(name):
+    """Every full-size workload, every output row and LSE against the fp64
+    oracle, on the AUTO plan, the forced cascade plan and the forced
+    non-cascade plan (the launch configurations the benchmark times)."""
     w = workloads.get(name)
     log(f"[parity-full] {name}")
     b = workloads.make_batch(w)
-    reqs = _sample_requests(w.num_reqs, w.seed)
-    rows = rows_of(b, reqs)
-    ref_o, ref_l = oracle_ref(b, requests=reqs)
+    ref_o, ref_l = oracle_cached(name, b)
     db = DeviceBatch(b)
-    outs = {}
     for mode in ("auto", "on", "off"):
         out, lse, info = run(db, mode=mode)
         log(f"  {mode}: cascade={info['use_cascade']} P_c={info['common_prefix_len']} "
-            f"psplit={info['prefix_splits']} schunks={info['suffix_chunks']}")
-        assert np.isfinite(out).all() and np.isfinite(lse).all()
-        assert_close(out, lse, ref_o, ref_l, rows=rows, what=f"{name}/{mode}")
-        outs[mode] = (out, lse)
-    # cascade against the GPU non-cascade baseline, every row
-    o_on, l_on = outs["on"]
-    o_off, l_off = outs["off"]
-    assert np.all(np.abs(o_on - o_off) <= 2e-2 + 1e-2 * np.abs(o_off))
-    assert np.abs(l_on - l_off).max() <= 1e-3
+            f"psplit={info['prefix_splits']} row tile={info['prefix_row_tile']} schunks={info['suffix_chunks']}")
+        assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}")
+
+
+def test_128_row_prefix_tile_every_row():
+    """A batch small enough for an every-row check whose packed prefix rows
+    (T * G = 2,304 per KV head) select the 128-row MFMA prefix tile, with
+    ragged query and suffix lengths; cascade forced on and under AUTO."""
+    w = Workload("prefix_128row_tile", 16, 512, (48, 96), (32, 40), 32, 8, 128, seed=2022)
+    b = workloads.make_batch(w)
+    assert int(b.total_q) * 4 >= 2048
+    ref_o, ref_l = oracle_ref(b)
+    db = DeviceBatch(b)
+    for mode in ("on", "auto"):
+        out, lse, info = run(db, mode=mode)
+        log(f"[128-row tile] mode={mode} cascade={info['use_cascade']} row tile={info['prefix_row_tile']} "
+            f"psplit={info['prefix_splits']}")
+        if mode == "on":
+            assert info["prefix_row_tile"] == 128
+        assert_close(out, lse, ref_o, ref_l, what=f"prefix_128row_tile/{mode}")
 
 
 SEPARATE = ["tiny_decode", "prefill_mix", "prefill_capped", "gqa8_outliers", "many_rows", "d64_gqa",
@@ -178,15 +194,9 @@ def test_second_level_against_single_level(name):
     assert i2["num_level1_groups"] > 0 and i1["num_level1_groups"] == 0
     log(f"  groups {i2['num_level1_groups']} x {i2['level1_splits']} splits; slots {i2['num_partial_slots']} "
         f"vs {i1['num_partial_slots']}")
-    if name in SMALL:
-        ref_o, ref_l = oracle_ref(b)
-        rows = None
-    else:
-        reqs = _sample_requests(w.num_reqs, w.seed)
-        ref_o, ref_l = oracle_ref(b, requests=reqs)
-        rows = rows_of(b, reqs)
-    assert_close(o2, l2, ref_o, ref_l, rows=rows, what=f"{name}/two-level")
-    assert_close(o1, l1, ref_o, ref_l, rows=rows, what=f"{name}/one-level")
+    ref_o, ref_l = oracle_ref(b) if name in SMALL else oracle_cached(name, b)
+    assert_close(o2, l2, ref_o, ref_l, what=f"{name}/two-level")
+    assert_close(o1, l1, ref_o, ref_l, what=f"{name}/one-level")
     assert np.all(np.abs(o2 - o1) <= 2e-2 + 1e-2 * np.abs(o1)) and np.abs(l2 - l1).max() <= 1e-3
 
 
@@ -306,19 +316,17 @@ def test_fp32_partials(name, mode):
 @pytest.mark.parametrize("num_reqs,ordered", [(512, 1), (600, 0)])
 def test_request_order_table_limits(num_reqs, ordered):
     """Decode batches at the request-order table's size: 512 requests fill
-    it (longest first), 600 run in batch order; sampled requests against the
+    it (longest first), 600 run in batch order; every row against the
     oracle, cascade and non-cascade."""
     w = Workload(f"many_requests_{num_reqs}", num_reqs, 256, (1, 200), (1, 1), 8, 2, 64, seed=3000 + num_reqs)
     b = workloads.make_batch(w)
-    reqs = [0, 1, num_reqs // 2, num_reqs - 2, num_reqs - 1]
-    ref_o, ref_l = oracle_ref(b, requests=reqs)
-    rows = rows_of(b, reqs)
+    ref_o, ref_l = oracle_ref(b)
     db = DeviceBatch(b)
     for mode in ("on", "off"):
         out, lse, info = run(db, mode=mode)
         log(f"[order] N={num_reqs} mode={mode} longest_first={info['suffix_longest_first']}")
         assert info["suffix_longest_first"] == ordered
-        assert_close(out, lse, ref_o, ref_l, rows=rows, what=f"N={num_reqs}/{mode}")
+        assert_close(out, lse, ref_o, ref_l, what=f"N={num_reqs}/{mode}")
 
 
 @pytest.mark.parametrize("num_reqs", [2, 3])
@@ -341,12 +349,12 @@ def test_long_prefill_chunks(mode):
     """Four requests with 1,100-1,600 query tokens each over a 2,048-token
     shared prefix (5,833 tokens, 23,332 packed prefix rows per KV head): many
     row tiles per request on the per-request phase, a large prefix phase.
-    Request 2 against the oracle."""
+    Every row against the oracle."""
     w = Workload("long_prefill", 4, 2048, (1500, 2500), (1000, 2000), 32, 8, 128, seed=4242)
     b = workloads.make_batch(w)
-    ref_o, ref_l = oracle_ref(b, requests=[2])
+    ref_o, ref_l = oracle_ref(b)
     out, lse, info = run(DeviceBatch(b), mode=mode)
     log(f"[long prefill] mode={mode} cascade={info['use_cascade']} psplit={info['prefix_splits']} "
         f"row tile={info['prefix_row_tile']} schunks={info['suffix_chunks']}")
     assert info["use_cascade"] == (1 if mode == "on" else 0)
-    assert_close(out, lse, ref_o, ref_l, rows=rows_of(b, [2]), what=f"long_prefill/{mode}")
+    assert_close(out, lse, ref_o, ref_l, what=f"long_prefill/{mode}")
