@@ -263,6 +263,30 @@ ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cascade_attn_run without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The partial states live in a
+ * library-owned device array of CA_NOALLOC_WORKSPACE_BYTES (32 MiB), one
+ * copy per GPU, taken when the library first runs this entry point on that
+ * GPU and held until the process ends. This call allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine); on its first call on
+ * a device it looks up that device's copy of the array.
+ * Arguments as for cascade_attn_run. Every call on one GPU shares that GPU's
+ * array and it keeps the last call's contents: calls that overlap in time on
+ * one GPU (two streams, two threads) race and must not be issued; calls on
+ * one stream are ordered and safe. No part of the array needs to start at
+ * zero (each call writes every partial state it reads back).
+ * Errors: as cascade_attn_run; CA_EWORKSPACE when the plan's workspace_bytes
+ * exceed CA_NOALLOC_WORKSPACE_BYTES (e.g. very large prefill batches, or
+ * partials_fp32); CA_EHIP if the array's device address cannot be found.
+ */
+#define CA_NOALLOC_WORKSPACE_BYTES (32u << 20)
+ca_status_t cascade_attn_run_noalloc(ca_plan_t plan, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table_d, const int32_t* query_start_loc_d,
+                                     const int32_t* seq_lens_d, const float* sinks_d, void* out,
+                                     float* lse_out, void* stream);
+
+/*
  * Per-shape autotuning ([p4] "Update Cascade Attention Heuristics for FA3":
  * the heuristic has to be re-derived for each kernel family; [p2] section 9:
  * cascade only when it beats the plain path). Plans the batch as AUTO would,

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     cascade_attn_profile_enable,
     cascade_attn_profile_read,
     cascade_attn_run,
+    cascade_attn_run_noalloc,
     header_symbols,
     load,
 )

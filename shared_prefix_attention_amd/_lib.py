@@ -117,6 +117,8 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(ca_plan_info_t)]
     lib.cascade_attn_run.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
         [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.cascade_attn_run_noalloc.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
+        [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
     lib.cascade_attn_autotune.argtypes = [ctypes.POINTER(ca_params_t), _i32p, _i32p, _i32p, _i32p] + \
         [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
@@ -130,7 +132,7 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_profile_enable.argtypes = [ctypes.c_int32]
     lib.cascade_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("cascade_attn_num_common_prefix_blocks", "cascade_attn_plan", "cascade_attn_plan_info",
-                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_autotune", "cascade_attn_autotune_record",
+                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_run_noalloc", "cascade_attn_autotune", "cascade_attn_autotune_record",
                  "cascade_attn_profile_enable", "cascade_attn_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -335,6 +337,29 @@ def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start
         query_start_loc_d.data_ptr(), seq_lens_d.data_ptr(), sinks.data_ptr() if sinks is not None else None,
         out.data_ptr(),
         lse_out.data_ptr() if lse_out is not None else None, ws_ptr, ws_bytes, s))
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20
+
+
+def cascade_attn_run_noalloc(plan: Plan, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d,
+                             out, lse_out=None, stream=None, sinks=None) -> None:
+    """cascade_attn_run with the library's own per-GPU workspace (no device
+    allocation anywhere in the call); see the header for its limit and for
+    calls that overlap on one GPU."""
+    import torch
+    for name, t in (("q", q), ("out", out)):
+        if not t.is_contiguous():
+            raise CascadeAttnError(CA_EINVAL, f"{name} must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise CascadeAttnError(CA_EINVAL, "sinks must be a contiguous float32 tensor")
+    _check(load().cascade_attn_run_noalloc(
+        plan.handle, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table_d.data_ptr(),
+        query_start_loc_d.data_ptr(), seq_lens_d.data_ptr(), sinks.data_ptr() if sinks is not None else None,
+        out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None, s))
 
 
 def cascade_attn_profile_enable(capacity: int = 4096) -> None:

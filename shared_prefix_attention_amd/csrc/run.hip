@@ -356,6 +356,59 @@ extern "C" ca_status_t cascade_attn_run(ca_plan_t pl, const void* q, const void*
                       workspace, s);
 }
 
+// ------------------------------------------------- run without allocation
+//
+// Workspace for cascade_attn_run_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up once per device,
+// with that device current).
+ca_status_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CA_EHIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CA_EINVAL, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CA_EHIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CA_OK;
+}
+}  // namespace
+
+extern "C" ca_status_t cascade_attn_run_noalloc(ca_plan_t pl, const void* q, const void* k_cache,
+                                                const void* v_cache, const int32_t* block_table_d,
+                                                const int32_t* query_start_loc_d, const int32_t* seq_lens_d,
+                                                const float* sinks_d, void* out, float* lse_out, void* stream) {
+  if (!pl) return fail(CA_EINVAL, "null plan");
+  if (pl->workspace_bytes > (int64_t)kScratchBytes)
+    return fail(CA_EWORKSPACE, "plan needs " + std::to_string(pl->workspace_bytes) +
+                                   " bytes of workspace; cascade_attn_run_noalloc holds at most " +
+                                   std::to_string(kScratchBytes) + " (use cascade_attn_run with a workspace)");
+  void* ws = nullptr;
+  if (pl->workspace_bytes > 0) {
+    const ca_status_t st = scratch_for_current_device(&ws);
+    if (st != CA_OK) return st;
+  }
+  // the kernels overwrite every partial state they read back: nothing in the
+  // array needs clearing between calls
+  return cascade_attn_run(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, sinks_d, out,
+                          lse_out, ws, ws ? kScratchBytes : 0, stream);
+}
+
 extern "C" ca_status_t cascade_attn_profile_enable(int32_t capacity) {
   if (capacity < 0 || capacity > (1 << 20)) return fail(CA_EINVAL, "capacity must be in [0, 2^20]");
   std::lock_guard<std::mutex> g(g_prof.mu);
