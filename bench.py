@@ -234,7 +234,7 @@ def decision_sweep(steps, warmup):
             pl = spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                                 k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
                                 seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode)
-            ws = torch.empty(max(pl.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(pl.workspace_bytes, 256), dtype=torch.uint8, device=dev)
 
             def f(i, pl=pl, ws=ws):
                 q, k, v = copies[i]
@@ -333,7 +333,7 @@ def main():
     lse = torch.empty(T, w.num_q_heads, dtype=torch.float32, device=dev)
 
     def workspace_for(pl):
-        return torch.empty(max(pl.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        return torch.zeros(max(pl.workspace_bytes, 256), dtype=torch.uint8, device=dev)
 
     ws = workspace_for(plan)
 

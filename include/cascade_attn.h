@@ -119,6 +119,11 @@ typedef struct {
   int32_t partials_fp32;       /* partial outputs of the phases before the merge: 0 = bf16 (the
                                   attention dtype, as [p2] section 8 Step 5 merges the two phases'
                                   outputs), 1 = fp32; partial LSEs are fp32 either way */
+  int32_t merge_mode;          /* where the partial states are merged: 0 (default) = the planner's
+                                  choice by cost; 1 = a separate merge launch (as always with
+                                  separate_phases); 2 = inside the attention launch, by the work item
+                                  that completes each row block (one launch per step). All merge in
+                                  the same order: same bits */
   int32_t use_tuned;           /* 0 (default) = AUTO is a pure function of the batch and these
                                   params; 1 = an AUTO plan whose batch shape has a choice recorded
                                   by cascade_attn_autotune / cascade_attn_autotune_record takes
@@ -142,7 +147,7 @@ typedef struct {
   int32_t num_partial_slots;           /* partial states per (token, head) */
   int32_t prefix_stages;               /* LDS pipeline depth of the prefix kernel */
   int32_t suffix_stages;               /* LDS pipeline depth of the suffix / only kernel */
-  int32_t reserved2;                   /* 0 */
+  int32_t merge_in_launch;             /* 1 if the partial states are merged inside the attention launch */
   int32_t suffix_heads_per_item;       /* consecutive KV heads one suffix (or only) work item runs */
   int32_t separate_phases;             /* 1 if the cascade phases run as separate launches */
   int32_t num_level1_groups;           /* request groups of the second shared level (0 = none) */
@@ -248,12 +253,21 @@ ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* 
  *   out              [T][num_q_heads][head_dim] bf16 (written)
  *   lse_out          [T][num_q_heads] fp32, natural log (written; may be NULL)
  *   workspace        device scratch of >= info.workspace_bytes bytes (may be
- *                    NULL when that is 0); 256-byte aligned. Its contents
- *                    need no initialisation and are meaningless afterwards;
- *                    two runs that overlap in time must not share it.
- * Cascade path: prefix kernel + suffix kernel + merge kernel ([p2] section 8
- * Step 5), with the group level beside the prefix when the plan has one. Non-cascade path: one attention over each request's full block
- * table (Step 4), plus a merge when the plan splits the KV range.
+ *                    NULL when that is 0); 256-byte aligned. Its first
+ *                    CA_WORKSPACE_COUNTER_BYTES hold the arrival counters of
+ *                    the merge inside the attention launch: they must be zero
+ *                    before the workspace's first run (allocate it zeroed, or
+ *                    call cascade_attn_workspace_init once), and every run
+ *                    leaves them zero, so one workspace serves any sequence
+ *                    of plans. The rest needs no initialisation. Nothing else
+ *                    may write the workspace between runs; two runs that
+ *                    overlap in time must not share it.
+ * Cascade path: the prefix phase, the group level (if the plan has one) and
+ * the suffix phase in one launch, then the LSE merge ([p2] section 8 Step
+ * 5); the merge runs as its own launch or inside the attention launch
+ * (merge_mode; info.merge_in_launch). Non-cascade path: one attention over each request's full
+ * block table (Step 4), merging its KV chunks the same way when the plan
+ * splits the KV range.
  * Errors: CA_EINVAL (null pointers/handle), CA_EWORKSPACE (too small),
  * CA_EHIP (launch failure).
  */
@@ -261,6 +275,16 @@ ca_status_t cascade_attn_run(ca_plan_t plan, const void* q, const void* k_cache,
                              const int32_t* block_table_d, const int32_t* query_start_loc_d,
                              const int32_t* seq_lens_d, const float* sinks_d, void* out, float* lse_out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Zeroes the merge counters at the start of a workspace (the first
+ * min(workspace_bytes, CA_WORKSPACE_COUNTER_BYTES) bytes) with a kernel on
+ * `stream` (graph-capturable; no memset). Needed once per workspace before
+ * its first run unless it was allocated zeroed.
+ * Errors: CA_EINVAL (null workspace with a size, misaligned), CA_EHIP.
+ */
+#define CA_WORKSPACE_COUNTER_BYTES (256u << 10)
+ca_status_t cascade_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * cascade_attn_run without a workspace argument, for callers that cannot
@@ -346,10 +370,9 @@ const char* cascade_attn_last_error(void);
  * Kernel timing for measurement. cascade_attn_profile_enable(capacity)
  * creates a pool of 2 * capacity HIP events (call it outside any timed
  * region; 0 disables timing and frees the pool). While enabled, each kernel
- * run() launches takes the next start / stop pair of the pool and carries it
- * on its own dispatch (the events bracket that kernel's execution on the
- * launch stream; no event is created during run()); launches past the
- * pool's capacity run untimed. cascade_attn_profile_read() waits for the
+ * run() launches takes the next start / stop pair of the pool, recorded on
+ * the launch stream right before and right after that kernel (no event is
+ * created during run()); launches past the pool's capacity run untimed. cascade_attn_profile_read() waits for the
  * recorded events, writes the summed milliseconds and launch counts per
  * kernel kind into ms[CA_PROFILE_KINDS] and counts[CA_PROFILE_KINDS], and
  * makes the whole pool available again.

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     cascade_attn_profile_read,
     cascade_attn_run,
     cascade_attn_run_noalloc,
+    cascade_attn_workspace_init,
     header_symbols,
     load,
 )

@@ -55,6 +55,7 @@ class ca_params_t(ctypes.Structure):
         ("prefix_splits", ctypes.c_int32),
         ("suffix_order", ctypes.c_int32),
         ("partials_fp32", ctypes.c_int32),
+        ("merge_mode", ctypes.c_int32),
         ("use_tuned", ctypes.c_int32),
     ]
 
@@ -73,7 +74,7 @@ class ca_plan_info_t(ctypes.Structure):
         ("num_partial_slots", ctypes.c_int32),
         ("prefix_stages", ctypes.c_int32),
         ("suffix_stages", ctypes.c_int32),
-        ("reserved2", ctypes.c_int32),
+        ("merge_in_launch", ctypes.c_int32),
         ("suffix_heads_per_item", ctypes.c_int32),
         ("separate_phases", ctypes.c_int32),
         ("num_level1_groups", ctypes.c_int32),
@@ -119,6 +120,7 @@ def load() -> ctypes.CDLL:
         [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.cascade_attn_run_noalloc.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
         [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.cascade_attn_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
     lib.cascade_attn_autotune.argtypes = [ctypes.POINTER(ca_params_t), _i32p, _i32p, _i32p, _i32p] + \
         [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
@@ -132,7 +134,7 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_profile_enable.argtypes = [ctypes.c_int32]
     lib.cascade_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("cascade_attn_num_common_prefix_blocks", "cascade_attn_plan", "cascade_attn_plan_info",
-                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_run_noalloc", "cascade_attn_autotune", "cascade_attn_autotune_record",
+                 "cascade_attn_plan_groups", "cascade_attn_run", "cascade_attn_run_noalloc", "cascade_attn_workspace_init", "cascade_attn_autotune", "cascade_attn_autotune_record",
                  "cascade_attn_profile_enable", "cascade_attn_profile_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -207,7 +209,7 @@ def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: in
             mode="auto", num_cus: int = 0, heads_per_item: int = 0, separate_phases: bool = False,
             max_levels: int = 0, kv_dtype="bf16", k_scale: float = 0.0, v_scale: float = 0.0,
             sliding_window: int = 0, prefix_splits: int = 0, suffix_order: int = 0,
-            partials_fp32: bool = False, use_tuned: bool = False):
+            partials_fp32: bool = False, use_tuned: bool = False, merge_mode: int = 0):
     """ca_params_t plus the host metadata arrays and their pointers."""
     bt, bt_p = _host_i32(block_table)
     qsl, qsl_p = _host_i32(query_start_loc)
@@ -240,6 +242,7 @@ def _params(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: in
     prm.suffix_order = int(suffix_order)
     prm.partials_fp32 = int(partials_fp32)
     prm.use_tuned = int(use_tuned)
+    prm.merge_mode = int(merge_mode)
     keep = (bt, qsl, sl, nc)   # the arrays behind the pointers
     return prm, (bt_p, qsl_p, sl_p, nc_p), keep
 
@@ -253,7 +256,7 @@ def cascade_attn_plan(**kw) -> Plan:
     arrays or CPU tensors), and the optional ca_params_t settings
     softmax_scale, mode, num_cus, heads_per_item, separate_phases,
     max_levels, kv_dtype, k_scale, v_scale, sliding_window, prefix_splits,
-    suffix_order, partials_fp32, use_tuned.
+    suffix_order, partials_fp32, use_tuned, merge_mode.
     """
     prm, ptrs, keep = _params(**kw)
     h = ctypes.c_void_p(0)
@@ -340,6 +343,17 @@ def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start
 
 
 NOALLOC_WORKSPACE_BYTES = 32 << 20
+WORKSPACE_COUNTER_BYTES = 256 << 10
+
+
+def cascade_attn_workspace_init(workspace, stream=None) -> None:
+    """Zeroes the merge counters at the start of ``workspace`` (a device
+    tensor) on ``stream``; needed once unless it was allocated zeroed."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(load().cascade_attn_workspace_init(workspace.data_ptr(), workspace.numel() * workspace.element_size(), s))
 
 
 def cascade_attn_run_noalloc(plan: Plan, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d,

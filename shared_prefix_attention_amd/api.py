@@ -29,7 +29,7 @@ def plan_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, k_cache: t
                heads_per_item: int = 0, separate_phases: bool = False, max_levels: int = 0,
                kv_dtype=None, k_scale: float = 0.0, v_scale: float = 0.0, sliding_window: int = 0,
                prefix_splits: int = 0, suffix_order: int = 0, partials_fp32: bool = False,
-               use_tuned: bool = False) -> Plan:
+               use_tuned: bool = False, merge_mode: int = 0) -> Plan:
     """Plan from host metadata; strides and pool size are read off ``k_cache``.
 
     kv_dtype: "bf16" or "fp8"; by default taken from ``k_cache`` (bf16, or a
@@ -44,20 +44,21 @@ def plan_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, k_cache: t
         softmax_scale=softmax_scale, mode=mode, num_cus=num_cus, heads_per_item=heads_per_item,
         separate_phases=separate_phases, max_levels=max_levels, kv_dtype=kv_dtype, k_scale=k_scale,
         v_scale=v_scale, sliding_window=sliding_window, prefix_splits=prefix_splits, suffix_order=suffix_order,
-        partials_fp32=partials_fp32, use_tuned=use_tuned)
+        partials_fp32=partials_fp32, use_tuned=use_tuned, merge_mode=merge_mode)
 
 
 def run_batch(plan: Plan, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_table_d: torch.Tensor, query_start_loc_d: torch.Tensor, seq_lens_d: torch.Tensor,
               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, stream=None, sinks: Optional[torch.Tensor] = None):
-    """Run the plan; allocates out / lse / workspace with torch when not given."""
+    """Run the plan; allocates out / lse / workspace with torch when not given
+    (the workspace zeroed, as its merge counters must start at zero)."""
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
     if workspace is None and plan.workspace_bytes > 0:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     cascade_attn_run(plan, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse,
                      workspace, stream, sinks)
     return out, lse

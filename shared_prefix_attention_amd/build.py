@@ -43,8 +43,12 @@ def check_resource_usage(remarks: str) -> list:
     kernel. The LDS reads of the attention kernels are inline asm whose
     results the code waits for by hand (an explicit lgkmcnt wait that names
     the destination registers); that is only sound while the compiler keeps
-    every such register in place, i.e. never spills or moves it through
-    scratch memory. So any kernel with scratch or spills fails the build."""
+    every such register in place. So a kernel that uses scratch memory
+    (VGPR spills, a stack) fails the build. SGPR spills are allowed and
+    reported: they go to lanes of a VGPR the compiler reserves for them
+    (v_writelane / v_readlane, no memory), and lds_wait_check verifies on the
+    final assembly that no instruction touches an LDS read's destination
+    before its wait."""
     kernels = []
     cur = None
     for line in remarks.splitlines():
@@ -57,12 +61,12 @@ def check_resource_usage(remarks: str) -> list:
                       r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]|Dynamic Stack): (\S+)", line)
         if m and cur is not None:
             cur[m.group(1)] = m.group(2)
-    bad = [k for k in kernels if k.get("ScratchSize [bytes/lane]", "0") != "0" or k.get("SGPRs Spill", "0") != "0"
-           or k.get("VGPRs Spill", "0") != "0" or k.get("Dynamic Stack", "False") != "False"]
+    bad = [k for k in kernels if k.get("ScratchSize [bytes/lane]", "0") != "0" or k.get("VGPRs Spill", "0") != "0"
+           or k.get("Dynamic Stack", "False") != "False"]
     if not kernels:
         raise RuntimeError("no kernel-resource-usage remarks found in the HIP compile output")
     if bad:
-        raise RuntimeError("kernels use scratch memory or spill registers (the inline-asm LDS reads rely on "
+        raise RuntimeError("kernels use scratch memory or spill VGPRs (the inline-asm LDS reads rely on "
                            "neither): " + "; ".join(f"{k['name']}: {k}" for k in bad))
     return kernels
 
@@ -106,8 +110,9 @@ def build(verbose: bool = True) -> str:
         for k in usage:
             f.write(" ".join(f"{key}={val}" for key, val in k.items()) + "\n")
     if verbose:
-        print(f"  {len(usage)} kernels: no scratch, no spills; max VGPRs "
-              f"{max(int(k.get('VGPRs', 0)) for k in usage)}", flush=True)
+        print(f"  {len(usage)} kernels: no scratch, no VGPR spills; max VGPRs "
+              f"{max(int(k.get('VGPRs', 0)) for k in usage)}; SGPR spills to VGPR lanes: max "
+              f"{max(int(k.get('SGPRs Spill', 0)) for k in usage)}", flush=True)
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

@@ -52,6 +52,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "merge.hpp"
 
 namespace ca {
 
@@ -89,6 +90,44 @@ struct TileArgs {
   float v_scale;                // dequantisation factor of V (1 for bf16 caches)
   int32_t window;               // per-request phase: sliding window W (> 0: keys p - W < t <= p)
   const float* sinks;           // [hq] attention-sink logits (natural log) or null; direct mode only
+  int32_t coherent;             // partial states are merged inside this launch: device-scope stores
+};
+
+// Merge inside the attention launch (counters null: a separate merge
+// launch). A merge unit is (request r, per-request row tile m, KV head g):
+// the rows [m * m_suf_rows, +m_suf_rows) of r under the query heads of g.
+// Every work item that writes partial states of a unit's rows counts itself
+// at the unit once; the item that brings the count to the unit's number of
+// such items merges the unit and resets the counter to 0. A kernel argument
+// of its own, read only at an item's end, so that none of its fields stays
+// in registers through the stage loop.
+struct MergeTailArgs {
+  int32_t* counters;            // [num_reqs][m_suf_mtiles][hkv] int32, zero between launches
+  const int32_t* qsl;           // [num_reqs + 1]
+  const void* part_o;           // partial states, as in TileArgs
+  const float* part_lse;
+  uint16_t* out;
+  float* lse_out;
+  const float* sinks;
+  int64_t slot_elems, slot_rows;
+  int32_t part_fp32;
+  int32_t merge_slots;          // partial states per row
+  int32_t hq, hkv, group, num_reqs;
+  int32_t m_pre_splits;         // prefix items per prefix row tile (0: no prefix phase)
+  int32_t m_pre_rows;           // rows per prefix / group-level tile
+  int32_t m_lvl_splits;         // group-level items per group row tile (0: none)
+  int32_t m_suf_splits;         // per-request items per (request, row tile, KV head)
+  int32_t m_suf_rows;           // rows per per-request tile
+  int32_t m_suf_mtiles;         // per-request row tiles of the longest query (counter stride)
+  int32_t uniform_q;            // > 0: every request has this many query tokens (request r's tokens
+                                // are [r * uniform_q, (r + 1) * uniform_q): no lookup needed)
+};
+
+// What an item wrote, for its merge tail: role (prefix_mode as in
+// TileArgs), request (or the group's first request), group, rows in the
+// role's own numbering, KV heads g0 .. g0 + H - 1. wrote = 0: nothing.
+struct ItemEnd {
+  int32_t wrote, mode, req, grp, row_begin, row_end, g0, H;
 };
 
 // Second shared level: request groups [req_begin, req_end) whose members
@@ -139,7 +178,8 @@ template <int D, int NS, int SK, int ESZ = 2>
 struct TileSmem {
   static constexpr int TILE_BYTES = SK * D * ESZ;          // one of K or V, one stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  static constexpr int BYTES = NS * STAGE_BYTES + kMaxItemPages * 4;
+  static constexpr int NS_STAGE_BYTES = NS * STAGE_BYTES;  // the page table follows
+  static constexpr int BYTES = NS_STAGE_BYTES + kMaxItemPages * 4;
 };
 
 // 16-byte chunk swizzles of a key row (rows are D*2 bytes apart), chosen
@@ -286,13 +326,179 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(const u32x2_t& a, const u32x2_t&
                                                    0, 0, 0);
 }
 
+// Token range [q0, q1) of request r.
+__device__ __forceinline__ void req_tokens(const MergeTailArgs& a, int r, int& q0, int& q1) {
+  if (a.uniform_q > 0) {
+    q0 = r * a.uniform_q;
+    q1 = q0 + a.uniform_q;
+  } else {
+    q0 = a.qsl[r];
+    q1 = a.qsl[r + 1];
+  }
+}
+
+// Items that write partial states of unit (r, m): the prefix tiles that
+// overlap its rows (times the prefix splits), likewise the group-level tiles
+// of r's group, and its own per-request items (one per KV chunk). q0 / q1:
+// r's token range.
+__device__ __forceinline__ int unit_item_count(const MergeTailArgs& a, const GroupTable& gt, int r, int m, int q0,
+                                               int q1) {
+  const int rows_r = (q1 - q0) * a.group;
+  const int lo = m * a.m_suf_rows, hi = min(lo + a.m_suf_rows, rows_r);   // request-local rows
+  int e = a.m_suf_splits;
+  if (a.m_pre_splits > 0) {
+    const int base = q0 * a.group;   // packed row of the request's first row
+    e += a.m_pre_splits * ((base + hi - 1) / a.m_pre_rows - (base + lo) / a.m_pre_rows + 1);
+  }
+  if (a.m_lvl_splits > 0 && gt.n > 0) {
+    const int j = group_of_request(gt, r);
+    if (j >= 0) {
+      int g0, g1;
+      req_tokens(a, gt.req_begin[j], g0, g1);
+      const int gb = (q0 - g0) * a.group;   // row offset inside the group
+      e += a.m_lvl_splits * ((gb + hi - 1) / a.m_pre_rows - (gb + lo) / a.m_pre_rows + 1);
+    }
+  }
+  return e;
+}
+
+// Work list of a merge tail in LDS: [0] = entries; entry k at 4 + 4k:
+// counter index, first token of the request, first row of the unit inside
+// the request, rows of the unit.
+constexpr int kTailEntryInts = 4;
+
+// Wave 0, one lane: counts this item's arrival at unit (r, m, g) and, if it
+// completes the unit, appends the unit to the work-group's list.
+__device__ __forceinline__ void arrive(const MergeTailArgs& a, const GroupTable& gt, int r, int m, int g, int q0,
+                                       int q1, int32_t* s_list) {
+  const int u = (r * a.m_suf_mtiles + m) * a.hkv + g;
+  const int expect = unit_item_count(a, gt, r, m, q0, q1);
+  const int old = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1 == expect) {
+    const int k = __hip_atomic_fetch_add(s_list, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int32_t* ent = s_list + 4 + kTailEntryInts * k;
+    const int lo = m * a.m_suf_rows;
+    ent[0] = u;
+    ent[1] = q0;
+    ent[2] = lo;
+    ent[3] = min(lo + a.m_suf_rows, (q1 - q0) * a.group) - lo;
+  }
+}
+
+// Wave 0: the last request r in [r_lo, r_end) with qsl[r] <= tok, searched
+// 64 candidates per memory round trip.
+__device__ __forceinline__ int request_of_token(const MergeTailArgs& a, int r_lo, int r_end, int tok) {
+  if (a.uniform_q > 0) return min(max(tok / a.uniform_q, r_lo), r_end - 1);
+  const int lane = threadIdx.x & 63;
+  int lo = r_lo, n = r_end - r_lo;   // answer in [lo, lo + n)
+  while (n > 1) {
+    const int step = (n + 63) / 64;
+    const int c = lo + lane * step;   // candidate starts
+    const bool le = c < lo + n && a.qsl[c] <= tok;
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(le);
+    const int j = mask ? 63 - __builtin_clzll(mask) : 0;   // last candidate with qsl <= tok
+    lo = lo + j * step;
+    n = min(step, r_end - lo);
+  }
+  return lo;
+}
+
+// End of a work item when the merge runs inside the launch. The item's
+// partial states were written with device-scope stores; every thread waits
+// until its stores are complete, then wave 0 counts the item at every unit
+// whose rows it wrote (device-scope atomic add). Units it completes are
+// merged here, by the whole work-group, reading the partial states with
+// device-scope loads issued after the counts came back: every row part in
+// the canonical slot order of the merge kernel, so the result does not
+// depend on which item came last. No L2-wide write-back or invalidation is
+// needed (the partial states never sit dirty, or stale, in an XCD's L2).
+// The counters go back to 0 for the next launch.
+// s_list: LDS the item no longer uses (its stage buffers), >= 4 KB.
+template <int D, int NT>
+__device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const GroupTable& gt, const ItemEnd& e,
+                                           int32_t* s_list) {
+  if (!e.wrote) return;
+  const int tid = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): this thread's stores are done
+  __syncthreads();                 // (and every wave is done with the stage buffers)
+  if (tid == 0) s_list[0] = 0;
+  __syncthreads();
+  if (tid < 64) {
+    const int G = a.group, RS = a.m_suf_rows;
+    if (e.mode == 0) {
+      const int m = e.row_begin / RS;
+      int q0, q1;
+      req_tokens(a, e.req, q0, q1);
+      for (int h = tid; h < e.H; h += 64) arrive(a, gt, e.req, m, e.g0 + h, q0, q1, s_list);
+    } else {
+      // packed rows [p_lo, p_hi) and the requests they may belong to
+      int p_lo = e.row_begin, p_hi = e.row_end, r_lo = 0, r_end = a.num_reqs;
+      if (e.mode == 2) {
+        int g0, g1;
+        req_tokens(a, gt.req_begin[e.grp], g0, g1);
+        p_lo += g0 * G;
+        p_hi += g0 * G;
+        r_lo = gt.req_begin[e.grp];
+        r_end = gt.req_end[e.grp];
+      }
+      const int tok_lo = p_lo / G, tok_hi = (p_hi - 1) / G;
+      const int first = request_of_token(a, r_lo, r_end, tok_lo);
+      for (int r = first + tid; r < r_end; r += 64) {
+        int q0, q1;
+        req_tokens(a, r, q0, q1);
+        if (q0 > tok_hi) break;
+        const int base = q0 * G, rows_r = (q1 - q0) * G;
+        const int l0 = max(p_lo, base) - base, l1 = min(p_hi, base + rows_r) - base;
+        if (l0 >= l1) continue;
+        for (int m = l0 / RS; m <= (l1 - 1) / RS; ++m) arrive(a, gt, r, m, e.g0, q0, q1, s_list);
+      }
+    }
+  }
+  __syncthreads();
+  const int n_won = s_list[0];
+  if (n_won == 0) return;
+  // each thread merges NCH 16-byte chunks of a row (16 chunks in flight per
+  // batch of slots); unit k owns flat work items [cum_k, cum_k + rows_k * tpr)
+  constexpr int NCH = 2;
+  constexpr int TPR_BF16 = D / 8 / NCH, TPR_F32 = D / 4 / NCH;
+  const int tpr = a.part_fp32 ? TPR_F32 : TPR_BF16;
+  MergeArgs ma;
+  ma.part_o = a.part_o;
+  ma.part_lse = a.part_lse;
+  ma.slots = a.merge_slots;
+  ma.rows = a.slot_rows;
+  ma.slot_elems = a.slot_elems;
+  ma.out = a.out;
+  ma.lse_out = a.lse_out;
+  ma.sinks = a.sinks;
+  ma.hq = a.hq;
+  int k = 0, cum = 0;   // the unit holding this thread's first work item (scan kept across passes)
+  for (int w = tid;; w += NT) {
+    while (k < n_won && cum + s_list[4 + kTailEntryInts * k + 3] * tpr <= w) {
+      cum += s_list[4 + kTailEntryInts * k + 3] * tpr;
+      ++k;
+    }
+    if (k >= n_won) break;
+    const int32_t* ent = s_list + 4 + kTailEntryInts * k;
+    const int g = ent[0] % a.hkv;
+    const int i = ent[2] + (w - cum) / tpr;   // request-local row
+    const int part = (w - cum) % tpr;
+    const int64_t row = (int64_t)(ent[1] + i / a.group) * a.hq + g * a.group + i % a.group;
+    if (a.part_fp32) merge_row_part<D, true, true, NCH>(ma, row, part);
+    else merge_row_part<D, false, true, NCH>(ma, row, part);
+  }
+  if (tid < n_won)
+    __hip_atomic_store(a.counters + s_list[4 + kTailEntryInts * tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // MH: the item may cover several consecutive KV heads of one request (same
 // pages and key range), run as one continuous stage pipeline.
 // WIN: the item may apply a sliding window and attention sinks (the
 // stand-alone kernel; the cascade launch has neither).
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const ReqOrder& ro, const int bid,
-                                          uint8_t* smem) {
+                                          uint8_t* smem, ItemEnd& end) {
+  end.wrote = 0;
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
   constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
@@ -431,7 +637,9 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         const int hh = rh / nrows;
         const int m = row_begin + (rh - hh * nrows);
         const int64_t row = (int64_t)(tok_base + m / a.group) * a.hq + (g0 + hh) * a.group + m % a.group;
-        a.part_lse[(int64_t)(a.lvl1_slot_base + s) * a.slot_rows + row] = -INFINITY;
+        float* lp = a.part_lse + (int64_t)(a.lvl1_slot_base + s) * a.slot_rows + row;
+        if (a.coherent) store_dev_f32(lp, -INFINITY);
+        else *lp = -INFINITY;
       }
     }
   }
@@ -717,22 +925,40 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
         if (a.part_fp32) {
           float* dst = static_cast<float*>(a.part_o) + e0;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(dst + db * 16 + lq * 4) = o[db][rb] * inv;
+          for (int db = 0; db < DB; ++db) {
+            const f32x4_t r = o[db][rb] * inv;
+            float* d = dst + db * 16 + lq * 4;
+            if (a.coherent) {
+              const u32x4_t w = __builtin_bit_cast(u32x4_t, r);
+              store_dev_u64(d, (uint64_t)w[0] | ((uint64_t)w[1] << 32));
+              store_dev_u64(d + 2, (uint64_t)w[2] | ((uint64_t)w[3] << 32));
+            } else {
+              *reinterpret_cast<f32x4_t*>(d) = r;
+            }
+          }
         } else {
           uint16_t* dst = static_cast<uint16_t*>(a.part_o) + e0;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const f32x4_t r = o[db][rb] * inv;
-            *reinterpret_cast<u32x2_t*>(dst + db * 16 + lq * 4) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+            const uint32_t lo = pack_bf16x2(r[0], r[1]), hi = pack_bf16x2(r[2], r[3]);
+            uint16_t* d = dst + db * 16 + lq * 4;
+            if (a.coherent) store_dev_u64(d, (uint64_t)lo | ((uint64_t)hi << 32));
+            else *reinterpret_cast<u32x2_t*>(d) = u32x2_t{lo, hi};
           }
         }
-        if (lq == 0) a.part_lse[(int64_t)slot * a.slot_rows + row] = lse;
+        if (lq == 0) {
+          float* lp = a.part_lse + (int64_t)slot * a.slot_rows + row;
+          if (a.coherent) store_dev_f32(lp, lse);
+          else *lp = lse;
+        }
       }
     }
   };
 
   // An empty KV range (a chunk past a short request's end) still writes its
   // rows: o = 0, lse = -inf, which the merge ignores.
+  end = ItemEnd{1, a.prefix_mode, req, grp, row_begin, row_end, g0, H};
   if (U == 0) {
     for (int hh = 0; hh < H; ++hh) finish_head(g0 + hh, 0);
     return;
@@ -987,9 +1213,11 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 
 template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
 __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt,
-                                                                  const ReqOrder ro) {
+                                                                  const ReqOrder ro, const MergeTailArgs mt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
-  attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, ro, blockIdx.x, smem);
+  ItemEnd end;
+  attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, ro, blockIdx.x, smem, end);
+  if (mt.counters) merge_tail<D, 64 * RW * KG>(mt, gt, end, reinterpret_cast<int32_t*>(smem));
 }
 
 // One launch for all cascade phases: work-groups [0, n_prefix) run prefix
@@ -1001,17 +1229,21 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
 template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK, bool F8>
 __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs ga, const TileArgs sa,
                                                              const int n_prefix, const int n_group,
-                                                             const GroupTable gt, const ReqOrder ro) {
+                                                             const GroupTable gt, const ReqOrder ro,
+                                                             const MergeTailArgs mt) {
   static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
   constexpr int ESZ = F8 ? 1 : 2;
   constexpr int PB = TileSmem<D, PNS, PSK, ESZ>::BYTES, SB = TileSmem<D, SNS, SSK, ESZ>::BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(pa, gt, ro, bid, smem);
+  ItemEnd end;
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(pa, gt, ro, bid, smem, end);
   else if (bid < n_prefix + n_group)
-    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(ga, gt, ro, bid - n_prefix, smem);
+    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(ga, gt, ro, bid - n_prefix, smem, end);
   else
-    attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false>(sa, gt, ro, bid - n_prefix - n_group, smem);
+    attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false>(sa, gt, ro, bid - n_prefix - n_group, smem,
+                                                                          end);
+  if (mt.counters) merge_tail<D, 256>(mt, gt, end, reinterpret_cast<int32_t*>(smem));
 }
 
 }  // namespace ca

@@ -74,21 +74,24 @@ __device__ __forceinline__ float wave_sum_across_quads(float x) {
   return a + b;
 }
 
-// Online LSE merge step: folds one partial state (lse_s natural log, o_s
-// normalised) into a running (m, wsum, acc) where acc / wsum is the merged
-// output and m + log(wsum) the merged LSE. A partial with lse_s = -inf has
-// weight 0 and its o_s (which may be garbage) is not used.
-template <int N>
-__device__ __forceinline__ void merge_step(float& m, float& wsum, f32x4_t (&acc)[N], float lse_s,
-                                           const f32x4_t (&o_s)[N]) {
-  if (lse_s == -INFINITY) return;
-  const float m_new = fmaxf(m, lse_s);
-  const float a_old = (m == -INFINITY) ? 0.f : exp2f((m - m_new) * kLog2e);
-  const float a_new = exp2f((lse_s - m_new) * kLog2e);
-  wsum = wsum * a_old + a_new;
-#pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = acc[i] * a_old + o_s[i] * a_new;
-  m = m_new;
+// Device-scope (agent) coherent accesses for data one work-group writes and
+// another reads inside the same launch: relaxed atomic stores and loads at
+// agent scope (gfx950: global_store / global_load with sc1), written through
+// to, and read from, the device's point of coherence rather than an XCD's
+// own L2. Ordering against the arrival counter comes from waiting for the
+// stores to complete (vmcnt 0) before the counter is bumped, and from issuing
+// the loads only after the counter's value has come back.
+__device__ __forceinline__ void store_dev_u64(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_dev_u64(const void* p) {
+  return __hip_atomic_load(static_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev_f32(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace ca

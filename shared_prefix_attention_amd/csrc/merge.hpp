@@ -8,6 +8,12 @@
 // Partials with lse = -inf have weight 0 and their o is not read. An
 // attention sink (one logit per query head) enters as one more state with
 // lse = sink and o = 0.
+//
+// One canonical order of operations, used by the stand-alone merge kernel
+// and by the merge inside the attention launch alike, so both give the same
+// bits: the slots are cut into SG contiguous groups (SG = 4 above 16 slots,
+// else 1); each group is folded in slot order (online form, group 0 starting
+// from the sink); then groups 1 .. SG-1 are folded into group 0 in order.
 #pragma once
 
 #include "device_common.hpp"
@@ -26,8 +32,12 @@ struct MergeArgs {
   int32_t hq;
 };
 
+constexpr int kMergeBatch = 16;   // slots whose loads are issued together
+__host__ __device__ constexpr int merge_groups(int slots) { return slots > kMergeBatch ? 4 : 1; }
+
 // Folds an unnormalised state (m2, w2, acc2) into (m, w, acc): acc / w is
-// the merged output and m + log(w) its LSE.
+// the merged output and m + log(w) its LSE. Products are fused explicitly so
+// that every inlined copy rounds the same way.
 template <int N>
 __device__ __forceinline__ void fold_state(float& m, float& w, f32x4_t (&acc)[N], float m2, float w2,
                                            const f32x4_t (&acc2)[N]) {
@@ -35,9 +45,11 @@ __device__ __forceinline__ void fold_state(float& m, float& w, f32x4_t (&acc)[N]
   const float mn = fmaxf(m, m2);
   const float a1 = (m == -INFINITY) ? 0.f : exp2f((m - mn) * kLog2e);
   const float a2 = exp2f((m2 - mn) * kLog2e);
-  w = w * a1 + w2 * a2;
+  w = __builtin_fmaf(w2, a2, w * a1);
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = acc[i] * a1 + acc2[i] * a2;
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(acc2[i][j], a2, acc[i][j] * a1);
   m = mn;
 }
 
@@ -45,12 +57,126 @@ __device__ __forceinline__ void fold_state(float& m, float& w, f32x4_t (&acc)[N]
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Each thread owns V consecutive d values of a row (16-byte loads: 4 fp32
-// or 8 bf16), so D/V threads cover a row. F32: partial outputs in fp32, else
-// bf16 (widened exactly). SG slot groups share a row's slots (contiguous
-// ranges) when there are many slots and few rows: each group merges its
-// range, and group 0 folds the others in, in group order, through LDS (so
-// the result is fixed by the slot count).
+// One slot group of one row part: NCH x V consecutive d values (V = 8 bf16
+// or 4 fp32 per 16-byte chunk) of flat row `row`, starting at chunk
+// part * NCH; slots [s_begin, s_end) folded in order onto (m, wsum, acc). The
+// loads of a batch of slots (LSE and o, only for slots that exist) are issued
+// before their first use, so a batch costs one memory round trip.
+template <int D, bool F32, bool COH = false, int NCH = 1>
+__device__ __forceinline__ void merge_slot_range(const MergeArgs& a, int64_t row, int part, int s_begin, int s_end,
+                                                 float& m, float& wsum, f32x4_t (&acc)[NCH * (F32 ? 1 : 2)]) {
+  constexpr int V = F32 ? 4 : 8;
+  constexpr int NV = NCH * (V / 4);
+  constexpr int B = kMergeBatch / NCH;   // slots per batch: 16 chunks in flight per thread
+  for (int s0 = s_begin; s0 < s_end; s0 += B) {
+    float l[B];
+    u32x4_t w[B][NCH];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      l[k] = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) w[k][c] = u32x4_t{0u, 0u, 0u, 0u};
+      if (s0 + k < s_end) {
+        const int sl = s0 + k;
+        const float* lp = a.part_lse + (int64_t)sl * a.rows + row;
+        const int64_t e = (int64_t)sl * a.slot_elems + row * D + part * NCH * V;
+        const uint8_t* src = static_cast<const uint8_t*>(a.part_o) + e * (F32 ? 4 : 2);
+        if constexpr (COH) {
+          l[k] = load_dev_f32(lp);
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const uint64_t w0 = load_dev_u64(src + 16 * c), w1 = load_dev_u64(src + 16 * c + 8);
+            w[k][c] = u32x4_t{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+          }
+        } else {
+          l[k] = *lp;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) w[k][c] = *reinterpret_cast<const u32x4_t*>(src + 16 * c);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      // bf16 partials widened exactly once every load of the batch is out
+      f32x4_t x[NV];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if constexpr (F32) {
+          x[c] = __builtin_bit_cast(f32x4_t, w[k][c]);
+        } else {
+          x[2 * c] = f32x4_t{bf16_lo(w[k][c][0]), bf16_hi(w[k][c][0]), bf16_lo(w[k][c][1]), bf16_hi(w[k][c][1])};
+          x[2 * c + 1] = f32x4_t{bf16_lo(w[k][c][2]), bf16_hi(w[k][c][2]), bf16_lo(w[k][c][3]), bf16_hi(w[k][c][3])};
+        }
+      }
+      // partial states are normalised (o_s = acc_s / w_s): one state of weight
+      // 1; slots past the range have lse = -inf and are skipped
+      fold_state(m, wsum, acc, l[k], 1.f, x);
+    }
+  }
+}
+
+// Start of slot group g: the sink (if any) joins group 0 as a state with no value.
+__device__ __forceinline__ void merge_seed(const MergeArgs& a, int64_t row, int g, float& m, float& wsum) {
+  m = -INFINITY;
+  wsum = 0.f;
+  if (a.sinks && g == 0) {
+    m = a.sinks[row % a.hq];
+    wsum = m == -INFINITY ? 0.f : 1.f;
+  }
+}
+
+// Normalises a merged state and writes the row part's bf16 output (RNE) and,
+// from part 0, the natural-log LSE.
+template <int D, bool F32, int NCH = 1>
+__device__ __forceinline__ void merge_store(const MergeArgs& a, int64_t row, int part, float m, float wsum,
+                                            const f32x4_t (&acc)[NCH * (F32 ? 1 : 2)]) {
+  constexpr int V = F32 ? 4 : 8;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint16_t* dst = a.out + row * D + part * NCH * V;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if constexpr (F32) {
+      const f32x4_t r = acc[c] * inv;
+      *reinterpret_cast<u32x2_t*>(dst + c * V) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    } else {
+      const f32x4_t r0 = acc[2 * c] * inv, r1 = acc[2 * c + 1] * inv;
+      *reinterpret_cast<u32x4_t*>(dst + c * V) = u32x4_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
+                                                         pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+    }
+  }
+  if (part == 0 && a.lse_out) a.lse_out[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+}
+
+// The canonical merge of one row part by one thread (all slot groups in
+// turn, then the fold of groups 1.. into group 0).
+template <int D, bool F32, bool COH, int NCH>
+__device__ __forceinline__ void merge_row_part(const MergeArgs& a, int64_t row, int part) {
+  constexpr int NV = NCH * (F32 ? 1 : 2);
+  const int sg = merge_groups(a.slots);
+  const int per = (a.slots + sg - 1) / sg;
+  float m, wsum;
+  f32x4_t acc[NV];
+  merge_seed(a, row, 0, m, wsum);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  merge_slot_range<D, F32, COH, NCH>(a, row, part, 0, min(a.slots, per), m, wsum, acc);
+  for (int g = 1; g < sg; ++g) {
+    float m2, w2;
+    f32x4_t acc2[NV];
+    merge_seed(a, row, g, m2, w2);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc2[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    merge_slot_range<D, F32, COH, NCH>(a, row, part, g * per, min(a.slots, (g + 1) * per), m2, w2, acc2);
+    fold_state(m, wsum, acc, m2, w2, acc2);
+  }
+  merge_store<D, F32, NCH>(a, row, part, m, wsum, acc);
+}
+
+// Stand-alone merge launch. Each thread owns V consecutive d values of a row
+// (16-byte loads: 4 fp32 or 8 bf16), so D/V threads cover a row. F32:
+// partial outputs in fp32, else bf16 (widened exactly). SG slot groups
+// (merge_groups) run in parallel thread groups, and group 0 folds the
+// others in, in group order, through LDS: the canonical order above.
 template <int D, bool F32, int SG>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   constexpr int V = F32 ? 4 : 8;
@@ -64,40 +190,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const bool live = row < a.rows;
   if (SG == 1 && !live) return;
   const int per = (a.slots + SG - 1) / SG;
-  const int s_begin = g * per, s_end = min(a.slots, s_begin + per);
-  // Online merge over the group's slots in batches whose loads (LSE and o,
-  // the latter unconditionally: every slot is in bounds) are all issued
-  // before the first use, so a row costs one memory round trip per batch.
-  constexpr int B = 16;
   float m = -INFINITY, wsum = 0.f;
-  if (a.sinks && g == 0 && live) {   // the sink joins the normaliser as one more state with no value
-    m = a.sinks[row % a.hq];
-    wsum = m == -INFINITY ? 0.f : 1.f;
-  }
   f32x4_t acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = s_begin; live && s0 < s_end; s0 += B) {
-    float l[B];
-    f32x4_t x[B][NV];
-    u32x4_t w[F32 ? 1 : B];   // bf16 partials: raw words, widened once all loads are out
-#pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const int sl = min(s0 + k, s_end - 1);
-      l[k] = (s0 + k < s_end) ? a.part_lse[(int64_t)sl * a.rows + row] : -INFINITY;
-      const int64_t e = (int64_t)sl * a.slot_elems + row * D + part * V;
-      if constexpr (F32) x[k][0] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.part_o) + e);
-      else w[k] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.part_o) + e);
-    }
-    if constexpr (!F32) {
-#pragma unroll
-      for (int k = 0; k < B; ++k) {
-        x[k][0] = f32x4_t{bf16_lo(w[k][0]), bf16_hi(w[k][0]), bf16_lo(w[k][1]), bf16_hi(w[k][1])};
-        x[k][1] = f32x4_t{bf16_lo(w[k][2]), bf16_hi(w[k][2]), bf16_lo(w[k][3]), bf16_hi(w[k][3])};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < B; ++k) merge_step(m, wsum, acc, l[k], x[k]);
+  if (live) {
+    merge_seed(a, row, g, m, wsum);
+    merge_slot_range<D, F32>(a, row, part, g * per, min(a.slots, (g + 1) * per), m, wsum, acc);
   }
   if constexpr (SG > 1) {
     constexpr int F = V + 2;   // floats a thread publishes: acc, m, wsum
@@ -122,17 +221,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
       fold_state(m, wsum, acc, r[V], r[V + 1], o2);
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* dst = a.out + row * D + part * V;
-  if constexpr (NV == 1) {
-    const f32x4_t r = acc[0] * inv;
-    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-  } else {
-    const f32x4_t r0 = acc[0] * inv, r1 = acc[1] * inv;
-    *reinterpret_cast<u32x4_t*>(dst) =
-        u32x4_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]), pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
-  }
-  if (part == 0 && a.lse_out) a.lse_out[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+  merge_store<D, F32>(a, row, part, m, wsum, acc);
 }
 
 }  // namespace ca

@@ -80,6 +80,10 @@ struct CostModel {
   double kernel_floor_us = 7.5;   // shortest attention launch: dispatch, page-table and first-stage round trips, store
   double chunked_floor_us = 11.0; // shortest launch of KV-chunked decode items (partial states out)
   double merge_floor_us = 3.5;    // shortest merge launch (its bytes move at hbm_bw on top)
+  double inlaunch_merge_us = 3.0; // merge inside the attention launch: waiting for the partial states' stores
+                                  // and counting at the end of the last item of a row block
+  double inlaunch_trip_us = 2.0;  // one dependent round trip of that item's merge loads
+  double inlaunch_item_us = 2.5;  // every item's own end: its stores complete, then it is counted
   double mall_bytes = 256.0e6;    // Infinity Cache capacity
 };
 
@@ -235,25 +239,55 @@ static double items_cu_us(const ca_plan& pl, const PhaseTile& t, const int32_t* 
   return us;
 }
 
-// One merge launch that reads and writes `bytes` (partial states in, output
-// out): a fixed floor plus the bytes at the streaming rate.
-static double est_merge_us(double bytes, const CostModel& cm) { return cm.merge_floor_us + bytes / cm.hbm_bw * 1e6; }
+// The merge as a launch of its own, reading and writing `bytes` (partial
+// states in, output out): a fixed floor plus the bytes at the streaming rate,
+// plus the launch.
+static double est_merge_launch_us(double bytes, const CostModel& cm) {
+  return cm.merge_floor_us + bytes / cm.hbm_bw * 1e6 + cm.launch_us;
+}
+
+// The merge inside the attention launch: the item that completes a row
+// block merges every row it wrote (up to `winner_rows`), each thread two
+// 16-byte chunks of a row, slots in batches of 8 per slot group, one memory
+// round trip per batch and pass of the work-group's 256 threads, after the
+// wait for its own stores and the count. Every item also ends by waiting
+// for its stores and being counted, which lengthens each round of items on
+// the CUs (`items` work items, two resident per CU).
+static double est_merge_in_launch_us(const ca_plan& pl, int64_t winner_rows, int32_t slots, int64_t items,
+                                     int32_t cus, const CostModel& cm) {
+  const int64_t tpr = pl.d * (pl.part_fp32 ? 4 : 2) / 32;
+  const int64_t passes = cdiv(winner_rows * tpr, kThreads);
+  const int64_t sg = slots > 16 ? 4 : 1;
+  const int64_t batches = sg * cdiv(cdiv(slots, sg), 8);
+  const int64_t rounds = cdiv(std::max<int64_t>(items, 1), 2 * (int64_t)cus);
+  return cm.inlaunch_merge_us + cm.inlaunch_trip_us * (double)(passes * batches) +
+         cm.inlaunch_item_us * (double)(rounds - 1);
+}
+
+// Where a plan merges: inside the attention launch when asked (merge_mode 2)
+// or, by default, when the model prices it below the merge launch; never
+// with separate phase launches or when the per-request tiles need more
+// counters than the workspace reserves.
+static bool merges_in_launch(const ca_params_t& p, int64_t num_reqs, int64_t mtiles, int64_t hkv, double in_us,
+                             double launch_us) {
+  if (p.merge_mode == 1 || p.separate_phases != 0 || num_reqs * mtiles * hkv > kMaxCounters) return false;
+  return p.merge_mode == 2 || in_us < launch_us;
+}
 
 // Per-request phase over KV positions [key_start, seq_len): HBM bytes for the
 // KV actually streamed, plus the MFMA work of 16-row padded query blocks, but
 // no less than `floor_us` (the launch's item rounds; 0 when the phase overlaps
 // another in one launch).
 static double est_suffix_us(const ca_plan& pl, int64_t kv_tokens, double padded_flops, int32_t chunks, bool merge,
-                            int32_t cus, const CostModel& cm, double extra_mall_bytes, double floor_us) {
+                            double merge_us, int32_t cus, const CostModel& cm, double extra_mall_bytes,
+                            double floor_us) {
   const double bpt = 2.0 * pl.kv_bytes() * pl.hkv * pl.d;
   const double io = (double)pl.total_q * pl.hq * pl.d * 2.0 * 2.0;
   const double t_bytes = (bpt * kv_tokens + io) / cm.hbm_bw + extra_mall_bytes / cm.reread_bw;
   const double t_mfma = padded_flops / ((double)cus * cm.cu_mfma_rows);
   double us = std::max(std::max(t_bytes, t_mfma) * 1e6, floor_us) + cm.launch_us;
-  if (merge) {
-    const double part = (double)chunks * pl.total_q * pl.hq * pl.part_row_bytes();
-    us += est_merge_us(part + (double)pl.total_q * pl.hq * pl.d * 2.0, cm) + cm.launch_us;
-  }
+  if (merge) us += merge_us;
+  (void)chunks;
   return us;
 }
 
@@ -411,6 +445,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.suffix_order != 0 && p.suffix_order != 1) return fail(CA_EINVAL, "suffix_order must be 0 or 1");
   if (p.partials_fp32 != 0 && p.partials_fp32 != 1) return fail(CA_EINVAL, "partials_fp32 must be 0 or 1");
   if (p.use_tuned != 0 && p.use_tuned != 1) return fail(CA_EINVAL, "use_tuned must be 0 or 1");
+  if (p.merge_mode < 0 || p.merge_mode > 2) return fail(CA_EINVAL, "merge_mode must be 0, 1 or 2");
   if (!std::isfinite(p.k_scale) || !std::isfinite(p.v_scale)) return fail(CA_EINVAL, "k_scale / v_scale must be finite");
   if (p.kv_dtype == CA_KV_FP8_E4M3) {
     if (p.head_dim != 128) return fail(CA_EUNSUPPORTED, "fp8 caches need head_dim 128");
@@ -455,6 +490,9 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   pl->ps = ps;
   pl->total_q = total_q;
   pl->max_q_len = max_q;
+  pl->uniform_q = max_q;
+  for (int32_t r = 0; r < n; ++r)
+    if (qsl[r + 1] - qsl[r] != max_q) pl->uniform_q = 0;
   pl->max_seq_len = max_seq;
   pl->scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)p.head_dim);
   pl->kv_fp8 = p.kv_dtype == CA_KV_FP8_E4M3 ? 1 : 0;
@@ -493,10 +531,22 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   pl->key_start = 0;
   pl->max_suffix_len = max_seq;
   PhaseTile nc = choose_suffix(*pl, cus, true);
+  // merge of the non-cascade path's KV chunks: a launch, or inside the
+  // attention launch by the last chunk of each (request, row tile, KV head)
+  auto nc_merge = [&](const PhaseTile& t, bool* in_launch) {
+    const double bytes = (double)t.splits * total_q * pl->hq * pl->part_row_bytes() + (double)total_q * pl->hq * pl->d * 2.0;
+    const double ml = est_merge_launch_us(bytes, cm);
+    const int64_t items = (int64_t)n * t.mtiles * pl->hkv * t.splits;
+    const double mi =
+        est_merge_in_launch_us(*pl, (int64_t)t.rows_per_wg() * (t.kernel == 1 ? pl->hkv : 1), t.splits, items, cus, cm);
+    *in_launch = merges_in_launch(p, n, t.mtiles, pl->hkv, mi, ml);
+    return *in_launch ? mi : ml;
+  };
+  bool nc_in_launch = false;
   {
-    // Chunking a request's KV range fills the chip but adds the merge
-    // launch: keep one chunk per request (the attention writes the output)
-    // when the chunked plan does not save that launch's cost.
+    // Chunking a request's KV range fills the chip but adds the merge: keep
+    // one chunk per request (the attention writes the output) when the
+    // chunked plan does not save the merge's cost.
     const PhaseTile direct = choose_suffix(*pl, cus, false);
     if (direct.splits < nc.splits) {
       const double t_stage = nc.kernel == 1 ? cm.decode_stage_us : cm.rows_stage_us;
@@ -505,7 +555,9 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
         const double rounds = std::ceil((double)(base * t.splits) / (2.0 * cus));
         return rounds * (cm.item_latency_us + (double)(t.split_tokens / kTileKeys) * t_stage);
       };
-      if (items_us(direct) <= items_us(nc) + cm.launch_us + cm.merge_trip_us) nc = direct;
+      bool il = false;
+      const double m_us = nc_merge(nc, &il);
+      if (items_us(direct) <= items_us(nc) + m_us - cm.merge_floor_us + cm.merge_trip_us) nc = direct;
     }
     const double shared_bytes = bpt * plen;
     const double reread = shared_bytes * (n - 1);
@@ -520,8 +572,9 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     const double floor_us = nc.splits > 1 && nc.kernel == 1 ? cm.chunked_floor_us : cm.kernel_floor_us;
     const double t_items =
         std::max(std::max(floor_us, t_longest), items_cu_us(*pl, nc, qsl, seq_lens, nullptr, cm) / cus);
+    const double m_us = nc.splits > 1 ? nc_merge(nc, &nc_in_launch) : 0.0;
     pl->est_us_noncascade = (float)est_suffix_us(*pl, hbm_tokens, suffix_padded_flops(*pl, qsl, seq_lens, nullptr),
-                                                 nc.splits, nc.splits > 1, cus, cm, extra, t_items);
+                                                 nc.splits, nc.splits > 1, m_us, cus, cm, extra, t_items);
   }
 
   // Cascade estimate (only meaningful when something is shared): the
@@ -529,6 +582,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   // remaining positions, and the merge.
   PhaseTile pre, suf;
   Level1 lvl1;
+  bool casc_in_launch = false;
   std::vector<int64_t> kstart(n, plen);   // first suffix position of each request
   int64_t group_items = 0, group_stages = 0;
   if (plen > 0) {
@@ -587,7 +641,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->max_suffix_len = (int32_t)max_suffix;
     suf = choose_suffix(*pl, cus, true);
     const double t_suf = est_suffix_us(*pl, suffix_tokens, suffix_padded_flops(*pl, qsl, seq_lens, kstart.data()),
-                                       suf.splits, false, cus, cm, 0.0, 0.0);
+                                       suf.splits, false, 0.0, cus, cm, 0.0, 0.0);
     const double merge_bytes = (double)(pre.splits + lvl1.splits + suf.splits) * total_q * pl->hq * pl->part_row_bytes() +
                                (double)total_q * pl->hq * pl->d * 2.0;
     // The single launch also takes no less than its items' CU time (decode
@@ -603,7 +657,15 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
                          items_cu_us(*pl, suf, qsl, seq_lens, kstart.data(), cm, heads);
     const double t_launch = std::max(cm.kernel_floor_us, cu_us / cus) + cm.launch_us;
     // one launch runs the phases (t_suf carries its launch cost), one the merge
-    pl->est_us_cascade = (float)(std::max(pre_us + t_grp + t_suf, t_launch) + est_merge_us(merge_bytes, cm) + cm.launch_us);
+    // merge: a launch, or inside the launch by the item completing each row
+    // block (a prefix item completes a whole prefix tile's rows)
+    const int32_t c_slots = pre.splits + lvl1.splits + suf.splits;
+    const double ml = est_merge_launch_us(merge_bytes, cm);
+    const int64_t c_items = pre_items + group_items + (int64_t)n * suf.mtiles * (pl->hkv / std::max(1, heads)) * suf.splits;
+    const double mi = est_merge_in_launch_us(*pl, std::min<int64_t>(pre.rows_per_wg(), total_q * pl->group), c_slots,
+                                             c_items, cus, cm);
+    casc_in_launch = merges_in_launch(p, n, suf.mtiles, pl->hkv, mi, ml);
+    pl->est_us_cascade = (float)(std::max(pre_us + t_grp + t_suf, t_launch) + (casc_in_launch ? mi : ml));
     pl->kv_tokens_cascade = plen + group_tokens + suffix_tokens;
   }
 
@@ -655,12 +717,16 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     order_requests(*pl, p, seq_lens, zero.data());
   }
   pl->slot_elems = total_q * pl->hq * pl->d;
+  // Merge inside the attention launch (the estimate's choice above)
+  pl->merge_in_launch = (pl->num_slots > 0 && (cascade ? casc_in_launch : nc_in_launch)) ? 1 : 0;
   if (pl->num_slots > 0) {
     const int64_t o_bytes = round_up((int64_t)pl->num_slots * pl->slot_elems * (pl->part_fp32 ? 4 : 2), 256);
     const int64_t l_bytes = round_up((int64_t)pl->num_slots * total_q * pl->hq * 4, 256);
-    pl->ws_lse_offset = o_bytes;
-    pl->workspace_bytes = o_bytes + l_bytes;
+    pl->ws_o_offset = kCounterBytes;
+    pl->ws_lse_offset = kCounterBytes + o_bytes;
+    pl->workspace_bytes = kCounterBytes + o_bytes + l_bytes;
   } else {
+    pl->ws_o_offset = 0;
     pl->ws_lse_offset = 0;
     pl->workspace_bytes = 0;
   }
@@ -699,6 +765,7 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->num_partial_slots = pl->num_slots;
   out->prefix_stages = pl->use_cascade ? pl->prefix.stages : 0;
   out->suffix_stages = pl->suffix.stages;
+  out->merge_in_launch = pl->merge_in_launch;
   out->suffix_heads_per_item = pl->suffix.heads_per_item;
   out->separate_phases = pl->separate_phases;
   out->num_level1_groups = pl->lvl1.n;

@@ -37,6 +37,13 @@ constexpr int kMaxLevel1Groups = 64;
 // Requests whose work-item order a plan can set (kernel-argument table).
 constexpr int kOrderCapacity = 512;
 
+// The first kCounterBytes of every workspace hold the arrival counters of
+// the merge inside the attention launch (zero before a workspace's first
+// run; every run leaves them zero). Fixed size and place, so one workspace
+// serves any sequence of plans.
+constexpr int64_t kCounterBytes = int64_t(256) << 10;
+constexpr int64_t kMaxCounters = kCounterBytes / 4;
+
 struct Level1 {
   int32_t n = 0;                               // groups in use
   int32_t splits = 0;                          // KV splits of every group
@@ -54,6 +61,7 @@ struct ca_plan {
   int32_t num_reqs = 0, hq = 0, hkv = 0, group = 0, d = 0, ps = 0;
   int64_t total_q = 0;
   int32_t max_q_len = 0;
+  int32_t uniform_q = 0;       // > 0: every request has this many query tokens
   int32_t max_seq_len = 0;
   float scale = 0.f;
   int32_t kv_fp8 = 0;          // K/V caches hold fp8 e4m3 (1 byte per element)
@@ -79,6 +87,8 @@ struct ca_plan {
   int32_t separate_phases = 0;// cascade: prefix and suffix as two launches
   ca::Level1 lvl1;            // cascade: second shared level (n = 0: none)
   int64_t slot_elems = 0;     // T * Hq * d
+  int32_t merge_in_launch = 0;// partial states merged inside the attention launch (no merge launch)
+  int64_t ws_o_offset = 0;    // byte offset of the partial outputs (after the counters)
   int64_t ws_lse_offset = 0;  // byte offset of the partial LSE array
   int64_t workspace_bytes = 0;
 

@@ -7,7 +7,6 @@
 // a merge when the plan splits the KV range. All launches go to the
 // caller's stream in order; nothing here allocates or synchronises.
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -29,10 +28,10 @@ static_assert(K_KINDS == CA_PROFILE_KINDS, "profile kinds");
 
 // Kernel timing for measurement: a pool of HIP events created when timing
 // is enabled (outside any timed region); each launch takes the next start /
-// stop pair and carries it on its own dispatch (hipExtLaunchKernelGGL), so
-// the recorded time is the kernel's execution, with no event creation or
-// other host work added between launches. When the pool is used up, further
-// launches run untimed.
+// stop pair, recorded on the launch stream right before and right after it
+// (hipEventRecord markers, events without a system-scope fence: no event is
+// created and no host work is added between launches). When the pool is
+// used up, further launches run untimed.
 struct Profiler {
   std::mutex mu;
   bool enabled = false;
@@ -70,11 +69,9 @@ void launch(int kind, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... ar
       }
     }
   }
-  if (a) {
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
-    return;
-  }
+  if (a) (void)hipEventRecord(a, s);
   hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  if (b) (void)hipEventRecord(b, s);
 }
 
 ca_status_t fail(ca_status_t c, const std::string& m) {
@@ -89,23 +86,25 @@ ca_status_t check_launch(const char* what) {
 }
 
 template <int D, int RB, int RW, int KG, int NS, bool F8>
-void launch_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, int grid, hipStream_t s, int kind) {
+void launch_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt, int grid,
+                 hipStream_t s, int kind) {
   launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, (KG > 1) && !F8, F8>, dim3(grid), dim3(64 * RW * KG), s, args,
-         gt, ro);
+         gt, ro, mt);
 }
 
 // bf16 caches: 2 or 4 stages of 64 keys; fp8 caches (head_dim 128 only):
 // 4 stages, the same 64 KB of LDS.
 template <int D, int RB, int RW, int KG>
-void launch_tile_ns(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, int ns, bool f8, int grid, hipStream_t s, int kind) {
+void launch_tile_ns(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt, int ns,
+                    bool f8, int grid, hipStream_t s, int kind) {
   if constexpr (D == 128) {
     if (f8) {
-      launch_tile<D, RB, RW, KG, 4, true>(args, gt, ro, grid, s, kind);
+      launch_tile<D, RB, RW, KG, 4, true>(args, gt, ro, mt, grid, s, kind);
       return;
     }
   }
-  if (ns == 4) launch_tile<D, RB, RW, KG, 4, false>(args, gt, ro, grid, s, kind);
-  else launch_tile<D, RB, RW, KG, 2, false>(args, gt, ro, grid, s, kind);
+  if (ns == 4) launch_tile<D, RB, RW, KG, 4, false>(args, gt, ro, mt, grid, s, kind);
+  else launch_tile<D, RB, RW, KG, 2, false>(args, gt, ro, mt, grid, s, kind);
 }
 
 bool item_ok(const PhaseTile& ph) { return ph.split_tokens > 0 && ph.split_tokens <= kMaxItemTokens && ph.split_tokens % kTileKeys == 0; }
@@ -120,16 +119,16 @@ int shape_id(const PhaseTile& ph) {
 }
 
 template <int D>
-ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const PhaseTile& ph, int64_t grid, bool f8,
-                     hipStream_t s, int kind) {
+ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt,
+                     const PhaseTile& ph, int64_t grid, bool f8, hipStream_t s, int kind) {
   if (grid <= 0) return CA_OK;
   if (grid > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(ph)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   if (f8 && (D != 128 || ph.stages != 4)) return fail(CA_EINVAL, "fp8 plan needs head_dim 128 and 4 stages");
   switch (shape_id(ph)) {
-    case 0: launch_tile_ns<D, 1, 4, 1>(args, gt, ro, ph.stages, f8, (int)grid, s, kind); break;
-    case 1: launch_tile_ns<D, 2, 4, 1>(args, gt, ro, ph.stages, f8, (int)grid, s, kind); break;
-    case 2: launch_tile_ns<D, 1, 1, 4>(args, gt, ro, ph.stages, f8, (int)grid, s, kind); break;
+    case 0: launch_tile_ns<D, 1, 4, 1>(args, gt, ro, mt, ph.stages, f8, (int)grid, s, kind); break;
+    case 1: launch_tile_ns<D, 2, 4, 1>(args, gt, ro, mt, ph.stages, f8, (int)grid, s, kind); break;
+    case 2: launch_tile_ns<D, 1, 1, 4>(args, gt, ro, mt, ph.stages, f8, (int)grid, s, kind); break;
     default: return fail(CA_EINVAL, "unsupported work-group shape in plan");
   }
   return check_launch("attention kernel launch");
@@ -139,30 +138,31 @@ ca_status_t run_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder&
 // of bf16, or 4 of fp8.
 template <int D, int P, int S, bool F8>
 void launch_phases(const TileArgs& pa, const TileArgs& ga, const TileArgs& sa, int n_prefix, int n_group,
-                   const GroupTable& gt, const ReqOrder& ro, int grid, hipStream_t s) {
+                   const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt, int grid, hipStream_t s) {
   constexpr int PRB = P == 1 ? 2 : 1;
   constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
   constexpr int NS = F8 ? 4 : 2;
   launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, NS, 64, 1, SRW, SKG, NS, 64, F8>, dim3(grid), dim3(256), s,
-         pa, ga, sa, n_prefix, n_group, gt, ro);
+         pa, ga, sa, n_prefix, n_group, gt, ro, mt);
 }
 
 template <int D, bool F8>
 void launch_phases_shapes(int pid, int sid, const TileArgs& pa, const TileArgs& ga, const TileArgs& sa, int np,
-                          int ng, const GroupTable& gt, const ReqOrder& ro, int grid, hipStream_t s) {
+                          int ng, const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt, int grid,
+                          hipStream_t s) {
   if (sid == 0) {
-    if (pid == 0) launch_phases<D, 0, 0, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
-    else launch_phases<D, 1, 0, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
+    if (pid == 0) launch_phases<D, 0, 0, F8>(pa, ga, sa, np, ng, gt, ro, mt, grid, s);
+    else launch_phases<D, 1, 0, F8>(pa, ga, sa, np, ng, gt, ro, mt, grid, s);
   } else {
-    if (pid == 0) launch_phases<D, 0, 2, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
-    else launch_phases<D, 1, 2, F8>(pa, ga, sa, np, ng, gt, ro, grid, s);
+    if (pid == 0) launch_phases<D, 0, 2, F8>(pa, ga, sa, np, ng, gt, ro, mt, grid, s);
+    else launch_phases<D, 1, 2, F8>(pa, ga, sa, np, ng, gt, ro, mt, grid, s);
   }
 }
 
 template <int D>
 ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix, const TileArgs& ga,
                        int64_t n_group, const GroupTable& gt, const ReqOrder& ro, const TileArgs& sa, const PhaseTile& sp,
-                       int64_t n_suffix, bool f8, hipStream_t s) {
+                       int64_t n_suffix, const MergeTailArgs& mt, bool f8, hipStream_t s) {
   if (n_prefix + n_group + n_suffix > 0x7fffffff) return fail(CA_EINVAL, "grid too large");
   if (!item_ok(pp) || !item_ok(sp)) return fail(CA_EINVAL, "work item exceeds the per-item KV limit");
   const int pid = shape_id(pp), sid = shape_id(sp);
@@ -172,10 +172,10 @@ ca_status_t run_phases(const TileArgs& pa, const PhaseTile& pp, int64_t n_prefix
   const int grid = (int)(n_prefix + n_group + n_suffix);
   const int np = (int)n_prefix, ng = (int)n_group;
   if constexpr (D == 128) {
-    if (f8) launch_phases_shapes<D, true>(pid, sid, pa, ga, sa, np, ng, gt, ro, grid, s);
-    else launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, ro, grid, s);
+    if (f8) launch_phases_shapes<D, true>(pid, sid, pa, ga, sa, np, ng, gt, ro, mt, grid, s);
+    else launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, ro, mt, grid, s);
   } else {
-    launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, ro, grid, s);
+    launch_phases_shapes<D, false>(pid, sid, pa, ga, sa, np, ng, gt, ro, mt, grid, s);
   }
   return check_launch("cascade phases kernel launch");
 }
@@ -226,11 +226,36 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   base.slot_rows = pl->total_q * pl->hq;
   base.out = static_cast<uint16_t*>(out);
   base.lse_out = lse;
-  void* part_o = ws;
+  void* part_o = ws ? static_cast<char*>(ws) + pl->ws_o_offset : nullptr;
   float* part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl->ws_lse_offset) : nullptr;
   base.part_o = part_o;
   base.part_fp32 = pl->part_fp32;
   base.part_lse = part_lse;
+  // merge inside the attention launch: counters at the workspace's start
+  MergeTailArgs mt{};
+  mt.counters = (pl->merge_in_launch && ws) ? static_cast<int32_t*>(ws) : nullptr;
+  mt.qsl = qsl;
+  mt.part_o = part_o;
+  mt.part_lse = part_lse;
+  mt.out = base.out;
+  mt.lse_out = lse;
+  mt.sinks = sinks;
+  mt.slot_elems = base.slot_elems;
+  mt.slot_rows = base.slot_rows;
+  mt.part_fp32 = pl->part_fp32;
+  mt.merge_slots = pl->num_slots;
+  mt.hq = pl->hq;
+  mt.hkv = pl->hkv;
+  mt.group = pl->group;
+  mt.num_reqs = pl->num_reqs;
+  mt.m_pre_splits = pl->use_cascade ? pl->prefix.splits : 0;
+  mt.m_pre_rows = pl->use_cascade ? pl->prefix.rows_per_wg() : 1;
+  mt.m_lvl_splits = (pl->use_cascade && pl->lvl1.n > 0) ? pl->lvl1.splits : 0;
+  mt.m_suf_splits = pl->suffix.splits;
+  mt.m_suf_rows = pl->suffix.rows_per_wg();
+  mt.m_suf_mtiles = pl->suffix.mtiles;
+  mt.uniform_q = pl->uniform_q;
+  base.coherent = mt.counters ? 1 : 0;
 
   // second shared level (none: n = 0)
   GroupTable gt{};
@@ -295,17 +320,17 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     ga.direct = 0;
     const int64_t n_group = gt.n > 0 ? gt.item_begin[gt.n] : 0;
     if (pl->separate_phases) {
-      st = run_tile<D>(pa, gt, ro, pl->prefix, n_prefix, f8, s, K_PREFIX);
-      if (st == CA_OK) st = run_tile<D>(ga, gt, ro, pl->prefix, n_group, f8, s, K_LEVEL1);
-      if (st == CA_OK) st = run_tile<D>(sa, gt, ro, pl->suffix, n_suffix, f8, s, K_SUFFIX);
+      st = run_tile<D>(pa, gt, ro, mt, pl->prefix, n_prefix, f8, s, K_PREFIX);
+      if (st == CA_OK) st = run_tile<D>(ga, gt, ro, mt, pl->prefix, n_group, f8, s, K_LEVEL1);
+      if (st == CA_OK) st = run_tile<D>(sa, gt, ro, mt, pl->suffix, n_suffix, f8, s, K_SUFFIX);
     } else {
-      st = run_phases<D>(pa, pl->prefix, n_prefix, ga, n_group, gt, ro, sa, pl->suffix, n_suffix, f8, s);
+      st = run_phases<D>(pa, pl->prefix, n_prefix, ga, n_group, gt, ro, sa, pl->suffix, n_suffix, mt, f8, s);
     }
   } else {
-    st = run_tile<D>(sa, gt, ro, pl->suffix, n_suffix, f8, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
+    st = run_tile<D>(sa, gt, ro, mt, pl->suffix, n_suffix, f8, s, pl->suffix.kernel == 1 ? K_DECODE : K_ATTN);
   }
   if (st != CA_OK) return st;
-  if (!pl->direct_out) {
+  if (!pl->direct_out && !mt.counters) {
     MergeArgs ma{};
     ma.part_o = part_o;
     ma.part_lse = part_lse;
@@ -322,7 +347,26 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   return CA_OK;
 }
 
+// Sets n 32-bit words to zero (a kernel rather than a memset, so that it can
+// be recorded in a HIP graph like any launch).
+__global__ __launch_bounds__(256) void zero_words_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+ca_status_t zero_counters(void* ws, int64_t bytes, hipStream_t s) {
+  const int64_t n = std::min<int64_t>(bytes, kCounterBytes) / 4;
+  if (n <= 0) return CA_OK;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, static_cast<int32_t*>(ws), n);
+  return check_launch("workspace init launch");
+}
+
 }  // namespace
+
+extern "C" ca_status_t cascade_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace && workspace_bytes > 0) return fail(CA_EINVAL, "null workspace");
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255)) return fail(CA_EINVAL, "workspace must be 256-byte aligned");
+  return zero_counters(workspace, (int64_t)workspace_bytes, static_cast<hipStream_t>(stream));
+}
 
 extern "C" int ca_query_num_cus(int32_t* out) {
   int dev = 0;
@@ -371,8 +415,10 @@ std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
 // Device address of this device's scratch array (looked up once per device,
-// with that device current).
-ca_status_t scratch_for_current_device(void** out) {
+// with that device current). The array starts zeroed (static storage); its
+// merge counters are also cleared once here, by a kernel on the caller's
+// stream, ahead of the first run on this device; runs leave them zero.
+ca_status_t scratch_for_current_device(void** out, hipStream_t s) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(CA_EHIP, "hipGetDevice failed");
   if (dev < 0 || dev >= kMaxDevices) return fail(CA_EINVAL, "device index beyond the scratch table");
@@ -382,6 +428,8 @@ ca_status_t scratch_for_current_device(void** out) {
     const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess || !p)
       return fail(CA_EHIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    const ca_status_t st = zero_counters(p, kCounterBytes, s);
+    if (st != CA_OK) return st;
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
@@ -400,11 +448,11 @@ extern "C" ca_status_t cascade_attn_run_noalloc(ca_plan_t pl, const void* q, con
                                    std::to_string(kScratchBytes) + " (use cascade_attn_run with a workspace)");
   void* ws = nullptr;
   if (pl->workspace_bytes > 0) {
-    const ca_status_t st = scratch_for_current_device(&ws);
+    const ca_status_t st = scratch_for_current_device(&ws, static_cast<hipStream_t>(stream));
     if (st != CA_OK) return st;
   }
-  // the kernels overwrite every partial state they read back: nothing in the
-  // array needs clearing between calls
+  // the kernels overwrite every partial state they read back, and the merge
+  // counters at the array's start return to zero at the end of every run
   return cascade_attn_run(pl, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, sinks_d, out,
                           lse_out, ws, ws ? kScratchBytes : 0, stream);
 }
@@ -417,8 +465,11 @@ extern "C" ca_status_t cascade_attn_profile_enable(int32_t capacity) {
   if (capacity == 0) return CA_OK;
   g_prof.pool.reserve(2 * (size_t)capacity);
   for (int32_t i = 0; i < 2 * capacity; ++i) {
+    // no system-scope fence when an event is recorded: the events only time
+    // kernels, and the fence's cache write-back / invalidation would slow
+    // the launches around it
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       g_prof.release();
       return fail(CA_EHIP, "event creation failed");
     }

@@ -179,6 +179,7 @@ static void fuzz(std::mt19937& rng, int iters) {
     p.suffix_order = U(0, 1);
     p.partials_fp32 = U(0, 1);
     p.use_tuned = U(0, 1);
+    p.merge_mode = U(0, 2);
     if (U(0, 3) == 0) p.prefix_splits = U(1, 70);
     if (U(0, 3) == 0) {
       const int h = U(1, hh[1]);
@@ -298,6 +299,7 @@ static void error_paths() {
       {[](ca_params_t& p) { p.suffix_order = 2; }, CA_EINVAL, "suffix_order"},
       {[](ca_params_t& p) { p.partials_fp32 = 2; }, CA_EINVAL, "partials_fp32"},
       {[](ca_params_t& p) { p.use_tuned = 2; }, CA_EINVAL, "use_tuned"},
+      {[](ca_params_t& p) { p.merge_mode = 3; }, CA_EINVAL, "merge_mode"},
       {[](ca_params_t& p) { p.k_scale = 1.0f / 0.0f; }, CA_EINVAL, "k_scale"},
       {[](ca_params_t& p) { p.kv_dtype = CA_KV_FP8_E4M3; p.head_dim = 64; p.kv_stride_page = 16 * 2 * 64;
                             p.kv_stride_token = 128; p.kv_stride_head = 64; }, CA_EUNSUPPORTED, "fp8 head_dim"},

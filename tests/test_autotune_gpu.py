@@ -46,7 +46,7 @@ def test_autotune_picks_a_valid_plan_and_records_it(name):
     b = workloads.make_batch(workloads.get(name))
     db = DeviceBatch(b)
     auto = plan(b, mode="auto")
-    ws = torch.empty(max(auto.workspace_bytes, 64 << 20), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(auto.workspace_bytes, 64 << 20), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(db.q)
     lse = torch.empty(b.total_q, b.workload.num_q_heads, dtype=torch.float32, device="cuda")
     tuned, us = spa.cascade_attn_autotune(db.q, db.k, db.v, db.bt, db.qsl, db.sl, out, lse, ws, iters=5,

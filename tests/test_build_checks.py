@@ -14,12 +14,12 @@ from shared_prefix_attention_amd import lds_wait_check as L
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _remarks(scratch="0", vspill="0"):
+def _remarks(scratch="0", vspill="0", sspill="0"):
     return "\n".join([
         "x.hpp:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
         "x.hpp:1:1: remark:     VGPRs: 100 [-Rpass-analysis=kernel-resource-usage]",
         f"x.hpp:1:1: remark:     ScratchSize [bytes/lane]: {scratch} [-Rpass-analysis=kernel-resource-usage]",
-        "x.hpp:1:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        f"x.hpp:1:1: remark:     SGPRs Spill: {sspill} [-Rpass-analysis=kernel-resource-usage]",
         f"x.hpp:1:1: remark:     VGPRs Spill: {vspill} [-Rpass-analysis=kernel-resource-usage]",
         "x.hpp:1:1: remark:     Dynamic Stack: False [-Rpass-analysis=kernel-resource-usage]",
     ])
@@ -27,6 +27,7 @@ def _remarks(scratch="0", vspill="0"):
 
 def test_resource_gate():
     assert B.check_resource_usage(_remarks())[0]["name"] == "kern_a"
+    assert B.check_resource_usage(_remarks(sspill="9"))[0]["SGPRs Spill"] == "9"   # VGPR lanes, no memory
     with pytest.raises(RuntimeError):
         B.check_resource_usage(_remarks(scratch="16"))
     with pytest.raises(RuntimeError):

@@ -274,14 +274,48 @@ def test_heads_per_item_choice_and_override():
 
 
 def test_separate_phases_changes_only_the_launch_count():
-    """Asking for the cascade phases as two launches leaves every other
-    decision of the plan as it was; a non-cascade plan ignores it."""
+    """Asking for the cascade phases as two launches (which then need the
+    merge as a launch of its own) leaves the partition as it was; a
+    non-cascade plan ignores it. merge_mode=1 keeps one attention launch but
+    moves the merge to a launch of its own, the partition again unchanged."""
     wd = workloads.make_batch(workloads.get("worked_decode"))
     fused, split = _plan(wd, mode="on").info, _plan(wd, mode="on", separate_phases=1).info
+    sep_merge = _plan(wd, mode="on", merge_mode=1).info
+    in_launch = _plan(wd, mode="on", merge_mode=2).info
     assert fused["separate_phases"] == 0 and split["separate_phases"] == 1
-    assert {k: v for k, v in fused.items() if k != "separate_phases"} == \
-        {k: v for k, v in split.items() if k != "separate_phases"}
+    assert in_launch["merge_in_launch"] == 1 and split["merge_in_launch"] == 0 and sep_merge["merge_in_launch"] == 0
+    assert _plan(wd, mode="on", separate_phases=1, merge_mode=2).info["merge_in_launch"] == 0
+    launch_only = ("separate_phases", "merge_in_launch", "est_us_cascade")
+    assert {k: v for k, v in fused.items() if k not in launch_only} == \
+        {k: v for k, v in split.items() if k not in launch_only}
+    assert {k: v for k, v in fused.items() if k not in launch_only} == \
+        {k: v for k, v in sep_merge.items() if k not in launch_only}
+    assert {k: v for k, v in fused.items() if k not in launch_only} == \
+        {k: v for k, v in in_launch.items() if k not in launch_only}
     assert _plan(wd, mode="off", separate_phases=1).info["separate_phases"] == 0
+    with pytest.raises(spa.CascadeAttnError) as e:
+        _plan(wd, mode="on", merge_mode=3)
+    assert e.value.status == _lib.CA_EINVAL
+
+
+def test_workspace_layout_reserves_the_merge_counters():
+    """Every plan with partial states reserves the merge counters at the
+    workspace's start, whatever its merge mode; direct plans need none."""
+    for name, mode in (("worked_decode", "on"), ("mixed_prefill", "on"), ("long_doc_n8", "off"),
+                       ("self_consistency", "off")):
+        b = workloads.make_batch(workloads.get(name))
+        for mm in (1, 2):
+            info = _plan(b, mode=mode, merge_mode=mm).info
+            w = b.workload
+            T = int(b.total_q)
+            slots = info["num_partial_slots"]
+            assert slots > 0
+            o = -(-slots * T * w.num_q_heads * w.head_dim * 2 // 256) * 256
+            l = -(-slots * T * w.num_q_heads * 4 // 256) * 256
+            assert info["workspace_bytes"] == _lib.WORKSPACE_COUNTER_BYTES + o + l
+            assert info["merge_in_launch"] == (mm - 1)
+    tiny = _plan(workloads.make_batch(workloads.get("tiny_decode")), mode="off").info
+    assert tiny["num_partial_slots"] == 0 and tiny["workspace_bytes"] == 0 and tiny["merge_in_launch"] == 0
 
 
 def test_auto_takes_the_measured_faster_path():

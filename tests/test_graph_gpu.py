@@ -29,7 +29,7 @@ def test_graph_replays_match_eager(name, mode):
     pl = plan(b, mode=mode)
     out = torch.empty_like(db.q)
     lse = torch.empty(b.total_q, b.workload.num_q_heads, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(pl.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(pl.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
 
     def run_into(o, l):
         spa.cascade_attn_run(pl, db.q, db.k, db.v, db.bt, db.qsl, db.sl, o, l, ws)

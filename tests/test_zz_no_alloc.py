@@ -26,7 +26,7 @@ def _both(b, mode):
     db = DeviceBatch(b)
     pl = plan(b, mode=mode, k_cache=db.k)
     T, hq = db.q.shape[0], db.q.shape[1]
-    ws = torch.empty(max(pl.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(pl.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     o_ref = torch.empty_like(db.q)
     l_ref = torch.empty(T, hq, dtype=torch.float32, device="cuda")
     spa.cascade_attn_run(pl, db.q, db.k, db.v, db.bt, db.qsl, db.sl, o_ref, l_ref, ws)
