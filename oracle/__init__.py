@@ -32,6 +32,8 @@ from .cascade_ref import (  # noqa: F401
     kv_tokens_cascade,
     level1_groups,
     kv_tokens_multilevel,
+    tree_groups,
+    kv_tokens_tree,
     fp8_e4m3_decode,
     MIN_PREFIX_TOKENS,
     MIN_NUM_REQS,

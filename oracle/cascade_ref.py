@@ -280,6 +280,75 @@ def kv_tokens_multilevel(level0_len, groups, seq_lens):
     return int(level0_len) + extra + int(sum(int(s) - st for s, st in zip(seq_lens, start)))
 
 
+def tree_groups(block_table, seq_lens, num_computed_tokens, page_size, level0_len, min_members=2,
+                min_extra_tokens=MIN_PREFIX_TOKENS, max_levels=4):
+    """Nested request groups of a multi-level cascade, found with a prefix tree.
+
+    FlashInfer's cascade takes any number of levels ([p2] section 7) and the
+    workloads of [p2] section 3 nest (a system prompt shared by all, a
+    document shared by some, a chapter by fewer). The pages give the
+    batch-wide rule only ([p2] section 8 Steps 1-2: shared leading pages,
+    capped at the smallest num_computed_tokens, floored to a page); this
+    applies it at every node of the prefix tree of the requests' page-id
+    sequences. Starting from all requests (the batch-wide prefix,
+    ``level0_len``, is level 0): let C be the number of leading pages every
+    member shares; split the members (those with more than C pages) by their
+    page at column C. A part of at least ``min_members`` requests gets its
+    shared length L = its own shared pages in tokens, capped at its smallest
+    num_computed_tokens, floored to a page. If L exceeds the length of the
+    group it lies in by at least ``min_extra_tokens`` (the prefix-length gate
+    of [p2] section 3) it is a group one level deeper, and its parts are
+    examined against it; otherwise its parts are examined against the same
+    enclosing group. Groups deeper than ``max_levels - 1`` are not formed.
+
+    Returns (members, parent_len, shared_len, level) tuples in the order found
+    (a group before the groups inside it); members in batch order.
+    """
+    bt = [list(map(int, row)) for row in block_table]
+    sl = [int(s) for s in seq_lens]
+    nc = [int(x) for x in num_computed_tokens]
+    ps = int(page_size)
+    pages = [-(-s // ps) for s in sl]
+    found = []
+
+    def shared_pages(members):
+        return common_prefix_blocks([bt[r] for r in members], [sl[r] for r in members], ps)
+
+    def visit(members, parent_len, level):
+        c = shared_pages(members)
+        parts = {}
+        for r in members:
+            if pages[r] > c:
+                parts.setdefault(bt[r][c], []).append(r)
+        for part in parts.values():
+            if len(part) < min_members:
+                continue
+            length = cascade_prefix_len(shared_pages(part), ps, [nc[r] for r in part])
+            if length - parent_len >= min_extra_tokens and level + 1 <= max_levels - 1:
+                found.append((tuple(part), int(parent_len), int(length), level + 1))
+                visit(part, length, level + 1)
+            else:
+                visit(part, parent_len, level)
+
+    if bt:
+        visit(list(range(len(bt))), int(level0_len), 0)
+    return found
+
+
+def kv_tokens_tree(level0_len, groups, seq_lens):
+    """KV positions read by a multi-level cascade: the batch-wide prefix once,
+    each group's positions beyond the group it lies in once, and each
+    request's positions past its innermost group ([p2] section 5's
+    accounting, applied at every level)."""
+    start = [int(level0_len)] * len(seq_lens)
+    extra = 0
+    for members, parent_len, length, _ in groups:
+        extra += int(length) - int(parent_len)
+        for r in members:
+            start[r] = max(start[r], int(length))
+    return int(level0_len) + extra + int(sum(int(s) - st for s, st in zip(seq_lens, start)))
+
+
 def fp8_e4m3_decode(codes):
     """Values of fp8 e4m3 codes (uint8) as float64.
 

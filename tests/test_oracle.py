@@ -481,6 +481,164 @@ def test_kv_tokens_multilevel_hand():
     assert oracle.kv_tokens_multilevel(16, [], [60, 70, 30]) == oracle.kv_tokens_cascade(16, [60, 70, 30])
 
 
+# ------------------------------------------------------- prefix-tree levels
+
+# Seven requests, page size 1 (so pages are tokens), level 0 = the 2 pages
+# P0 P1 every row starts with. Requests 0, 2 and 4 (not consecutive) share a
+# document A A A (pages 10-12); within it 0 and 4 share a chapter C C (20,
+# 21); requests 1 and 3 share a document B B B (30-32); request 5 shares one
+# page (40) with request 6, and then 5 and 6 part.
+_T_BT = [[0, 1, 10, 11, 12, 20, 21, 50, 0],
+         [0, 1, 30, 31, 32, 51, 0, 0, 0],
+         [0, 1, 10, 11, 12, 52, 0, 0, 0],
+         [0, 1, 30, 31, 32, 53, 54, 0, 0],
+         [0, 1, 10, 11, 12, 20, 21, 55, 56],
+         [0, 1, 40, 57, 0, 0, 0, 0, 0],
+         [0, 1, 40, 58, 59, 0, 0, 0, 0]]
+_T_SEQ = [8, 6, 6, 7, 9, 4, 5]
+
+
+def test_tree_groups_hand_case():
+    """Worked by hand (min_extra_tokens 2, every request computed all but its
+    last token). Level 0 is 2 pages. At column 2 the rows split into {0, 2,
+    4} (page 10), {1, 3} (page 30) and {5, 6} (page 40). {0, 2, 4} shares 5
+    pages -> 5 tokens, 3 more than level 0: a level-1 group; inside it, at
+    column 5, {0, 4} (page 20) shares 7 -> 7 tokens, 2 more: a level-2 group.
+    {1, 3} shares 5 -> level 1. {5, 6} shares 3 pages, 1 more than level 0:
+    not a group (and its rows part at column 3)."""
+    nc = [s - 1 for s in _T_SEQ]
+    want = [((0, 2, 4), 2, 5, 1), ((0, 4), 5, 7, 2), ((1, 3), 2, 5, 1)]
+    assert oracle.tree_groups(_T_BT, _T_SEQ, nc, 1, 2, min_extra_tokens=2) == want
+    # two shared levels at most: the chapter is not formed
+    assert oracle.tree_groups(_T_BT, _T_SEQ, nc, 1, 2, min_extra_tokens=2, max_levels=2) == [want[0], want[2]]
+    # the cap: request 4 has computed only 6 tokens, so {0, 4} shares 6, 1
+    # more than its document -- not a group
+    nc2 = list(nc)
+    nc2[4] = 6
+    assert oracle.tree_groups(_T_BT, _T_SEQ, nc2, 1, 2, min_extra_tokens=2) == [want[0], want[2]]
+    # a gate of 3 leaves the documents; with 4 neither document passes, but
+    # the chapter {0, 4}, 5 tokens past level 0, becomes a level-1 group;
+    # with 6 nothing is left
+    assert oracle.tree_groups(_T_BT, _T_SEQ, nc, 1, 2, min_extra_tokens=3) == [want[0], want[2]]
+    assert oracle.tree_groups(_T_BT, _T_SEQ, nc, 1, 2, min_extra_tokens=4) == [((0, 4), 2, 7, 1)]
+    assert oracle.tree_groups(_T_BT, _T_SEQ, nc, 1, 2, min_extra_tokens=6) == []
+    # KV positions: level 0 (2) + A's 3 + C's 2 + B's 3 + each request past its innermost group
+    rest = [8 - 7, 6 - 5, 6 - 5, 7 - 5, 9 - 7, 4 - 2, 5 - 2]
+    assert oracle.kv_tokens_tree(2, want, _T_SEQ) == 2 + 3 + 2 + 3 + sum(rest)
+
+
+def test_tree_groups_look_past_a_small_split():
+    """Four requests share one page beyond level 0 (too little for a group);
+    inside it two pairs share three more each: the pairs are groups one level
+    below level 0, their extra length counted from level 0."""
+    bt = [[0, 1, 9, 10, 11, 12, 60], [0, 1, 9, 10, 11, 12, 61], [0, 1, 9, 20, 21, 22, 62], [0, 1, 9, 20, 21, 22, 63]]
+    seq = [7, 7, 7, 7]
+    nc = [6] * 4
+    assert oracle.tree_groups(bt, seq, nc, 1, 2, min_extra_tokens=3) == [((0, 1), 2, 6, 1), ((2, 3), 2, 6, 1)]
+
+
+def _tree_brute(bt, seq, nc, ps, level0, min_extra, max_levels):
+    """Declarative form: a set of >= 2 requests (not the whole batch) is a
+    candidate if no other request shares all the pages its members share;
+    candidates are taken largest first, each measured against the smallest
+    accepted group that contains it (or level 0)."""
+    n = len(bt)
+    sets = []
+    for mask in range(1, 1 << n):
+        S = [r for r in range(n) if mask >> r & 1]
+        if len(S) < 2 or len(S) == n:
+            continue
+        c = oracle.common_prefix_blocks([bt[r] for r in S], [seq[r] for r in S], ps)
+        closed = all(oracle.common_prefix_blocks([bt[r] for r in S + [o]], [seq[r] for r in S + [o]], ps) < c
+                     for o in range(n) if o not in S)
+        if closed:
+            sets.append((S, c))
+    sets.sort(key=lambda x: -len(x[0]))
+    accepted = []
+    for S, c in sets:
+        parent_len, level = level0, 0
+        for T, plen, tlen, tlev in sorted(accepted, key=lambda g: len(g[0])):
+            if set(S) < set(T):
+                parent_len, level = tlen, tlev
+                break
+        length = oracle.cascade_prefix_len(c, ps, [nc[r] for r in S])
+        if length - parent_len >= min_extra and level + 1 <= max_levels - 1:
+            accepted.append((tuple(S), parent_len, length, level + 1))
+    return sorted(accepted)
+
+
+def test_tree_groups_brute_force_tiny():
+    rng = np.random.default_rng(43)
+    checked = 0
+    for _ in range(1200):
+        n = int(rng.integers(2, 7))
+        cols = int(rng.integers(3, 7))
+        ps = int(rng.integers(1, 3))
+        bt = rng.integers(0, 3, (n, cols)).tolist()
+        for row in bt:
+            row[0] = 7
+        lens = rng.integers(ps + 1, cols * ps + 1, n).tolist()
+        nc = [int(rng.integers(1, x + 1)) for x in lens]
+        level0 = oracle.cascade_prefix_len(oracle.common_prefix_blocks(bt, lens, ps), ps, nc)
+        ml = int(rng.integers(2, 5))
+        got = sorted(oracle.tree_groups(bt, lens, nc, ps, level0, min_extra_tokens=1, max_levels=ml))
+        assert got == _tree_brute(bt, lens, nc, ps, level0, 1, ml)
+        checked += bool(got)
+    assert checked > 100
+
+
+def test_tree_groups_match_the_consecutive_runs():
+    """On batches whose documents are consecutive runs, the tree's level-1
+    groups are the runs the second-level rule finds."""
+    for name in ("multi_doc", "multi_doc_prefill"):
+        b = workloads.make_batch(workloads.get(name))
+        bt, sl, nc = b.block_table.numpy(), b.seq_lens.numpy(), b.num_computed.numpy()
+        p0 = oracle.cascade_prefix_len(oracle.common_prefix_blocks(bt, sl, 16), 16, nc)
+        runs = oracle.level1_groups(bt, sl, nc, 16, p0)
+        tree = oracle.tree_groups(bt, sl, nc, 16, p0)
+        assert [(m[0], m[-1] + 1, L) for m, _, L, lev in tree if lev == 1] == runs
+        assert all(lev == 1 for *_, lev in tree)
+
+
+def test_tree_split_equals_full_attention():
+    """A three-level tree with interleaved members, computed with the
+    oracle's own pieces -- every query over the level-0 prefix, each group's
+    queries over its positions beyond the group it lies in (non-causal), each
+    request over the rest (causal), LSE merge -- equals full attention."""
+    w = workloads.Workload("tree", 8, 16, (3, 20), (1, 4), 4, 2, 16, page_size=8, seed=23,
+                           docs=(((0, 2, 4, 6), 24), ((1, 3, 5), 16), ((0, 4), 19), ((3, 5), 21)))
+    b = workloads.make_batch(w)
+    G = w.num_q_heads // w.num_kv_heads
+    bt, qsl, sl = b.block_table.numpy(), b.query_start_loc.numpy(), b.seq_lens.numpy()
+    full_o, full_l = oracle.attention_full(b.q.float().numpy(), b.k_cache.float().numpy(),
+                                           b.v_cache.float().numpy(), bt, qsl, sl, w.page_size)
+    nc = b.num_computed.numpy()
+    p0 = oracle.cascade_prefix_len(oracle.common_prefix_blocks(bt, sl, 8), 8, nc)
+    groups = oracle.tree_groups(bt, sl, nc, 8, p0, min_extra_tokens=1)
+    # whole shared pages only: the chapters (19, 21 tokens) share 16 each
+    assert p0 == 16 and groups == [((0, 2, 4, 6), 16, 40, 1), ((0, 4), 40, 56, 2), ((1, 3, 5), 16, 32, 1),
+                                   ((3, 5), 32, 48, 2)]
+    assert oracle.kv_tokens_tree(p0, groups, sl) == 16 + 24 + 16 + 16 + 16 + sum(
+        int(sl[r]) - s for r, s in enumerate([56, 32, 40, 48, 56, 48, 40, 16]))
+    for r in range(w.num_reqs):
+        q0, q1 = int(qsl[r]), int(qsl[r + 1])
+        k, v = _dense_kv(b, r)
+        pos = int(nc[r]) + np.arange(q1 - q0)
+        bounds = [0, p0] + [L for m, _, L, _ in groups if r in m]
+        for h in range(w.num_q_heads):
+            g = h // G
+            rows = b.q[q0:q1, h].double().numpy()
+            parts = [oracle.attend(rows, k[a:e, g].numpy(), v[a:e, g].numpy(), w.softmax_scale)
+                     for a, e in zip(bounds[:-1], bounds[1:])]
+            t = np.arange(bounds[-1], k.shape[0])
+            vis = t[None, :] <= pos[:, None]
+            parts.append(oracle.attend(rows, k[bounds[-1]:, g].numpy(), v[bounds[-1]:, g].numpy(), w.softmax_scale,
+                                       vis))
+            o_m, l_m = oracle.merge_states([p[0] for p in parts], [p[1] for p in parts])
+            assert np.abs(o_m - full_o[q0:q1, h]).max() < 1e-12
+            assert np.abs(l_m - full_l[q0:q1, h]).max() < 1e-12
+
+
 # ------------------------------------------------- sinks and sliding window
 
 def test_sink_hand_case():

@@ -31,6 +31,14 @@ a document of L_g tokens after the batch-wide prefix (system prompt ->
 document -> own tokens). Members get ``seq_len = P + L_g + S_r``; the
 document's full pages are physically shared by the members and a partial
 last document page is copied into each member's own first page.
+
+Documents in a tree (``docs``): any sets of requests, not only consecutive
+ones, each sharing a document after the prefix and after the documents of
+every earlier-listed set that contains it (the sets must nest or be
+disjoint: system prompt -> document -> chapter -> own tokens). A request's
+sequence is the prefix, its documents outermost first, then its own tokens.
+Documents that contain others must fill whole pages; the innermost may end
+in a partial page, which is copied into each member's own first page.
 """
 
 from __future__ import annotations
@@ -62,6 +70,9 @@ class Workload:
     # (members, shared tokens): runs of consecutive requests from request 0
     # that share a document after the prefix; remaining requests share none
     groups: Tuple[Tuple[int, int], ...] = ()
+    # (member request indices, shared tokens): documents of a prefix tree, outer
+    # documents first; the member sets nest or are disjoint
+    docs: Tuple[Tuple[Tuple[int, ...], int], ...] = ()
     kv_dtype: str = "bf16"           # "bf16" or "fp8" (e4m3 codes, dequantised by the scales)
     k_scale: float = 1.0
     v_scale: float = 1.0
@@ -147,15 +158,26 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
     suffix = torch.randint(s_lo, s_hi + 1, (n,), generator=gen)
     qlen = torch.randint(q_lo, q_hi + 1, (n,), generator=gen)
     qlen = torch.minimum(qlen, suffix)
-    grp_of = [-1] * n
+    # documents: the consecutive runs of `groups`, then the tree of `docs`
+    docs = []
     r = 0
-    for gi, (members, _) in enumerate(w.groups):
-        for _ in range(members):
-            grp_of[r] = gi
-            r += 1
-    assert r <= n and (not w.groups or w.prefix % ps == 0)
-    grp_len = [g[1] for g in w.groups]
-    doc = torch.tensor([grp_len[g] if g >= 0 else 0 for g in grp_of], dtype=suffix.dtype)
+    for members, tokens in w.groups:
+        docs.append((tuple(range(r, r + members)), tokens))
+        r += members
+    assert r <= n
+    docs += [(tuple(m), t) for m, t in w.docs]
+    chain = [[] for _ in range(n)]     # documents of each request, outermost first
+    for di, (members, _) in enumerate(docs):
+        for m in members:
+            if chain[m]:   # nested: the enclosing document holds every member of this one
+                assert set(members) <= set(docs[chain[m][-1]][0]), "document sets must nest or be disjoint"
+            chain[m].append(di)
+    assert not docs or w.prefix % ps == 0
+    for r in range(n):
+        for di in chain[r][:-1]:
+            assert docs[di][1] % ps == 0, "a document that contains others must fill whole pages"
+    doc_tokens = [sum(docs[di][1] for di in chain[r]) for r in range(n)]
+    doc = torch.tensor(doc_tokens, dtype=suffix.dtype)
     seq = suffix + w.prefix + doc
     for r, sl, ql in w.override:
         seq[r] = sl
@@ -164,17 +186,17 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
     q_l = [int(x) for x in qlen]
 
     shared_pages = w.prefix // ps
-    grp_pages = [L // ps for L in grp_len]            # full document pages, shared by the members
-    lead = [shared_pages + (grp_pages[g] if g >= 0 else 0) for g in grp_of]   # shared columns of each row
+    doc_pages = [t // ps for _, t in docs]          # full document pages, shared by the members
+    lead = [shared_pages + sum(doc_pages[di] for di in chain[r]) for r in range(n)]   # shared columns
     own_pages = [-(-s // ps) - lead[r] for r, s in enumerate(seq_l)]
-    used = shared_pages + sum(grp_pages) + sum(own_pages)
+    used = shared_pages + sum(doc_pages) + sum(own_pages)
     num_pages = used + max(1, int(math.ceil(0.05 * used)))
     perm = torch.randperm(num_pages, generator=gen)
     shared_ids = perm[:shared_pages]
     pos = shared_pages
-    grp_ids = []
-    for k in grp_pages:
-        grp_ids.append(perm[pos:pos + k])
+    doc_ids = []
+    for k in doc_pages:
+        doc_ids.append(perm[pos:pos + k])
         pos += k
     own_ids = []
     for k in own_pages:
@@ -185,8 +207,10 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
     block_table = torch.randint(0, num_pages, (n, stride), generator=gen, dtype=torch.int64)
     for r in range(n):
         block_table[r, :shared_pages] = shared_ids
-        if grp_of[r] >= 0:
-            block_table[r, shared_pages:lead[r]] = grp_ids[grp_of[r]]
+        col = shared_pages
+        for di in chain[r]:
+            block_table[r, col:col + doc_pages[di]] = doc_ids[di]
+            col += doc_pages[di]
         block_table[r, lead[r]:lead[r] + own_pages[r]] = own_ids[r]
 
     nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
@@ -197,10 +221,10 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
         if shared_pages:
             cache[shared_ids] = prefix_vals[:shared_pages * ps].reshape(shared_pages, ps, hkv, d)
         doc_vals = []
-        for g, L in enumerate(grp_len):
+        for di, (_, L) in enumerate(docs):
             vals = _randn((L, hkv, d), gen, w.outlier_frac, w.outlier_scale)
-            if grp_pages[g]:
-                cache[grp_ids[g]] = vals[:grp_pages[g] * ps].reshape(grp_pages[g], ps, hkv, d)
+            if doc_pages[di]:
+                cache[doc_ids[di]] = vals[:doc_pages[di] * ps].reshape(doc_pages[di], ps, hkv, d)
             doc_vals.append(vals)
         for r in range(n):
             start = lead[r] * ps
@@ -212,10 +236,12 @@ def make_batch(w: Workload, seed: Optional[int] = None) -> Batch:
             in_prefix = t < w.prefix
             if bool(in_prefix.any()):
                 own_vals[in_prefix] = prefix_vals[t[in_prefix]]
-            if grp_of[r] >= 0:   # the partial last page of the document
-                in_doc = (t >= w.prefix) & (t < w.prefix + grp_len[grp_of[r]])
+            if chain[r]:   # the partial last page of the innermost document
+                leaf = chain[r][-1]
+                d0 = w.prefix + sum(docs[di][1] for di in chain[r][:-1])
+                in_doc = (t >= d0) & (t < d0 + docs[leaf][1])
                 if bool(in_doc.any()):
-                    own_vals[in_doc] = doc_vals[grp_of[r]][t[in_doc] - w.prefix]
+                    own_vals[in_doc] = doc_vals[leaf][t[in_doc] - d0]
             pages = own_ids[r][(t - start) // ps]
             cache[pages, t % ps] = own_vals
         caches.append(cache)
