@@ -101,9 +101,10 @@ typedef struct {
   int32_t heads_per_item;      /* KV heads one decode-shaped suffix item runs back to back
                                   (0 = planner's choice; else must divide num_kv_heads;
                                   ignored for items of more than 16 rows) */
-  int32_t max_levels;          /* shared levels of the cascade path: 0 = planner default (2);
-                                  1 = the batch-wide prefix only; 2 = also groups of consecutive
-                                  requests sharing more pages (see cascade_attn_plan_groups) */
+  int32_t max_levels;          /* shared levels of the cascade path, 0..4: 0 = planner default (4);
+                                  1 = the batch-wide prefix only; L >= 2 = also nested groups of
+                                  requests (any, not only consecutive) that share more pages, up to
+                                  L - 1 levels below the prefix (see cascade_attn_plan_groups) */
   int32_t kv_dtype;            /* ca_kv_dtype_t */
   float k_scale;               /* fp8: K dequantisation factor (<= 0 selects 1); ignored for bf16 */
   float v_scale;               /* fp8: V dequantisation factor (<= 0 selects 1); ignored for bf16 */
@@ -122,8 +123,9 @@ typedef struct {
   int32_t merge_mode;          /* where the partial states are merged: 0 (default) = the planner's
                                   choice by cost; 1 = a separate merge launch (as always with
                                   separate_phases); 2 = inside the attention launch, by the work item
-                                  that completes each row block (one launch per step). All merge in
-                                  the same order: same bits */
+                                  that completes each row block (one launch per step; plans with
+                                  nested levels merge separately). All merge in the same order:
+                                  same bits */
   int32_t use_tuned;           /* 0 (default) = AUTO is a pure function of the batch and these
                                   params; 1 = an AUTO plan whose batch shape has a choice recorded
                                   by cascade_attn_autotune / cascade_attn_autotune_record takes
@@ -150,8 +152,8 @@ typedef struct {
   int32_t merge_in_launch;             /* 1 if the partial states are merged inside the attention launch */
   int32_t suffix_heads_per_item;       /* consecutive KV heads one suffix (or only) work item runs */
   int32_t separate_phases;             /* 1 if the cascade phases run as separate launches */
-  int32_t num_level1_groups;           /* request groups of the second shared level (0 = none) */
-  int32_t level1_splits;               /* KV splits of every group (partial slots of that level) */
+  int32_t num_level1_groups;           /* request groups of the nested shared levels (0 = none) */
+  int32_t level1_splits;               /* KV splits of every group of the first nested level */
   int32_t kv_dtype;                    /* ca_kv_dtype_t of the plan */
   int32_t sliding_window;              /* window applied by the plan (0: none, or it never binds) */
   int32_t suffix_longest_first;        /* 1 if per-request items start longest key range first */
@@ -162,7 +164,8 @@ typedef struct {
   float est_us_cascade;                /* cost-model estimates used by AUTO */
   float est_us_noncascade;
   int32_t partials_fp32;               /* 1 if partial outputs are fp32, 0 if bf16 */
-  int32_t reserved1;
+  int32_t shared_levels;               /* shared levels the cascade path runs (1 = the batch-wide
+                                          prefix only; 0 = non-cascade) */
 } ca_plan_info_t;
 
 typedef struct ca_plan* ca_plan_t;
@@ -216,24 +219,31 @@ ca_status_t cascade_attn_plan(const ca_params_t* params, const int32_t* block_ta
 ca_status_t cascade_attn_plan_info(ca_plan_t plan, ca_plan_info_t* out);
 
 /*
- * Second shared level of the plan. FlashInfer's cascade takes any number of
+ * Nested shared levels of the plan. FlashInfer's cascade takes any number of
  * levels ([p2] section 7) and the workloads of [p2] section 3 nest (system
- * prompt -> document -> request). When the cascade path is taken and
- * params->max_levels != 1, the planner looks for groups: maximal runs of
- * consecutive requests in which every adjacent pair shares more leading
- * pages than the batch-wide prefix. A group's shared length is the pages
- * all its members share, capped at their smallest num_computed_tokens and
- * floored to a page (the batch-wide rule of section 8 Step 2); it is used if
- * the group has >= 2 requests and shares >= 256 tokens more than the
- * batch-wide prefix. At most 64 groups (those that save the most KV reads).
- * The group's queries, packed, attend non-causally once to its extra
- * positions [common_prefix_len, shared_len); its members' suffixes start at
- * shared_len. Writes min(n, capacity) triples (first request, end request
- * (exclusive), shared_len) to groups_out [capacity][3] and n to *n_out.
- * Errors: CA_EINVAL (null plan / n_out, capacity < 0, null groups_out with
- * capacity > 0).
+ * prompt -> document -> chapter -> request). When the cascade path is taken
+ * and params->max_levels != 1, the planner applies the batch-wide rule of
+ * [p2] section 8 Steps 1-2 (leading pages shared by the members, capped at
+ * their smallest num_computed_tokens, floored to a page) at every node of
+ * the prefix tree of the requests' page-id sequences: members that share
+ * every page up to some column are split by their page at that column; a
+ * part of >= 2 requests whose shared length exceeds the enclosing level's by
+ * >= 256 tokens (the pages' prefix-length gate, [p2] section 3) becomes a
+ * group one level deeper. Members need not be consecutive in the batch.
+ * Levels below the prefix: at most max_levels - 1 (default 3); groups: at
+ * most 64, kept level by level by the KV reads they save; batches of more
+ * than 512 requests get none. A group's queries, packed, attend non-causally
+ * once to its positions [key_begin, key_end) (key_begin: the enclosing
+ * level's shared length); each request's own phase starts at the key_end of
+ * its innermost group. Writes min(n, capacity) rows (level >= 1, parent
+ * group index or -1 for the batch-wide prefix, key_begin, key_end) to
+ * groups_out [capacity][4], parents before children; if deepest_out is not
+ * NULL, each request's innermost group (or -1) to deepest_out [num_reqs];
+ * and n to *n_out. Errors: CA_EINVAL (null plan / n_out, capacity < 0, null
+ * groups_out with capacity > 0).
  */
-ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* groups_out, int32_t* n_out);
+ca_status_t cascade_attn_plan_groups(ca_plan_t plan, int32_t capacity, int32_t* groups_out, int32_t* deepest_out,
+                                     int32_t* n_out);
 
 /*
  * Runs one attention step of the plan on `stream` (a hipStream_t; NULL =

@@ -89,7 +89,7 @@ class ca_plan_info_t(ctypes.Structure):
         ("est_us_cascade", ctypes.c_float),
         ("est_us_noncascade", ctypes.c_float),
         ("partials_fp32", ctypes.c_int32),
-        ("reserved1", ctypes.c_int32),
+        ("shared_levels", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -121,7 +121,7 @@ def load() -> ctypes.CDLL:
     lib.cascade_attn_run_noalloc.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p] * 3 + \
         [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.cascade_attn_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-    lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p]
+    lib.cascade_attn_plan_groups.argtypes = [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p, _i32p]
     lib.cascade_attn_autotune.argtypes = [ctypes.POINTER(ca_params_t), _i32p, _i32p, _i32p, _i32p] + \
         [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
                                   ctypes.POINTER(ctypes.c_float)]
@@ -178,8 +178,9 @@ def cascade_attn_num_common_prefix_blocks(block_table, seq_lens, page_size: int)
 class Plan:
     """Owns a ``ca_plan_t`` handle; ``info`` holds ``cascade_attn_plan_info``."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, num_reqs: int):
         self._h = ctypes.c_void_p(handle)
+        self.num_reqs = int(num_reqs)
         info = ca_plan_info_t()
         _check(load().cascade_attn_plan_info(self._h, ctypes.byref(info)))
         self.info = info.as_dict()
@@ -262,7 +263,7 @@ def cascade_attn_plan(**kw) -> Plan:
     h = ctypes.c_void_p(0)
     _check(load().cascade_attn_plan(ctypes.byref(prm), *ptrs, ctypes.byref(h)))
     del keep
-    return Plan(h.value)
+    return Plan(h.value, prm.num_reqs)
 
 
 def cascade_attn_autotune(q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d, out, lse_out,
@@ -285,7 +286,7 @@ def cascade_attn_autotune(q, k_cache, v_cache, block_table_d, query_start_loc_d,
         workspace.data_ptr() if workspace is not None else None, ws_bytes, s, int(iters), ctypes.byref(h),
         ctypes.byref(us)))
     del keep
-    return Plan(h.value), float(us.value)
+    return Plan(h.value, prm.num_reqs), float(us.value)
 
 
 def cascade_attn_autotune_record(mode="on", prefix_splits: int = 0, heads_per_item: int = 0, max_levels: int = 0,
@@ -308,13 +309,16 @@ def cascade_attn_plan_info(plan: Plan) -> dict:
 
 
 def cascade_attn_plan_groups(plan: Plan):
-    """Second shared level of the plan: [(first request, end request, shared_len)]."""
+    """Nested shared levels of the plan: ([(level, parent, key_begin, key_end)]
+    parents first, [innermost group of each request or -1])."""
     n = ctypes.c_int32(0)
-    _check(load().cascade_attn_plan_groups(plan.handle, 0, None, ctypes.byref(n)))
+    _check(load().cascade_attn_plan_groups(plan.handle, 0, None, None, ctypes.byref(n)))
     cap = int(n.value)
-    buf = (ctypes.c_int32 * max(1, 3 * cap))()
-    _check(load().cascade_attn_plan_groups(plan.handle, cap, buf, ctypes.byref(n)))
-    return [(buf[3 * j], buf[3 * j + 1], buf[3 * j + 2]) for j in range(cap)]
+    buf = (ctypes.c_int32 * max(1, 4 * cap))()
+    deepest = (ctypes.c_int32 * max(1, plan.num_reqs))()
+    _check(load().cascade_attn_plan_groups(plan.handle, cap, buf, deepest, ctypes.byref(n)))
+    groups = [tuple(buf[4 * j + i] for i in range(4)) for j in range(cap)]
+    return groups, [deepest[r] for r in range(plan.num_reqs)]
 
 
 def cascade_attn_run(plan: Plan, q, k_cache, v_cache, block_table_d, query_start_loc_d, seq_lens_d,

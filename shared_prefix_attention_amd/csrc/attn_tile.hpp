@@ -67,7 +67,7 @@ struct TileArgs {
   int32_t bt_stride;
   int32_t hq, hkv, group;
   float scale_log2;             // softmax_scale * log2(e)
-  int32_t prefix_mode;          // 1: prefix phase, 2: group level, 0: per-request phase
+  int32_t prefix_mode;          // 1: prefix phase, 2: nested group levels, 0: per-request phase
   int32_t total_rows;           // prefix: T * group
   int32_t key_start;            // per-request phase: first KV position
   int32_t prefix_len;           // prefix phase: number of shared KV positions
@@ -85,8 +85,6 @@ struct TileArgs {
   uint16_t* out;                // [T][hq][D] bf16 (direct / merge mode)
   float* lse_out;               // [T][hq] (may be null)
   int32_t direct;               // write the final output (no partial)
-  int32_t lvl1_slot_base;       // per-request phase: first partial slot of the group level
-  int32_t lvl1_slots;           //   and its slot count (rows of requests in no group get -inf there)
   float v_scale;                // dequantisation factor of V (1 for bf16 caches)
   int32_t window;               // per-request phase: sliding window W (> 0: keys p - W < t <= p)
   const float* sinks;           // [hq] attention-sink logits (natural log) or null; direct mode only
@@ -114,8 +112,7 @@ struct MergeTailArgs {
   int32_t merge_slots;          // partial states per row
   int32_t hq, hkv, group, num_reqs;
   int32_t m_pre_splits;         // prefix items per prefix row tile (0: no prefix phase)
-  int32_t m_pre_rows;           // rows per prefix / group-level tile
-  int32_t m_lvl_splits;         // group-level items per group row tile (0: none)
+  int32_t m_pre_rows;           // rows per prefix tile
   int32_t m_suf_splits;         // per-request items per (request, row tile, KV head)
   int32_t m_suf_rows;           // rows per per-request tile
   int32_t m_suf_mtiles;         // per-request row tiles of the longest query (counter stride)
@@ -130,31 +127,57 @@ struct ItemEnd {
   int32_t wrote, mode, req, grp, row_begin, row_end, g0, H;
 };
 
-// Second shared level: request groups [req_begin, req_end) whose members
-// share KV positions [key_start, key_end) beyond the batch-wide prefix. Group
-// j's work items are [item_begin[j], item_begin[j + 1]) of the group-level
-// launch, (row tile, KV head, split) with `splits` splits of split_tokens
-// keys. Passed by value (kernel arguments), so the plan needs no device copy.
+// Nested shared levels: groups of requests that share KV positions
+// [key_begin, key_end) beyond the level that encloses them (the batch-wide
+// prefix, or another group). Members are any requests: in the tree order
+// (requests sorted so that every group's members are adjacent) group j holds
+// positions [pos_begin[j], pos_end[j]). Its packed query rows are its
+// members' tokens in that order, times the query heads of a KV head; pos_tok
+// and pos_cum give the first token of the request at each position and the
+// tokens before it. Group j's work items are [item_begin[j], item_begin[j +
+// 1]) of the group-level launch, (row tile, KV head, split) with its level's
+// split count; the levels' partial slots follow one another. Passed by value
+// (kernel arguments), so the plan needs no device copy.
 constexpr int kMaxGroups = 64;
+constexpr int kMaxLevels = 4;              // shared levels, the batch-wide prefix included
+constexpr int kMaxTreeOrder = 512;
 struct GroupTable {
-  int32_t n;                            // groups (0: one shared level)
+  int32_t n;                               // groups (0: one shared level)
+  int32_t levels;                          // shared levels in use
+  int32_t level_splits[kMaxLevels];        // [l]: KV splits of every group of level l >= 1
+  int32_t level_slot_base[kMaxLevels];     // [l]: first partial slot of level l
+  int32_t uniform_q;                       // > 0: every request has this many query tokens
   int32_t item_begin[kMaxGroups + 1];
-  int32_t req_begin[kMaxGroups];        // ascending, ranges disjoint
-  int32_t req_end[kMaxGroups];
-  int32_t key_end[kMaxGroups];          // shared positions end (page multiple)
-  int32_t split_tokens[kMaxGroups];     // multiple of 64
+  int32_t level[kMaxGroups];
+  int32_t first_req[kMaxGroups];           // a member: its block-table row holds the shared pages
+  int32_t pos_begin[kMaxGroups];
+  int32_t pos_end[kMaxGroups];
+  int32_t key_begin[kMaxGroups];
+  int32_t key_end[kMaxGroups];
+  int32_t split_tokens[kMaxGroups];        // multiple of 64
+  int32_t rows[kMaxGroups];                // packed query rows of the group
+  int32_t pos_tok[kMaxTreeOrder];
+  int32_t pos_cum[kMaxTreeOrder + 1];
+  uint8_t deepest[kMaxTreeOrder];          // [request]: innermost group, 0xff: none
 };
 
-// Group holding request `req` (or -1): the last group starting at or before
-// it, if it also ends after it. Uniform arguments: scalar binary search.
-__device__ __forceinline__ int group_of_request(const GroupTable& gt, int req) {
-  int lo = 0, hi = gt.n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (gt.req_begin[mid] <= req) lo = mid + 1;
-    else hi = mid;
+// Query token of group-local token t of group j (its members' tokens in tree
+// order): the position p holding it, then the token within p's request.
+__device__ __forceinline__ int group_token(const GroupTable& gt, int j, int t) {
+  const int tg = gt.pos_cum[gt.pos_begin[j]] + t;
+  int p;
+  if (gt.uniform_q > 0) {
+    p = gt.pos_begin[j] + t / gt.uniform_q;
+  } else {   // the last position in [pos_begin, pos_end) with pos_cum <= tg
+    int lo = gt.pos_begin[j], hi = gt.pos_end[j] - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gt.pos_cum[mid] <= tg) lo = mid;
+      else hi = mid - 1;
+    }
+    p = lo;
   }
-  return (lo > 0 && req < gt.req_end[lo - 1]) ? lo - 1 : -1;
+  return gt.pos_tok[p] + (tg - gt.pos_cum[p]);
 }
 
 // Dispatch order of the per-request work items: request slot j runs request
@@ -338,26 +361,16 @@ __device__ __forceinline__ void req_tokens(const MergeTailArgs& a, int r, int& q
 }
 
 // Items that write partial states of unit (r, m): the prefix tiles that
-// overlap its rows (times the prefix splits), likewise the group-level tiles
-// of r's group, and its own per-request items (one per KV chunk). q0 / q1:
-// r's token range.
-__device__ __forceinline__ int unit_item_count(const MergeTailArgs& a, const GroupTable& gt, int r, int m, int q0,
-                                               int q1) {
+// overlap its rows (times the prefix splits) and its own per-request items
+// (one per KV chunk). Plans with nested shared levels merge in a launch of
+// their own. q0 / q1: r's token range.
+__device__ __forceinline__ int unit_item_count(const MergeTailArgs& a, int m, int q0, int q1) {
   const int rows_r = (q1 - q0) * a.group;
   const int lo = m * a.m_suf_rows, hi = min(lo + a.m_suf_rows, rows_r);   // request-local rows
   int e = a.m_suf_splits;
   if (a.m_pre_splits > 0) {
     const int base = q0 * a.group;   // packed row of the request's first row
     e += a.m_pre_splits * ((base + hi - 1) / a.m_pre_rows - (base + lo) / a.m_pre_rows + 1);
-  }
-  if (a.m_lvl_splits > 0 && gt.n > 0) {
-    const int j = group_of_request(gt, r);
-    if (j >= 0) {
-      int g0, g1;
-      req_tokens(a, gt.req_begin[j], g0, g1);
-      const int gb = (q0 - g0) * a.group;   // row offset inside the group
-      e += a.m_lvl_splits * ((gb + hi - 1) / a.m_pre_rows - (gb + lo) / a.m_pre_rows + 1);
-    }
   }
   return e;
 }
@@ -369,10 +382,10 @@ constexpr int kTailEntryInts = 4;
 
 // Wave 0, one lane: counts this item's arrival at unit (r, m, g) and, if it
 // completes the unit, appends the unit to the work-group's list.
-__device__ __forceinline__ void arrive(const MergeTailArgs& a, const GroupTable& gt, int r, int m, int g, int q0,
-                                       int q1, int32_t* s_list) {
+__device__ __forceinline__ void arrive(const MergeTailArgs& a, int r, int m, int g, int q0, int q1,
+                                       int32_t* s_list) {
   const int u = (r * a.m_suf_mtiles + m) * a.hkv + g;
-  const int expect = unit_item_count(a, gt, r, m, q0, q1);
+  const int expect = unit_item_count(a, m, q0, q1);
   const int old = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (old + 1 == expect) {
     const int k = __hip_atomic_fetch_add(s_list, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -415,8 +428,7 @@ __device__ __forceinline__ int request_of_token(const MergeTailArgs& a, int r_lo
 // The counters go back to 0 for the next launch.
 // s_list: LDS the item no longer uses (its stage buffers), >= 4 KB.
 template <int D, int NT>
-__device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const GroupTable& gt, const ItemEnd& e,
-                                           int32_t* s_list) {
+__device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const ItemEnd& e, int32_t* s_list) {
   if (!e.wrote) return;
   const int tid = threadIdx.x;
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): this thread's stores are done
@@ -429,18 +441,10 @@ __device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const GroupTa
       const int m = e.row_begin / RS;
       int q0, q1;
       req_tokens(a, e.req, q0, q1);
-      for (int h = tid; h < e.H; h += 64) arrive(a, gt, e.req, m, e.g0 + h, q0, q1, s_list);
+      for (int h = tid; h < e.H; h += 64) arrive(a, e.req, m, e.g0 + h, q0, q1, s_list);
     } else {
       // packed rows [p_lo, p_hi) and the requests they may belong to
-      int p_lo = e.row_begin, p_hi = e.row_end, r_lo = 0, r_end = a.num_reqs;
-      if (e.mode == 2) {
-        int g0, g1;
-        req_tokens(a, gt.req_begin[e.grp], g0, g1);
-        p_lo += g0 * G;
-        p_hi += g0 * G;
-        r_lo = gt.req_begin[e.grp];
-        r_end = gt.req_end[e.grp];
-      }
+      const int p_lo = e.row_begin, p_hi = e.row_end, r_lo = 0, r_end = a.num_reqs;
       const int tok_lo = p_lo / G, tok_hi = (p_hi - 1) / G;
       const int first = request_of_token(a, r_lo, r_end, tok_lo);
       for (int r = first + tid; r < r_end; r += 64) {
@@ -450,7 +454,7 @@ __device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const GroupTa
         const int base = q0 * G, rows_r = (q1 - q0) * G;
         const int l0 = max(p_lo, base) - base, l1 = min(p_hi, base + rows_r) - base;
         if (l0 >= l1) continue;
-        for (int m = l0 / RS; m <= (l1 - 1) / RS; ++m) arrive(a, gt, r, m, e.g0, q0, q1, s_list);
+        for (int m = l0 / RS; m <= (l1 - 1) / RS; ++m) arrive(a, r, m, e.g0, q0, q1, s_list);
       }
     }
   }
@@ -495,10 +499,12 @@ __device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const GroupTa
 // pages and key range), run as one continuous stage pipeline.
 // WIN: the item may apply a sliding window and attention sinks (the
 // stand-alone kernel; the cascade launch has neither).
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN>
+// PM: the role (prefix_mode) when fixed at compile time, -1: a.prefix_mode.
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN, int PM = -1>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const ReqOrder& ro, const int bid,
                                           uint8_t* smem, ItemEnd& end) {
   end.wrote = 0;
+  const int pmode = PM >= 0 ? PM : a.prefix_mode;
   constexpr int W = RW * KG;              // waves per work-group
   constexpr int NT = 64 * W;              // threads
   constexpr int ROWS = 16 * RB * RW;      // query rows per work-group
@@ -552,10 +558,11 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   int win_lo_max = 0x80000000;          // window start of the item's last row (no window: none)
   int page_skip = 0;                    // pages of the item skipped below a sliding window
   const int H = MH ? a.heads_per_item : 1;   // KV heads g0 .. g0 + H - 1, one after another
-  if (a.prefix_mode) {
-    int local = bid;
-    if (a.prefix_mode == 2) {
-      // group level: find the group whose items contain bid
+  if (pmode) {
+    int local = bid, splits = a.splits;
+    key_begin = a.key_start;
+    if (pmode == 2) {
+      // nested level: find the group whose items contain bid
       int lo = 0, hi = gt.n - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -565,14 +572,16 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       grp = lo;
       local = bid - gt.item_begin[grp];
       split_tokens = gt.split_tokens[grp];
-      req = gt.req_begin[grp];
+      splits = gt.level_splits[gt.level[grp]];
+      req = gt.first_req[grp];
+      key_begin = gt.key_begin[grp];
     }
-    const int kv_items = a.hkv * a.splits;
+    const int kv_items = a.hkv * splits;
     mt = local / kv_items;
     const int kvi = local - mt * kv_items;
-    g0 = kvi / a.splits;
-    c = kvi - g0 * a.splits;
-    key_begin = a.key_start + c * split_tokens;
+    g0 = kvi / splits;
+    c = kvi - g0 * splits;
+    key_begin += c * split_tokens;
     causal = false;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
   } else {
@@ -583,8 +592,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     const int groups = a.hkv / H;
     g0 = (rest % groups) * H;
     req = ro.n > 0 ? ro.req[rest / groups] : rest / groups;
-    // a request in a group starts after the group's shared positions
-    grp = gt.n > 0 ? group_of_request(gt, req) : -1;
+    // a request in a group starts after its innermost group's shared positions
+    grp = (gt.n > 0 && gt.deepest[req] != 0xff) ? gt.deepest[req] : -1;
     key_begin = (grp >= 0 ? gt.key_end[grp] : a.key_start) + c * split_tokens;
     causal = true;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
@@ -599,16 +608,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     pg_reg[k] = i < item_pages ? bt_row[min(first_page + i, a.bt_stride - 1)] : 0;
   }
   row_begin = mt * ROWS;
-  slot = a.slot_base + c;
-  if (a.prefix_mode == 1) {
+  slot = (pmode == 2 ? gt.level_slot_base[gt.level[grp]] : a.slot_base) + c;
+  if (pmode == 1) {
     row_end = min(row_begin + ROWS, a.total_rows);
     key_end = min(key_begin + split_tokens, a.prefix_len);
-  } else if (a.prefix_mode == 2) {
-    const int q0 = a.qsl[req];
-    row_end = min(row_begin + ROWS, (a.qsl[gt.req_end[grp]] - q0) * a.group);
+  } else if (pmode == 2) {
+    row_end = min(row_begin + ROWS, gt.rows[grp]);
     if (row_begin >= row_end) return;   // uniform across the work-group
     key_end = max(key_begin, min(key_begin + split_tokens, gt.key_end[grp]));
-    tok_base = q0;
   } else {
     const int q0 = a.qsl[req];
     const int q_len = a.qsl[req + 1] - q0;
@@ -627,17 +634,22 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
       key_begin += skip * SK;
       page_skip = skip * SK / 16;
     }
-    // rows of a request in no group have no group-level state: mark those
-    // partial slots empty (weight 0 in the merge)
-    if (grp < 0 && c == 0 && a.lvl1_slots > 0) {
+    // levels deeper than the request's innermost group hold no state for
+    // its rows: mark those partial slots (contiguous, the last levels')
+    // empty, weight 0 in the merge
+    const int lv = grp >= 0 ? gt.level[grp] + 1 : 1;
+    const int e_lo = lv < gt.levels ? gt.level_slot_base[lv] : 0;
+    const int n_empty =
+        lv < gt.levels ? gt.level_slot_base[gt.levels - 1] + gt.level_splits[gt.levels - 1] - e_lo : 0;
+    if (c == 0 && n_empty > 0) {
       const int nrows = row_end - row_begin;
-      for (int e = tid; e < nrows * H * a.lvl1_slots; e += NT) {
+      for (int e = tid; e < nrows * H * n_empty; e += NT) {
         const int s = e / (nrows * H);
         const int rh = e - s * (nrows * H);
         const int hh = rh / nrows;
         const int m = row_begin + (rh - hh * nrows);
         const int64_t row = (int64_t)(tok_base + m / a.group) * a.hq + (g0 + hh) * a.group + m % a.group;
-        float* lp = a.part_lse + (int64_t)(a.lvl1_slot_base + s) * a.slot_rows + row;
+        float* lp = a.part_lse + (int64_t)(e_lo + s) * a.slot_rows + row;
         if (a.coherent) store_dev_f32(lp, -INFINITY);
         else *lp = -INFINITY;
       }
@@ -667,7 +679,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     row_ok[rb] = m < row_end;
     const int t_in = m / a.group;
     row_j[rb] = m - t_in * a.group;
-    row_tok[rb] = tok_base + t_in;
+    // nested level: packed rows are the group members' tokens in tree order
+    row_tok[rb] = pmode == 2 ? (row_ok[rb] ? group_token(gt, grp, t_in) : 0) : tok_base + t_in;
     row_qpos[rb] = q_pos_base + t_in;
   }
   auto load_q = [&](int g, u32x4_t (&q)[RB][KC]) {
@@ -958,7 +971,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
 
   // An empty KV range (a chunk past a short request's end) still writes its
   // rows: o = 0, lse = -inf, which the merge ignores.
-  end = ItemEnd{1, a.prefix_mode, req, grp, row_begin, row_end, g0, H};
+  end = ItemEnd{1, pmode, req, grp, row_begin, row_end, g0, H};
   if (U == 0) {
     for (int hh = 0; hh < H; ++hh) finish_head(g0 + hh, 0);
     return;
@@ -1217,12 +1230,12 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
   ItemEnd end;
   attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, ro, blockIdx.x, smem, end);
-  if (mt.counters) merge_tail<D, 64 * RW * KG>(mt, gt, end, reinterpret_cast<int32_t*>(smem));
+  if (mt.counters) merge_tail<D, 64 * RW * KG>(mt, end, reinterpret_cast<int32_t*>(smem));
 }
 
 // One launch for all cascade phases: work-groups [0, n_prefix) run prefix
-// items, the next n_group run group-level items (same shape as the prefix),
-// the rest run suffix items, so the MFMA-heavy shared levels and the
+// items, the next n_group run nested-level items (same shape as the
+// prefix), the rest run suffix items, so the MFMA-heavy shared levels and the
 // bandwidth-heavy suffix share the CUs. All write partial states. Each role
 // has its own pipeline shape (stages x keys per stage) inside one LDS
 // allocation, sized so that two work-groups fit on a CU.
@@ -1237,13 +1250,13 @@ __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PB > SB ? PB : SB];
   const int bid = blockIdx.x;
   ItemEnd end;
-  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(pa, gt, ro, bid, smem, end);
+  if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false, 1>(pa, gt, ro, bid, smem, end);
   else if (bid < n_prefix + n_group)
-    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false>(ga, gt, ro, bid - n_prefix, smem, end);
+    attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false, 2>(ga, gt, ro, bid - n_prefix, smem, end);
   else
-    attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false>(sa, gt, ro, bid - n_prefix - n_group, smem,
-                                                                          end);
-  if (mt.counters) merge_tail<D, 256>(mt, gt, end, reinterpret_cast<int32_t*>(smem));
+    attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false, 0>(sa, gt, ro, bid - n_prefix - n_group,
+                                                                             smem, end);
+  if (mt.counters) merge_tail<D, 256>(mt, end, reinterpret_cast<int32_t*>(smem));
 }
 
 }  // namespace ca

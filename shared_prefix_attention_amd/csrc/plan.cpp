@@ -308,54 +308,93 @@ static double suffix_padded_flops(const ca_plan& pl, const int32_t* qsl, const i
   return f * 4.0 * pl.d * pl.hkv;
 }
 
-// Second shared level. FlashInfer's cascade runs any number of levels
+// Nested shared levels. FlashInfer's cascade runs any number of levels
 // ([p2] section 7), and the workloads of [p2] section 3 nest: a system
-// prompt shared by every request, then a document or prompt shared by some,
-// then each request's own tokens. A candidate group is a maximal run of
-// consecutive requests in which every adjacent pair shares more leading
-// pages than the batch-wide prefix (equality of page ids is transitive, so
-// the run's members share exactly the minimum of those adjacent counts). Its
-// shared length follows the batch-wide rule ([p2] section 8 Step 2): capped
-// at the members' smallest num_computed, floored to a page. A group is kept
-// when it has >= 2 requests and shares >= 256 tokens beyond the batch-wide
-// prefix (the pages' prefix-length gate, [p2] section 3).
-struct GroupCand {
-  int32_t a, b, len;
-  int64_t saving;   // KV positions not re-read: (members - 1) * extra length
+// prompt shared by every request, then a document shared by some, a chapter
+// by fewer, then each request's own tokens. The batch-wide rule of [p2]
+// section 8 Steps 1-2 (shared leading pages, capped at the members' smallest
+// num_computed, floored to a page) is applied at every node of the prefix
+// tree of the requests' page-id sequences: members that share every page up
+// to column c are split by their page at column c; a part of >= 2 requests
+// whose shared length exceeds its enclosing group's by >= 256 tokens (the
+// pages' prefix-length gate, [p2] section 3) is a group one level deeper,
+// and its parts are examined against it; otherwise its parts are examined
+// against the same enclosing group. Members need not be consecutive.
+struct TreeCand {
+  std::vector<int32_t> members;   // batch order
+  int32_t parent_len, len, level, parent;
+  int64_t saving() const { return (int64_t)(members.size() - 1) * (len - parent_len); }
 };
 
-static std::vector<GroupCand> find_level1_groups(const int32_t* bt, int32_t n, int32_t stride,
-                                                 const int32_t* seq_lens, const int32_t* qsl, int32_t ps,
-                                                 int32_t common_blocks, int64_t plen) {
-  std::vector<GroupCand> out;
-  const int64_t j0 = plen / ps;
-  // pages shared by requests r and r + 1 (columns below common_blocks are
-  // shared by every request and inside every request's pages)
-  std::vector<int64_t> lcp(n > 1 ? n - 1 : 0);
-  for (int32_t r = 0; r + 1 < n; ++r) {
-    const int64_t lim = std::min(cdiv(seq_lens[r], ps), cdiv(seq_lens[r + 1], ps));
-    const int32_t* x = bt + (int64_t)r * stride;
-    const int32_t* y = x + stride;
-    int64_t j = std::min<int64_t>(common_blocks, lim);
-    while (j < lim && x[j] == y[j]) ++j;
-    lcp[r] = j;
+static int64_t shared_columns(const int32_t* bt, int32_t stride, const int32_t* seq_lens, int32_t ps,
+                              const std::vector<int32_t>& members) {
+  int64_t limit = stride;
+  for (int32_t r : members) limit = std::min<int64_t>(limit, cdiv(seq_lens[r], ps));
+  const int32_t* first = bt + (int64_t)members[0] * stride;
+  int64_t c = 0;
+  for (; c < limit; ++c) {
+    bool same = true;
+    for (size_t k = 1; k < members.size() && same; ++k) same = bt[(int64_t)members[k] * stride + c] == first[c];
+    if (!same) break;
   }
-  for (int32_t a = 0; a < n;) {
-    int32_t b = a + 1;
-    int64_t shared = INT64_MAX;
-    while (b < n && lcp[b - 1] > j0) shared = std::min(shared, lcp[b++ - 1]);
-    if (b - a >= 2) {
-      int64_t len = shared * ps;
-      for (int32_t r = a; r < b; ++r) len = std::min<int64_t>(len, seq_lens[r] - (qsl[r + 1] - qsl[r]));
-      len = len / ps * ps;
-      if (len - plen >= 256) out.push_back({a, b, (int32_t)len, (int64_t)(b - a - 1) * (len - plen)});
+  return c;
+}
+
+static void tree_visit(const int32_t* bt, int32_t stride, const int32_t* seq_lens, const int32_t* qsl, int32_t ps,
+                       const std::vector<int32_t>& members, int32_t parent_len, int32_t level, int32_t parent,
+                       int32_t max_levels, std::vector<TreeCand>& out) {
+  const int64_t c = shared_columns(bt, stride, seq_lens, ps, members);
+  // parts by the page at column c, in order of first appearance
+  std::vector<std::pair<int32_t, std::vector<int32_t>>> parts;
+  for (int32_t r : members) {
+    if (cdiv(seq_lens[r], ps) <= c) continue;
+    const int32_t page = bt[(int64_t)r * stride + c];
+    auto it = std::find_if(parts.begin(), parts.end(), [&](const auto& x) { return x.first == page; });
+    if (it == parts.end()) parts.push_back({page, {r}});
+    else it->second.push_back(r);
+  }
+  for (const auto& part : parts) {
+    const std::vector<int32_t>& m = part.second;
+    if (m.size() < 2) continue;
+    int64_t len = shared_columns(bt, stride, seq_lens, ps, m) * ps;
+    for (int32_t r : m) len = std::min<int64_t>(len, seq_lens[r] - (qsl[r + 1] - qsl[r]));
+    len = len / ps * ps;
+    if (len - parent_len >= 256 && level + 1 <= max_levels - 1) {
+      out.push_back({m, parent_len, (int32_t)len, level + 1, parent});
+      tree_visit(bt, stride, seq_lens, qsl, ps, m, (int32_t)len, level + 1, (int32_t)out.size() - 1, max_levels, out);
+    } else {
+      tree_visit(bt, stride, seq_lens, qsl, ps, m, parent_len, level, parent, max_levels, out);
     }
-    a = b;
   }
-  if ((int)out.size() > kMaxLevel1Groups) {   // keep the groups that save the most
-    std::stable_sort(out.begin(), out.end(), [](const GroupCand& x, const GroupCand& y) { return x.saving > y.saving; });
-    out.resize(kMaxLevel1Groups);
-    std::sort(out.begin(), out.end(), [](const GroupCand& x, const GroupCand& y) { return x.a < y.a; });
+}
+
+// At most kMaxTreeGroups groups: level by level, the groups that save the
+// most KV reads ((members - 1) x extra length) among those whose enclosing
+// group was kept. A dropped group's members fall back to the nearest kept
+// enclosing level (results are exact either way).
+static std::vector<TreeCand> limit_tree(std::vector<TreeCand> all) {
+  if ((int)all.size() <= kMaxTreeGroups) return all;
+  std::vector<int32_t> keep_idx;
+  std::vector<char> kept(all.size(), 0);
+  for (int32_t lev = 1; lev < kMaxShared && (int)keep_idx.size() < kMaxTreeGroups; ++lev) {
+    std::vector<int32_t> cand;
+    for (int32_t g = 0; g < (int32_t)all.size(); ++g)
+      if (all[g].level == lev && (all[g].parent < 0 || kept[all[g].parent])) cand.push_back(g);
+    std::stable_sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) { return all[a].saving() > all[b].saving(); });
+    for (int32_t g : cand) {
+      if ((int)keep_idx.size() >= kMaxTreeGroups) break;
+      kept[g] = 1;
+      keep_idx.push_back(g);
+    }
+  }
+  std::sort(keep_idx.begin(), keep_idx.end());   // parents before children, as found
+  std::vector<int32_t> remap(all.size(), -1);
+  std::vector<TreeCand> out;
+  for (int32_t g : keep_idx) {
+    remap[g] = (int32_t)out.size();
+    TreeCand t = all[g];
+    t.parent = t.parent >= 0 ? remap[t.parent] : -1;
+    out.push_back(t);
   }
   return out;
 }
@@ -438,7 +477,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   if (p.heads_per_item < 0 || (p.heads_per_item > 0 && p.num_kv_heads % p.heads_per_item != 0))
     return fail(CA_EINVAL, "heads_per_item must be 0 or divide num_kv_heads");
   if (p.separate_phases != 0 && p.separate_phases != 1) return fail(CA_EINVAL, "separate_phases must be 0 or 1");
-  if (p.max_levels < 0 || p.max_levels > 2) return fail(CA_EINVAL, "max_levels must be 0, 1 or 2");
+  if (p.max_levels < 0 || p.max_levels > kMaxShared) return fail(CA_EINVAL, "max_levels must be in [0, 4]");
   if (p.kv_dtype != CA_KV_BF16 && p.kv_dtype != CA_KV_FP8_E4M3) return fail(CA_EINVAL, "unknown kv_dtype");
   if (p.sliding_window < 0) return fail(CA_EINVAL, "sliding_window must be >= 0");
   if (p.prefix_splits < 0) return fail(CA_EINVAL, "prefix_splits must be >= 0");
@@ -581,7 +620,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   // batch-wide prefix, the group level when there is one, each request's
   // remaining positions, and the merge.
   PhaseTile pre, suf;
-  Level1 lvl1;
+  Tree tree;
   bool casc_in_launch = false;
   std::vector<int64_t> kstart(n, plen);   // first suffix position of each request
   int64_t group_items = 0, group_stages = 0;
@@ -596,39 +635,100 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
       pre.splits = (int32_t)cdiv(ntiles, tiles_per);
       pre.split_tokens = (int32_t)(tiles_per * kTileKeys);
     }
-    std::vector<GroupCand> groups;
-    groups = find_level1_groups(bt, n, stride, seq_lens, qsl, ps, pl->common_blocks, plen);
+    // nested levels: the prefix tree below the batch-wide prefix (requests
+    // of a batch larger than the tree-order table run without them)
+    const int32_t max_levels = p.max_levels == 0 ? kMaxShared : p.max_levels;
+    std::vector<TreeCand> groups;
+    if (n <= kOrderCapacity) {
+      std::vector<int32_t> all(n);
+      for (int32_t r = 0; r < n; ++r) all[r] = r;
+      tree_visit(bt, stride, seq_lens, qsl, ps, all, (int32_t)plen, 0, -1, kMaxShared, groups);
+    }
     pl->cand_groups = (int32_t)groups.size();   // part of the shape, whether used or not
-    if (p.max_levels == 1) groups.clear();
+    if (max_levels < kMaxShared) {   // keep the shallower levels (children follow their parents)
+      std::vector<TreeCand> kept;
+      std::vector<int32_t> remap(groups.size(), -1);
+      for (size_t g = 0; g < groups.size(); ++g) {
+        if (groups[g].level > max_levels - 1) continue;
+        remap[g] = (int32_t)kept.size();
+        kept.push_back(groups[g]);
+        kept.back().parent = groups[g].parent >= 0 ? remap[groups[g].parent] : -1;
+      }
+      groups.swap(kept);
+    }
+    groups = limit_tree(std::move(groups));
     double t_grp = 0.0;
     int64_t group_tokens = 0;
     if (!groups.empty()) {
-      // Every group gets the same number of KV splits (so a group's rows
-      // fill the same partial slots): about 512 keys per item for the
-      // longest group, at most 8 splits unless the per-item cap needs more.
-      lvl1.n = (int32_t)groups.size();
-      int64_t max_tiles = 1;
-      for (const auto& g : groups) max_tiles = std::max(max_tiles, cdiv(g.len - plen, kTileKeys));
-      const int64_t splits =
-          std::max(std::min<int64_t>(cdiv(max_tiles, 8), 8), cdiv(max_tiles, kMaxItemTokens / kTileKeys));
-      lvl1.splits = (int32_t)splits;
-      double flops = 0.0;
-      for (int32_t j = 0; j < lvl1.n; ++j) {
-        const GroupCand& g = groups[j];
-        lvl1.req_begin[j] = g.a;
-        lvl1.req_end[j] = g.b;
-        lvl1.key_end[j] = g.len;
-        const int64_t tiles_per = cdiv(cdiv(g.len - plen, kTileKeys), splits);
-        lvl1.split_tokens[j] = (int32_t)(tiles_per * kTileKeys);
-        group_stages = std::max(group_stages, tiles_per);
-        lvl1.item_begin[j] = (int32_t)group_items;
-        const int64_t mtiles = cdiv((int64_t)(qsl[g.b] - qsl[g.a]) * pl->group, pre.rows_per_wg());
-        group_items += mtiles * pl->hkv * splits;
-        group_tokens += g.len - plen;
-        flops += 4.0 * (double)(mtiles * pre.rows_per_wg()) * pl->hkv * pl->d * (double)(g.len - plen);
-        for (int32_t r = g.a; r < g.b; ++r) kstart[r] = g.len;
+      const int32_t G = (int32_t)groups.size();
+      tree.n = G;
+      std::vector<int32_t> deep(n, -1);   // innermost group of each request
+      for (int32_t g = 0; g < G; ++g)
+        for (int32_t r : groups[g].members) deep[r] = g;   // children come after their parents
+      // tree order: requests sorted by the chain of groups that hold them
+      // (outermost first), so that every group's members are adjacent
+      std::vector<std::vector<int32_t>> key(n);
+      for (int32_t r = 0; r < n; ++r) {
+        for (int32_t g = deep[r]; g >= 0; g = groups[g].parent) key[r].insert(key[r].begin(), g);
+        key[r].resize(kMaxShared, INT32_MAX);
       }
-      lvl1.item_begin[lvl1.n] = (int32_t)group_items;
+      std::vector<int32_t> order(n);
+      for (int32_t r = 0; r < n; ++r) order[r] = r;
+      std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
+      std::vector<int32_t> pos_of(n);
+      tree.pos_cum[0] = 0;
+      for (int32_t p2 = 0; p2 < n; ++p2) {
+        pos_of[order[p2]] = p2;
+        tree.pos_tok[p2] = qsl[order[p2]];
+        tree.pos_cum[p2 + 1] = tree.pos_cum[p2] + (qsl[order[p2] + 1] - qsl[order[p2]]);
+      }
+      for (int32_t r = 0; r < n; ++r) tree.deepest[r] = deep[r] >= 0 ? (uint8_t)deep[r] : (uint8_t)0xff;
+      tree.levels = 1;
+      for (const auto& g : groups) tree.levels = std::max(tree.levels, g.level + 1);
+      // Every group of a level gets the same number of KV splits (so its
+      // rows fill that level's partial slots): about 512 keys per item for
+      // the level's longest group, at most 8 splits unless the per-item cap
+      // needs more.
+      for (int32_t lev = 1; lev < tree.levels; ++lev) {
+        int64_t max_tiles = 1;
+        for (const auto& g : groups)
+          if (g.level == lev) max_tiles = std::max(max_tiles, cdiv(g.len - g.parent_len, kTileKeys));
+        tree.level_splits[lev] = (int32_t)std::max(std::min<int64_t>(cdiv(max_tiles, 8), 8),
+                                                    cdiv(max_tiles, kMaxItemTokens / kTileKeys));
+      }
+      int32_t slot = pre.splits;
+      for (int32_t lev = 1; lev < tree.levels; ++lev) {
+        tree.level_slot_base[lev] = slot;
+        slot += tree.level_splits[lev];
+      }
+      double flops = 0.0;
+      for (int32_t j = 0; j < G; ++j) {
+        const TreeCand& g = groups[j];
+        int32_t pb = n, pe = 0;
+        for (int32_t r : g.members) {
+          pb = std::min(pb, pos_of[r]);
+          pe = std::max(pe, pos_of[r] + 1);
+        }
+        tree.level[j] = g.level;
+        tree.parent[j] = g.parent;
+        tree.first_req[j] = g.members[0];
+        tree.pos_begin[j] = pb;
+        tree.pos_end[j] = pe;
+        tree.key_begin[j] = g.parent_len;
+        tree.key_end[j] = g.len;
+        const int64_t splits = tree.level_splits[g.level];
+        const int64_t tiles_per = cdiv(cdiv(g.len - g.parent_len, kTileKeys), splits);
+        tree.split_tokens[j] = (int32_t)(tiles_per * kTileKeys);
+        group_stages = std::max(group_stages, tiles_per);
+        tree.rows[j] = (tree.pos_cum[pe] - tree.pos_cum[pb]) * pl->group;
+        tree.item_begin[j] = (int32_t)group_items;
+        const int64_t mtiles = cdiv(tree.rows[j], pre.rows_per_wg());
+        group_items += mtiles * pl->hkv * splits;
+        group_tokens += g.len - g.parent_len;
+        flops += 4.0 * (double)(mtiles * pre.rows_per_wg()) * pl->hkv * pl->d * (double)(g.len - g.parent_len);
+        for (int32_t r : g.members) kstart[r] = std::max<int64_t>(kstart[r], g.len);
+      }
+      tree.item_begin[G] = (int32_t)group_items;
       t_grp = std::max(flops / ((double)cus * cm.cu_mfma_rows), bpt * group_tokens / cm.hbm_bw) * 1e6 +
               cm.item_latency_us;
     }
@@ -642,7 +742,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     suf = choose_suffix(*pl, cus, true);
     const double t_suf = est_suffix_us(*pl, suffix_tokens, suffix_padded_flops(*pl, qsl, seq_lens, kstart.data()),
                                        suf.splits, false, 0.0, cus, cm, 0.0, 0.0);
-    const double merge_bytes = (double)(pre.splits + lvl1.splits + suf.splits) * total_q * pl->hq * pl->part_row_bytes() +
+    const double merge_bytes = (double)(pre.splits + tree.slots() + suf.splits) * total_q * pl->hq * pl->part_row_bytes() +
                                (double)total_q * pl->hq * pl->d * 2.0;
     // The single launch also takes no less than its items' CU time (decode
     // items running several KV heads pay their start-up once).
@@ -659,12 +759,13 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     // one launch runs the phases (t_suf carries its launch cost), one the merge
     // merge: a launch, or inside the launch by the item completing each row
     // block (a prefix item completes a whole prefix tile's rows)
-    const int32_t c_slots = pre.splits + lvl1.splits + suf.splits;
+    const int32_t c_slots = pre.splits + tree.slots() + suf.splits;
     const double ml = est_merge_launch_us(merge_bytes, cm);
     const int64_t c_items = pre_items + group_items + (int64_t)n * suf.mtiles * (pl->hkv / std::max(1, heads)) * suf.splits;
     const double mi = est_merge_in_launch_us(*pl, std::min<int64_t>(pre.rows_per_wg(), total_q * pl->group), c_slots,
                                              c_items, cus, cm);
-    casc_in_launch = merges_in_launch(p, n, suf.mtiles, pl->hkv, mi, ml);
+    // (not with nested levels: the merge units would need the tree's rows)
+    casc_in_launch = tree.n == 0 && merges_in_launch(p, n, suf.mtiles, pl->hkv, mi, ml);
     pl->est_us_cascade = (float)(std::max(pre_us + t_grp + t_suf, t_launch) + (casc_in_launch ? mi : ml));
     pl->kv_tokens_cascade = plen + group_tokens + suffix_tokens;
   }
@@ -690,7 +791,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
     pl->key_start = (int32_t)plen;
     pl->prefix = pre;
     pl->suffix = suf;
-    pl->lvl1 = lvl1;
+    pl->tree = tree;
     // all phases share one launch (two work-groups per CU): 2 stages of
     // bf16 or 4 of fp8 in the same LDS; fp8 items run one KV head each
     pl->prefix.stages = pl->kv_fp8 ? 4 : 2;
@@ -700,7 +801,7 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
                    : pick_heads_per_item(*pl, (int64_t)pre.mtiles * pl->hkv * pre.splits + group_items,
                                          std::max<int64_t>(pre.split_tokens / kTileKeys, group_stages), suf, cus);
     pl->separate_phases = p.separate_phases;
-    pl->num_slots = pre.splits + lvl1.splits + suf.splits;
+    pl->num_slots = pre.splits + tree.slots() + suf.splits;
     pl->direct_out = false;
     order_requests(*pl, p, seq_lens, kstart.data());
   } else {
@@ -768,8 +869,9 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   out->merge_in_launch = pl->merge_in_launch;
   out->suffix_heads_per_item = pl->suffix.heads_per_item;
   out->separate_phases = pl->separate_phases;
-  out->num_level1_groups = pl->lvl1.n;
-  out->level1_splits = pl->lvl1.splits;
+  out->num_level1_groups = pl->tree.n;
+  out->level1_splits = pl->tree.n > 0 ? pl->tree.level_splits[1] : 0;
+  out->shared_levels = pl->use_cascade ? pl->tree.levels : 0;
   out->kv_dtype = pl->kv_fp8 ? CA_KV_FP8_E4M3 : CA_KV_BF16;
   out->sliding_window = pl->window;
   out->suffix_longest_first = pl->order_n > 0 ? 1 : 0;
@@ -783,16 +885,20 @@ extern "C" ca_status_t cascade_attn_plan_info(ca_plan_t pl, ca_plan_info_t* out)
   return CA_OK;
 }
 
-extern "C" ca_status_t cascade_attn_plan_groups(ca_plan_t pl, int32_t capacity, int32_t* groups_out, int32_t* n_out) {
+extern "C" ca_status_t cascade_attn_plan_groups(ca_plan_t pl, int32_t capacity, int32_t* groups_out,
+                                                int32_t* deepest_out, int32_t* n_out) {
   if (!pl || !n_out || (capacity > 0 && !groups_out)) return fail(CA_EINVAL, "null plan or output");
   if (capacity < 0) return fail(CA_EINVAL, "capacity must be >= 0");
-  const Level1& L = pl->lvl1;
-  for (int32_t j = 0; j < L.n && j < capacity; ++j) {
-    groups_out[3 * j] = L.req_begin[j];
-    groups_out[3 * j + 1] = L.req_end[j];
-    groups_out[3 * j + 2] = L.key_end[j];
+  const Tree& T = pl->tree;
+  for (int32_t j = 0; j < T.n && j < capacity; ++j) {
+    groups_out[4 * j] = T.level[j];
+    groups_out[4 * j + 1] = T.parent[j];
+    groups_out[4 * j + 2] = T.key_begin[j];
+    groups_out[4 * j + 3] = T.key_end[j];
   }
-  *n_out = L.n;
+  if (deepest_out)
+    for (int32_t r = 0; r < pl->num_reqs; ++r) deepest_out[r] = (T.n > 0 && T.deepest[r] != 0xff) ? T.deepest[r] : -1;
+  *n_out = T.n;
   return CA_OK;
 }
 
@@ -804,8 +910,8 @@ extern "C" ca_status_t cascade_attn_autotune_record(const ca_params_t* params, c
                                                     int32_t max_levels) {
   if (!params) return fail(CA_EINVAL, "null pointer argument");
   if (mode != CA_MODE_FORCE_ON && mode != CA_MODE_FORCE_OFF) return fail(CA_EINVAL, "mode must be FORCE_ON or FORCE_OFF");
-  if (prefix_splits < 0 || heads_per_item < 0 || max_levels < 0 || max_levels > 2)
-    return fail(CA_EINVAL, "prefix_splits, heads_per_item must be >= 0 and max_levels in [0, 2]");
+  if (prefix_splits < 0 || heads_per_item < 0 || max_levels < 0 || max_levels > kMaxShared)
+    return fail(CA_EINVAL, "prefix_splits, heads_per_item must be >= 0 and max_levels in [0, 4]");
   // the shape key is that of the AUTO plan, made without the table
   ca_params_t p = *params;
   p.mode = CA_MODE_AUTO;

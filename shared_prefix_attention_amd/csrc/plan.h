@@ -30,10 +30,13 @@ struct PhaseTile {
 // Longest KV range one work item may cover (its page ids are held in LDS).
 constexpr int kMaxItemTokens = 512 * 16;
 
-// Second shared level: groups of consecutive requests that share pages
-// beyond the batch-wide prefix. At most kMaxLevel1Groups (they travel to the
-// kernels as launch arguments).
-constexpr int kMaxLevel1Groups = 64;
+// Nested shared levels: groups of requests (any requests, not only
+// consecutive ones) that share pages beyond the batch-wide prefix, found on
+// the prefix tree of the requests' page-id sequences, up to kMaxShared
+// shared levels in all (the batch-wide prefix is level 0). At most
+// kMaxTreeGroups groups; they travel to the kernels as launch arguments.
+constexpr int kMaxTreeGroups = 64;
+constexpr int kMaxShared = 4;
 // Requests whose work-item order a plan can set (kernel-argument table).
 constexpr int kOrderCapacity = 512;
 
@@ -44,14 +47,31 @@ constexpr int kOrderCapacity = 512;
 constexpr int64_t kCounterBytes = int64_t(256) << 10;
 constexpr int64_t kMaxCounters = kCounterBytes / 4;
 
-struct Level1 {
+struct Tree {
   int32_t n = 0;                               // groups in use
-  int32_t splits = 0;                          // KV splits of every group
-  int32_t req_begin[kMaxLevel1Groups] = {};    // requests [req_begin, req_end), ascending
-  int32_t req_end[kMaxLevel1Groups] = {};
-  int32_t key_end[kMaxLevel1Groups] = {};      // group shares positions [prefix_len, key_end)
-  int32_t split_tokens[kMaxLevel1Groups] = {}; // keys per split (multiple of kTileKeys)
-  int32_t item_begin[kMaxLevel1Groups + 1] = {};
+  int32_t levels = 1;                          // shared levels in use (1: the batch-wide prefix only)
+  int32_t level_splits[kMaxShared] = {};       // KV splits of every group of level l (l >= 1)
+  int32_t level_slot_base[kMaxShared] = {};    // first partial slot of level l
+  // per group, parents before children
+  int32_t level[kMaxTreeGroups] = {};          // 1 .. levels - 1
+  int32_t parent[kMaxTreeGroups] = {};         // enclosing group, -1: the batch-wide prefix
+  int32_t first_req[kMaxTreeGroups] = {};      // a member (its block-table row holds the shared pages)
+  int32_t pos_begin[kMaxTreeGroups] = {};      // members: tree-order positions [pos_begin, pos_end)
+  int32_t pos_end[kMaxTreeGroups] = {};
+  int32_t key_begin[kMaxTreeGroups] = {};      // positions shared beyond the enclosing level
+  int32_t key_end[kMaxTreeGroups] = {};
+  int32_t split_tokens[kMaxTreeGroups] = {};   // keys per split (multiple of kTileKeys)
+  int32_t rows[kMaxTreeGroups] = {};           // packed query rows: member tokens x group size
+  int32_t item_begin[kMaxTreeGroups + 1] = {};
+  // tree order: requests sorted so that every group's members are adjacent
+  int32_t pos_tok[kOrderCapacity] = {};        // first query token of the request at each position
+  int32_t pos_cum[kOrderCapacity + 1] = {};    // query tokens before each position
+  uint8_t deepest[kOrderCapacity] = {};        // innermost group of each request, 0xff: none
+  int32_t slots() const {
+    int32_t s = 0;
+    for (int l = 1; l < levels; ++l) s += level_splits[l];
+    return s;
+  }
 };
 
 }  // namespace ca
@@ -85,7 +105,7 @@ struct ca_plan {
   int32_t num_slots = 0;      // partial states per (token, head)
   bool direct_out = false;    // the last attention launch writes the bf16 output directly
   int32_t separate_phases = 0;// cascade: prefix and suffix as two launches
-  ca::Level1 lvl1;            // cascade: second shared level (n = 0: none)
+  ca::Tree tree;              // cascade: nested shared levels (n = 0: none)
   int64_t slot_elems = 0;     // T * Hq * d
   int32_t merge_in_launch = 0;// partial states merged inside the attention launch (no merge launch)
   int64_t ws_o_offset = 0;    // byte offset of the partial outputs (after the counters)
@@ -93,7 +113,7 @@ struct ca_plan {
   int64_t workspace_bytes = 0;
 
   int64_t sum_seq = 0;         // shape signature inputs (autotuning table)
-  int32_t cand_groups = 0;     // second-level groups the detector found (taken or not)
+  int32_t cand_groups = 0;     // nested groups the detector found (taken or not)
   // dispatch order of the per-request work items: the j-th request slot runs
   // request order[j] (order_n = 0: batch order; else order_n = num_reqs)
   int32_t order_n = 0;

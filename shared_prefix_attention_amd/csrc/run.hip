@@ -22,7 +22,7 @@ using namespace ca;
 namespace {
 
 enum KernelKind { K_PHASES = 0, K_ATTN = 1, K_MERGE = 2, K_DECODE = 3, K_PREFIX = 4, K_SUFFIX = 5, K_LEVEL1 = 6, K_KINDS = 7 };
-static_assert(kMaxGroups == kMaxLevel1Groups, "group table size");
+static_assert(kMaxGroups == kMaxTreeGroups && kMaxLevels == kMaxShared && kMaxTreeOrder == kOrderCapacity, "group table size");
 static_assert(kOrderCapacity == kMaxOrderedReqs, "request order table size");
 static_assert(K_KINDS == CA_PROFILE_KINDS, "profile kinds");
 
@@ -250,28 +250,50 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   mt.num_reqs = pl->num_reqs;
   mt.m_pre_splits = pl->use_cascade ? pl->prefix.splits : 0;
   mt.m_pre_rows = pl->use_cascade ? pl->prefix.rows_per_wg() : 1;
-  mt.m_lvl_splits = (pl->use_cascade && pl->lvl1.n > 0) ? pl->lvl1.splits : 0;
   mt.m_suf_splits = pl->suffix.splits;
   mt.m_suf_rows = pl->suffix.rows_per_wg();
   mt.m_suf_mtiles = pl->suffix.mtiles;
   mt.uniform_q = pl->uniform_q;
   base.coherent = mt.counters ? 1 : 0;
 
-  // second shared level (none: n = 0)
+  // nested shared levels (none: n = 0)
   GroupTable gt{};
-  const Level1& L = pl->lvl1;
-  gt.n = pl->use_cascade ? L.n : 0;
-  for (int j = 0; j < gt.n; ++j) {
-    gt.item_begin[j] = L.item_begin[j];
-    gt.req_begin[j] = L.req_begin[j];
-    gt.req_end[j] = L.req_end[j];
-    gt.key_end[j] = L.key_end[j];
-    gt.split_tokens[j] = L.split_tokens[j];
+  const Tree& T = pl->tree;
+  gt.n = pl->use_cascade ? T.n : 0;
+  gt.levels = gt.n > 0 ? T.levels : 1;
+  gt.uniform_q = pl->uniform_q;
+  if (gt.n > kMaxGroups || gt.levels > kMaxLevels || (gt.n > 0 && pl->num_reqs > kMaxTreeOrder))
+    return fail(CA_EINVAL, "nested levels exceed the kernel's group table");
+  if (gt.n > 0 && mt.counters) return fail(CA_EINVAL, "plans with nested levels merge in a launch of their own");
+  for (int l = 0; l < gt.levels; ++l) {
+    gt.level_splits[l] = T.level_splits[l];
+    gt.level_slot_base[l] = T.level_slot_base[l];
   }
-  gt.item_begin[gt.n] = gt.n > 0 ? L.item_begin[gt.n] : 0;
-  for (int j = 0; j < gt.n; ++j)
-    if (L.split_tokens[j] <= 0 || L.split_tokens[j] > kMaxItemTokens || L.split_tokens[j] % kTileKeys)
+  for (int j = 0; j < gt.n; ++j) {
+    gt.item_begin[j] = T.item_begin[j];
+    gt.level[j] = T.level[j];
+    gt.first_req[j] = T.first_req[j];
+    gt.pos_begin[j] = T.pos_begin[j];
+    gt.pos_end[j] = T.pos_end[j];
+    gt.key_begin[j] = T.key_begin[j];
+    gt.key_end[j] = T.key_end[j];
+    gt.split_tokens[j] = T.split_tokens[j];
+    gt.rows[j] = T.rows[j];
+    if (T.split_tokens[j] <= 0 || T.split_tokens[j] > kMaxItemTokens || T.split_tokens[j] % kTileKeys)
       return fail(CA_EINVAL, "group work item exceeds the per-item KV limit");
+    if (T.level[j] < 1 || T.level[j] >= gt.levels || T.pos_begin[j] < 0 || T.pos_end[j] > pl->num_reqs ||
+        T.pos_begin[j] >= T.pos_end[j])
+      return fail(CA_EINVAL, "malformed group table in plan");
+  }
+  gt.item_begin[gt.n] = gt.n > 0 ? T.item_begin[gt.n] : 0;
+  if (gt.n > 0) {
+    for (int r = 0; r < pl->num_reqs; ++r) {
+      gt.pos_tok[r] = T.pos_tok[r];
+      gt.pos_cum[r] = T.pos_cum[r];
+      gt.deepest[r] = T.deepest[r];
+    }
+    gt.pos_cum[pl->num_reqs] = T.pos_cum[pl->num_reqs];
+  }
 
   // dispatch order of the per-request items (n = 0: batch order)
   ReqOrder ro{};
@@ -290,11 +312,9 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
   sa.splits = pl->suffix.splits;
   sa.split_tokens = pl->suffix.split_tokens;
   sa.heads_per_item = pl->suffix.heads_per_item;
-  sa.slot_base = pl->use_cascade ? pl->prefix.splits + (gt.n > 0 ? L.splits : 0) : 0;
+  sa.slot_base = pl->use_cascade ? pl->prefix.splits + (gt.n > 0 ? T.slots() : 0) : 0;
   sa.direct = pl->direct_out ? 1 : 0;
   sa.window = pl->use_cascade ? 0 : pl->window;
-  sa.lvl1_slot_base = pl->prefix.splits;
-  sa.lvl1_slots = gt.n > 0 ? L.splits : 0;
   // several KV heads per item only in the decode shape (its waves split the keys)
   if (sa.heads_per_item < 1 || pl->hkv % sa.heads_per_item != 0 ||
       (sa.heads_per_item > 1 && pl->suffix.key_groups == 1))
@@ -311,12 +331,10 @@ ca_status_t run_impl(const ca_plan* pl, const void* q, const void* k, const void
     pa.slot_base = 0;
     pa.direct = 0;
     const int64_t n_prefix = (int64_t)pa.mtiles * pl->hkv * pa.splits;
-    TileArgs ga = base;   // group level: prefix-shaped items over each group's extra pages
+    TileArgs ga = base;   // nested levels: prefix-shaped items over each group's extra pages
     ga.prefix_mode = 2;
-    ga.key_start = pl->prefix_len;
-    ga.splits = gt.n > 0 ? L.splits : 1;
-    ga.split_tokens = kTileKeys;   // per group in the table
-    ga.slot_base = pl->prefix.splits;
+    ga.splits = 1;                 // per level, key ranges and slots per group: in the table
+    ga.split_tokens = kTileKeys;
     ga.direct = 0;
     const int64_t n_group = gt.n > 0 ? gt.item_begin[gt.n] : 0;
     if (pl->separate_phases) {

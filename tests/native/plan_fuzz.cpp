@@ -12,6 +12,7 @@
 //     whose shared length lies past the batch-wide prefix.
 // Exit status 0 when every check passes; the sanitizers abort on the first
 // memory or undefined-behaviour error.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -28,7 +29,7 @@ extern "C" int ca_query_num_cus(int32_t* out) {
 }
 
 static int g_fail = 0;
-static int g_cascade = 0, g_grouped = 0, g_ordered = 0;
+static int g_cascade = 0, g_grouped = 0, g_deep = 0, g_ordered = 0;
 #define CHECK(cond, ...)                                  \
   do {                                                    \
     if (!(cond)) {                                        \
@@ -44,8 +45,10 @@ struct Batch {
   std::vector<int32_t> bt, qsl, sl, nc;
 };
 
-// Random batch: a shared prefix, optional runs of consecutive requests that
-// share a document, then each request's own pages; some block-table padding.
+// Random batch: a shared prefix, optional runs of requests that share a
+// document, some of whose members share a chapter of it, and so on (up to 3
+// nested levels), then each request's own pages; the requests in random
+// order half of the time; some block-table padding.
 static Batch make_batch(std::mt19937& rng, int n, int prefix_pages, int max_groups, int max_own, int max_q) {
   auto U = [&](int lo, int hi) { return std::uniform_int_distribution<int>(lo, hi)(rng); };
   Batch b;
@@ -59,13 +62,21 @@ static Batch make_batch(std::mt19937& rng, int n, int prefix_pages, int max_grou
   std::vector<int> doc(n, 0);
   std::vector<std::vector<int32_t>> doc_pages(n);
   for (int gi = 0; gi < groups && r < n; ++gi) {
-    const int m = std::min(n - r, U(1, 4));
-    const int dp = U(1, 40);
-    std::vector<int32_t> d;
-    for (int j = 0; j < dp; ++j) d.push_back(next++);
-    for (int k = 0; k < m; ++k) doc_pages[r + k] = d;
+    const int m = std::min(n - r, U(1, 6));
+    for (int lvl = 0, lo = r, hi = r + m; lvl < 3 && hi - lo >= 1; ++lvl) {
+      const int dp = U(1, 40);
+      for (int j = 0; j < dp; ++j)
+        for (int k = lo; k < hi; ++k) doc_pages[k].push_back(next + j);
+      next += dp;
+      // a sub-run of the members goes one level deeper
+      const int a = U(lo, hi - 1), e = U(a + 1, hi);
+      lo = a;
+      hi = e;
+      if (U(0, 2) == 0) break;
+    }
     r += m + U(0, 2);
   }
+  if (U(0, 1)) std::shuffle(doc_pages.begin(), doc_pages.end(), rng);
   int maxp = 0;
   for (int i = 0; i < n; ++i) {
     rows[i] = shared;
@@ -138,25 +149,54 @@ static void check_plan(const Batch& b, const ca_params_t& p, ca_plan_t pl) {
   CHECK(info.total_q == b.qsl[b.n], "total_q");
   g_cascade += info.use_cascade;
   g_grouped += info.num_level1_groups > 0;
+  g_deep += info.shared_levels >= 3;
   g_ordered += info.suffix_longest_first;
   CHECK(info.workspace_bytes >= 0 && (info.num_partial_slots == 0) == (info.workspace_bytes == 0), "workspace");
-  // groups: disjoint ascending runs, shared length past the batch prefix
+  // groups: a tree under the batch prefix (parents first), each group
+  // sharing >= 256 more tokens than its parent, capped at its members'
+  // num_computed; >= 2 members, which share the group's pages
   int32_t n_groups = -1;
-  CHECK(cascade_attn_plan_groups(pl, 0, nullptr, &n_groups) == CA_OK, "groups count");
+  CHECK(cascade_attn_plan_groups(pl, 0, nullptr, nullptr, &n_groups) == CA_OK, "groups count");
   CHECK(n_groups == info.num_level1_groups && n_groups <= 64, "groups %d", n_groups);
+  if (!info.use_cascade) CHECK(info.shared_levels == 0 && n_groups == 0, "non-cascade levels");
+  else if (n_groups == 0) CHECK(info.shared_levels == 1, "one level");
+  CHECK(info.shared_levels <= (p.max_levels == 0 ? 4 : p.max_levels), "shared levels %d", info.shared_levels);
   if (n_groups > 0) {
-    const int cap = n_groups > 1 ? n_groups - 1 : 1;   // a short buffer: only cap triples are written
-    std::vector<int32_t> g((size_t)3 * cap);
+    std::vector<int32_t> g((size_t)4 * n_groups), deep(b.n, -7);
     int32_t n2 = 0;
-    CHECK(cascade_attn_plan_groups(pl, cap, g.data(), &n2) == CA_OK && n2 == n_groups, "groups");
-    int prev_end = 0;
-    for (int j = 0; j < std::min(cap, n_groups); ++j) {
-      const int a = g[3 * j], e = g[3 * j + 1], len = g[3 * j + 2];
-      CHECK(a >= prev_end && e - a >= 2 && e <= b.n, "group range %d %d", a, e);
-      CHECK(len % 16 == 0 && len - plen >= 256, "group length %d", len);
-      for (int r = a; r < e; ++r) CHECK(len <= b.nc[r], "group cap");
-      prev_end = e;
+    CHECK(cascade_attn_plan_groups(pl, n_groups, g.data(), deep.data(), &n2) == CA_OK && n2 == n_groups, "groups");
+    std::vector<int> members(n_groups, 0);
+    int max_level = 0;
+    for (int j = 0; j < n_groups; ++j) {
+      const int lev = g[4 * j], par = g[4 * j + 1], kb = g[4 * j + 2], ke = g[4 * j + 3];
+      max_level = std::max(max_level, lev);
+      CHECK(par >= -1 && par < j, "parent order %d %d", j, par);
+      CHECK(lev == (par < 0 ? 1 : g[4 * par] + 1), "level %d", lev);
+      CHECK(kb == (par < 0 ? plen : g[4 * par + 3]), "key_begin %d", kb);
+      CHECK(ke % 16 == 0 && ke - kb >= 256, "group length %d %d", kb, ke);
     }
+    CHECK(info.shared_levels == max_level + 1, "levels %d %d", info.shared_levels, max_level);
+    for (int r = 0; r < b.n; ++r) {
+      CHECK(deep[r] >= -1 && deep[r] < n_groups, "deepest %d", deep[r]);
+      for (int j = deep[r]; j >= 0; j = g[4 * j + 1]) {
+        ++members[j];
+        CHECK(g[4 * j + 3] <= b.nc[r], "group cap");
+        // the member holds the group's pages: those of the group's first
+        // member found so far (page ids equal on every shared column)
+        for (int c = 0; c < g[4 * j + 3] / 16; ++c) {
+          int first = -1;
+          for (int r2 = 0; r2 < b.n && first < 0; ++r2)
+            for (int k = deep[r2]; k >= 0; k = g[4 * k + 1])
+              if (k == j) { first = r2; break; }
+          CHECK(first >= 0 && b.bt[(size_t)r * b.stride + c] == b.bt[(size_t)first * b.stride + c], "group pages");
+        }
+      }
+    }
+    for (int j = 0; j < n_groups; ++j) CHECK(members[j] >= 2, "group members %d", members[j]);
+    // a short buffer: only cap rows are written
+    std::vector<int32_t> s((size_t)4 * n_groups + 4, -9);
+    CHECK(cascade_attn_plan_groups(pl, n_groups - 1, s.data(), nullptr, &n2) == CA_OK && n2 == n_groups, "short");
+    CHECK(s[(size_t)4 * (n_groups - 1)] == -9, "wrote past capacity");
   }
 }
 
@@ -174,7 +214,7 @@ static void fuzz(std::mt19937& rng, int iters) {
     const int d = U(0, 1) ? 128 : 64;
     ca_params_t p = base_params(b, hh[0], hh[1], d);
     p.mode = U(0, 2);
-    p.max_levels = U(0, 2);
+    p.max_levels = U(0, 4);
     p.separate_phases = U(0, 1);
     p.suffix_order = U(0, 1);
     p.partials_fp32 = U(0, 1);
@@ -196,7 +236,7 @@ static void fuzz(std::mt19937& rng, int iters) {
       const int mode = U(1, 2);
       const ca_status_t rs =
           cascade_attn_autotune_record(&p, b.bt.data(), b.qsl.data(), b.sl.data(), b.nc.data(), mode, U(0, 8), 0,
-                                       U(0, 2));
+                                       U(0, 4));
       // a cascade choice is refused where a sliding window rules cascade out
       CHECK(rs == CA_OK || (rs == CA_EUNSUPPORTED && mode == CA_MODE_FORCE_ON && p.sliding_window > 0),
             "record %d: %s", rs, cascade_attn_last_error());
@@ -292,7 +332,7 @@ static void error_paths() {
       {[](ca_params_t& p) { p.mode = 3; }, CA_EINVAL, "mode"},
       {[](ca_params_t& p) { p.heads_per_item = 3; }, CA_EINVAL, "heads_per_item"},
       {[](ca_params_t& p) { p.separate_phases = 2; }, CA_EINVAL, "separate_phases"},
-      {[](ca_params_t& p) { p.max_levels = 3; }, CA_EINVAL, "max_levels"},
+      {[](ca_params_t& p) { p.max_levels = 5; }, CA_EINVAL, "max_levels"},
       {[](ca_params_t& p) { p.kv_dtype = 2; }, CA_EINVAL, "kv_dtype"},
       {[](ca_params_t& p) { p.sliding_window = -1; }, CA_EINVAL, "window"},
       {[](ca_params_t& p) { p.prefix_splits = -1; }, CA_EINVAL, "prefix_splits"},
@@ -342,7 +382,7 @@ static void error_paths() {
   // getters and record
   CHECK(cascade_attn_plan_info(nullptr, nullptr) == CA_EINVAL, "info null");
   int32_t n_out = 0;
-  CHECK(cascade_attn_plan_groups(nullptr, 0, nullptr, &n_out) == CA_EINVAL, "groups null");
+  CHECK(cascade_attn_plan_groups(nullptr, 0, nullptr, nullptr, &n_out) == CA_EINVAL, "groups null");
   CHECK(cascade_attn_autotune_record(&good, bt, qsl, sl, nc, CA_MODE_AUTO, 0, 0, 0) == CA_EINVAL, "record mode");
   CHECK(cascade_attn_autotune_record(nullptr, bt, qsl, sl, nc, CA_MODE_FORCE_ON, 0, 0, 0) == CA_EINVAL,
         "record null");
@@ -360,7 +400,12 @@ int main(int argc, char** argv) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);
     return 1;
   }
-  std::printf("plan_fuzz: %d random batches (%d cascade plans, %d with groups, %d longest-first), error paths and "
-              "the group limit: all checks passed\n", iters, g_cascade, g_grouped, g_ordered);
+  if (g_grouped < iters / 20 || g_deep < iters / 200) {
+    std::fprintf(stderr, "too few plans with groups (%d) or with >= 3 levels (%d)\n", g_grouped, g_deep);
+    return 1;
+  }
+  std::printf("plan_fuzz: %d random batches (%d cascade plans, %d with groups, %d with >= 3 levels, %d "
+              "longest-first), error paths and the group limit: all checks passed\n",
+              iters, g_cascade, g_grouped, g_deep, g_ordered);
   return 0;
 }

@@ -95,13 +95,13 @@ def test_plan_matches_oracle_on_workloads(name):
     assert info["common_prefix_len"] == plen
     assert info["gates_pass"] == int(oracle.passes_cascade_gates(plen, b.workload.num_reqs))
     assert info["kv_tokens_noncascade"] == oracle.kv_tokens_standard(b.seq_lens.tolist())
-    groups = oracle.level1_groups(b.block_table.tolist(), b.seq_lens.tolist(), b.num_computed.tolist(), ps, plen)
-    assert info["kv_tokens_cascade"] == oracle.kv_tokens_multilevel(plen, groups, b.seq_lens.tolist())
+    groups = oracle.tree_groups(b.block_table.tolist(), b.seq_lens.tolist(), b.num_computed.tolist(), ps, plen)
+    assert info["kv_tokens_cascade"] == oracle.kv_tokens_tree(plen, groups, b.seq_lens.tolist())
     if not groups:
         assert info["kv_tokens_cascade"] == oracle.kv_tokens_cascade(plen, b.seq_lens.tolist())
     assert info["total_q"] == b.total_q
     if plen > 0:
-        assert spa.cascade_attn_plan_groups(_plan(b, mode="on")) == groups
+        assert _tree_of(_plan(b, mode="on")) == groups
     if plen < 256 or b.workload.num_reqs < 2:   # AUTO's gate
         assert info["use_cascade"] == 0
     on = _plan(b, mode="on").info
@@ -210,7 +210,7 @@ def test_error_codes():
         _try(separate_phases=2)
     assert e.value.status == _lib.CA_EINVAL
     with pytest.raises(spa.CascadeAttnError) as e:
-        _try(max_levels=3)
+        _try(max_levels=5)
     assert e.value.status == _lib.CA_EINVAL
     with pytest.raises(spa.CascadeAttnError) as e:
         _try(kv_dtype=2)
@@ -240,8 +240,12 @@ def test_plan_partition_is_consistent():
             assert wide["partials_fp32"] == 1
             assert wide["workspace_bytes"] >= wide["num_partial_slots"] * T * hq * (d + 1) * 4
             if info["use_cascade"]:
-                assert slots == info["prefix_splits"] + info["level1_splits"] + info["suffix_chunks"]
+                if info["shared_levels"] <= 2:
+                    assert slots == info["prefix_splits"] + info["level1_splits"] + info["suffix_chunks"]
+                else:
+                    assert slots > info["prefix_splits"] + info["level1_splits"] + info["suffix_chunks"]
                 assert (info["level1_splits"] > 0) == (info["num_level1_groups"] > 0)
+                assert (info["shared_levels"] > 1) == (info["num_level1_groups"] > 0)
                 assert info["prefix_splits"] >= 1
             assert info["suffix_chunk_tokens"] % 64 == 0
             assert 0 < info["suffix_chunk_tokens"] <= 8192
@@ -365,9 +369,23 @@ def test_auto_matches_the_decision_sweep(name, n, p, s, q, casc):
     assert info["use_cascade"] == casc, (info["est_us_cascade"], info["est_us_noncascade"])
 
 
-def _nested_tables(rng, n, ps=16):
+def _tree_of(pl):
+    """The plan's nested groups in the oracle's form: (members in batch
+    order, enclosing length, shared length, level), parents first."""
+    groups, deepest = spa.cascade_attn_plan_groups(pl)
+    members = [[] for _ in groups]
+    for r, g in enumerate(deepest):
+        while g >= 0:
+            members[g].append(r)
+            g = groups[g][1]
+    return [(tuple(sorted(members[j])), kb, ke, lev) for j, (lev, _, kb, ke) in enumerate(groups)]
+
+
+def _nested_tables(rng, n, ps=16, depth=1, shuffle=False):
     """Random block tables with a level-0 prefix, runs of requests sharing
-    extra pages (sometimes only some of a run), and random lengths."""
+    extra pages (sometimes only some of a run), nested `depth` levels deep,
+    and random lengths; with `shuffle`, the requests in random order (group
+    members not adjacent)."""
     level0 = int(rng.integers(16, 20))
     rows, seq, nxt = [], [], [1000]
 
@@ -376,18 +394,25 @@ def _nested_tables(rng, n, ps=16):
         nxt[0] += k
         return ids
 
-    base = fresh(level0)
-    r = 0
-    while r < n:
-        m = int(rng.integers(1, 5))
-        extra = fresh(int(rng.integers(0, 40)))
-        for i in range(min(m, n - r)):
-            keep = len(extra) if rng.random() < 0.8 else int(rng.integers(0, len(extra) + 1))
-            own = fresh(int(rng.integers(1, 6)))
-            row = base + extra[:keep] + own
-            rows.append(row)
-            seq.append((len(row) - 1) * ps + int(rng.integers(1, ps + 1)))
-        r += m
+    def fill(prefix, count, lvl):
+        r = 0
+        while r < count:
+            m = min(int(rng.integers(1, 5)), count - r)
+            extra = fresh(int(rng.integers(0, 40)))
+            if lvl < depth and m >= 2 and rng.random() < 0.6:
+                fill(prefix + extra, m, lvl + 1)
+            else:
+                for _ in range(m):
+                    keep = len(extra) if rng.random() < 0.8 else int(rng.integers(0, len(extra) + 1))
+                    row = prefix + extra[:keep] + fresh(int(rng.integers(1, 6)))
+                    rows.append(row)
+                    seq.append((len(row) - 1) * ps + int(rng.integers(1, ps + 1)))
+            r += m
+
+    fill(fresh(level0), n, 1)
+    order = rng.permutation(n) if shuffle else np.arange(n)
+    rows = [rows[i] for i in order]
+    seq = [seq[i] for i in order]
     stride = max(len(x) for x in rows) + 1
     bt = np.zeros((n, stride), dtype=np.int32)
     for i, row in enumerate(rows):
@@ -398,45 +423,53 @@ def _nested_tables(rng, n, ps=16):
     return bt, seq, q, nxt[0]
 
 
-def test_level1_groups_match_oracle_on_random_batches():
-    rng = np.random.default_rng(41)
-    for _ in range(300):
-        n = int(rng.integers(1, 24))
-        bt, seq, q, pages = _nested_tables(rng, n)
+@pytest.mark.parametrize("depth,shuffle", [(1, False), (1, True), (3, False), (3, True)])
+def test_tree_groups_match_oracle_on_random_batches(depth, shuffle):
+    rng = np.random.default_rng(41 + 10 * depth + int(shuffle))
+    deep_seen = 0
+    for _ in range(150):
+        n = int(rng.integers(1, 40))
+        bt, seq, q, pages = _nested_tables(rng, n, depth=depth, shuffle=shuffle)
         nc = seq - q
         qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
-        pl = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=pages,
-                                   kv_strides=(16 * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
-                                   seq_lens=seq, num_computed_tokens=nc, mode="on", num_cus=256)
+        kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=pages,
+                  kv_strides=(16 * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl, seq_lens=seq,
+                  num_computed_tokens=nc, mode="on", num_cus=256)
+        pl = spa.cascade_attn_plan(**kw)
         info = pl.info
         plen = info["common_prefix_len"]
-        want = oracle.level1_groups(bt.tolist(), seq.tolist(), nc.tolist(), 16, plen)
-        got = spa.cascade_attn_plan_groups(pl)
-        assert got == want
+        want = oracle.tree_groups(bt.tolist(), seq.tolist(), nc.tolist(), 16, plen)
+        assert _tree_of(pl) == want
         assert info["num_level1_groups"] == len(want)
-        assert info["kv_tokens_cascade"] == oracle.kv_tokens_multilevel(plen, want, seq.tolist())
-        single = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=pages,
-                                       kv_strides=(16 * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
-                                       seq_lens=seq, num_computed_tokens=nc, mode="on", num_cus=256, max_levels=1)
-        assert single.info["num_level1_groups"] == 0 and spa.cascade_attn_plan_groups(single) == []
+        assert info["shared_levels"] == 1 + max([g[3] for g in want], default=0)
+        assert info["kv_tokens_cascade"] == oracle.kv_tokens_tree(plen, want, seq.tolist())
+        deep_seen += info["shared_levels"] >= 3
+        for levels in (1, 2, 3):
+            lim = spa.cascade_attn_plan(**kw, max_levels=levels)
+            want_l = oracle.tree_groups(bt.tolist(), seq.tolist(), nc.tolist(), 16, plen, max_levels=levels)
+            assert _tree_of(lim) == want_l
+            assert lim.info["shared_levels"] <= levels
+    if depth > 1:
+        assert deep_seen >= 10
 
 
-def test_level1_keeps_the_64_groups_that_save_most():
+def test_tree_keeps_the_64_groups_that_save_most():
     """100 pairs of requests, each pair sharing its own document of a
-    different length beyond the batch prefix: the plan keeps 64 groups, the
-    ones whose documents are longest (saving = extra tokens), in batch order."""
+    different length beyond the batch prefix, interleaved (pair i is
+    requests i and i + 100): the plan keeps 64 groups, the ones whose
+    documents are longest (saving = extra tokens), in the order found."""
     ps, level0 = 16, 16
-    rows, seq = [], []
+    rows, seq = [None] * 200, [None] * 200
     nxt = 1000
     doc_pages = [17 + (i * 37) % 50 for i in range(100)]
     for i in range(100):
         doc = list(range(nxt, nxt + doc_pages[i]))
         nxt += doc_pages[i]
-        for _ in range(2):
+        for r in (i, i + 100):
             row = list(range(level0)) + doc + [nxt]
             nxt += 1
-            rows.append(row)
-            seq.append(len(row) * ps)
+            rows[r] = row
+            seq[r] = len(row) * ps
     stride = max(len(x) for x in rows)
     bt = np.zeros((200, stride), dtype=np.int32)
     for i, row in enumerate(rows):
@@ -446,11 +479,32 @@ def test_level1_keeps_the_64_groups_that_save_most():
     pl = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=ps, num_pages=nxt,
                                kv_strides=(ps * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
                                seq_lens=seq, mode="on", num_cus=256)
-    got = spa.cascade_attn_plan_groups(pl)
-    every = oracle.level1_groups(bt.tolist(), seq.tolist(), (seq - 1).tolist(), ps, level0 * ps)
+    got = _tree_of(pl)
+    every = oracle.tree_groups(bt.tolist(), seq.tolist(), (seq - 1).tolist(), ps, level0 * ps)
     assert len(every) == 100 and len(got) == 64
-    by_saving = sorted(every, key=lambda g: -(g[2] - level0 * ps))
-    assert sorted(got) == sorted(by_saving[:64]) and got == sorted(got)
+    by_saving = sorted(every, key=lambda g: -(g[2] - g[1]))
+    assert sorted(got) == sorted(by_saving[:64])
+    assert got == [g for g in every if g in got]   # order found
+    assert all(len(g[0]) == 2 and g[0][1] == g[0][0] + 100 for g in got)
+
+
+def test_tree_batches_beyond_the_order_table_use_one_level():
+    """More than 512 requests: no nested levels (the kernels' tree-order
+    table holds 512 positions); the batch-wide prefix still applies."""
+    n = 600
+    rows = []
+    nxt = 100000
+    for r in range(n):
+        rows.append(list(range(20)) + list(range(1000 + 40 * (r % 7), 1000 + 40 * (r % 7) + 30)) + [nxt])
+        nxt += 1
+    bt = np.array(rows, dtype=np.int32)
+    seq = np.full(n, bt.shape[1] * 16, dtype=np.int32)
+    qsl = np.arange(n + 1, dtype=np.int32)
+    pl = spa.cascade_attn_plan(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=nxt,
+                               kv_strides=(16 * 2 * 128, 2 * 128, 128), block_table=bt, query_start_loc=qsl,
+                               seq_lens=seq, mode="on", num_cus=256)
+    assert pl.info["use_cascade"] == 1 and pl.info["common_prefix_len"] == 320
+    assert pl.info["num_level1_groups"] == 0 and pl.info["shared_levels"] == 1
 
 
 def test_fp8_plans():
@@ -558,7 +612,7 @@ def test_auto_is_a_function_of_the_batch_unless_tuning_is_asked_for():
         assert _plan(wd, mode="auto").info == before
         spa.cascade_attn_autotune_reset()
         assert _plan(wd, mode="auto", use_tuned=True).info == before
-        for bad in (dict(mode="auto"), dict(mode="on", prefix_splits=-1), dict(mode="on", max_levels=3)):
+        for bad in (dict(mode="auto"), dict(mode="on", prefix_splits=-1), dict(mode="on", max_levels=5)):
             with pytest.raises(spa.CascadeAttnError) as e:
                 spa.cascade_attn_autotune_record(**bad, **kw)
             assert e.value.status == _lib.CA_EINVAL

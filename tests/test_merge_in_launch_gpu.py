@@ -3,7 +3,9 @@ choice where it pays): the work item that completes a row block's partial
 states merges it, in the same slot order as the stand-alone merge kernel. So
 its outputs and LSEs equal, bit for bit, those of the same plan with a
 separate merge launch (merge_mode=1), run after run (the arrival counters go
-back to zero), and match the oracle."""
+back to zero), and match the oracle. Plans with nested shared levels merge
+in a launch of their own whatever merge_mode asks; batches with documents
+are run here with the batch-wide level only (max_levels=1)."""
 
 import numpy as np
 import pytest
@@ -51,6 +53,8 @@ def _batch(name):
 def test_merge_in_launch_equals_merge_launch(name, mode, kw):
     log(f"[merge in launch] {name} mode={mode} {kw}")
     b = _batch(name)
+    if b.workload.groups or b.workload.docs:
+        kw = dict(kw, max_levels=1)
     db = DeviceBatch(b)
     o1, l1, i1 = run(db, mode=mode, merge_mode=2, **kw)
     o2, l2, i2 = run(db, mode=mode, merge_mode=1, **kw)
@@ -72,8 +76,8 @@ def test_merge_in_launch_with_sinks(name, mode):
     z = np.random.default_rng(5).normal(0.0, 2.0, b.workload.num_q_heads).astype(np.float32)
     z[0] = -np.inf
     db = DeviceBatch(b)
-    o1, l1, i1 = run(db, mode=mode, sinks=z, merge_mode=2)
-    o2, l2, _ = run(db, mode=mode, sinks=z, merge_mode=1)
+    o1, l1, i1 = run(db, mode=mode, sinks=z, merge_mode=2, max_levels=1)
+    o2, l2, _ = run(db, mode=mode, sinks=z, merge_mode=1, max_levels=1)
     assert i1["merge_in_launch"] == 1
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     ref_o, ref_l = oracle_ref(b, sinks=z)
@@ -111,3 +115,18 @@ def test_counters_return_to_zero_and_workspace_init():
         assert int(ws[:spa._lib.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, f"{name}: counters not reset"
         ref_o, ref_l = run(db, mode=mode, merge_mode=1)[:2]
         assert np.array_equal(out.float().cpu().numpy(), ref_o) and np.array_equal(lse.cpu().numpy(), ref_l)
+
+
+@pytest.mark.parametrize("name", ["nested_prefill", "fp8_nested", "multi_doc"])
+def test_nested_levels_merge_in_a_launch_of_their_own(name):
+    """merge_mode=2 on a plan with nested levels: the plan reports a separate
+    merge, and the result equals merge_mode=1's bit for bit and the oracle."""
+    b = _batch(name)
+    db = DeviceBatch(b)
+    o1, l1, i1 = run(db, mode="on", merge_mode=2)
+    o2, l2, i2 = run(db, mode="on", merge_mode=1)
+    assert i1["num_level1_groups"] > 0 and i1["merge_in_launch"] == 0 and i2["merge_in_launch"] == 0
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    if b.workload.num_reqs <= 16:
+        ref_o, ref_l = oracle_ref(b)
+        assert_close(o1, l1, ref_o, ref_l, what=f"{name}/nested/merge_mode=2")

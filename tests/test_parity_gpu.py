@@ -56,6 +56,20 @@ SMALL = {
                  groups=((4, 512), (3, 300)), kv_dtype="fp8", k_scale=0.25, v_scale=0.125),
         Workload("fp8_fresh_prefill", 4, 0, (30, 50), (30, 50), 4, 1, 128, seed=2021,
                  kv_dtype="fp8", k_scale=0.125, v_scale=0.0625),
+        # nested levels in a tree: members not adjacent in the batch, up to
+        # four shared levels (prefix -> document -> chapter -> section)
+        Workload("tree_decode", 16, 256, (1, 40), (1, 1), 8, 2, 128, seed=2023,
+                 docs=(((0, 3, 5, 8, 11, 14), 512), ((3, 8, 14), 256), ((8, 14), 300), ((1, 6, 9), 640))),
+        Workload("tree_prefill", 12, 256, (5, 60), (1, 12), 8, 2, 128, seed=2024,
+                 docs=(((1, 4, 7, 10), 768), ((4, 10), 512), ((2, 11), 400))),
+        Workload("tree_d64", 10, 256, (1, 30), (1, 3), 16, 4, 64, seed=2025,
+                 docs=(((0, 2, 4, 6, 8), 512), ((2, 6), 300), ((1, 9), 700))),
+        Workload("tree_fp8", 14, 256, (1, 40), (1, 3), 8, 2, 128, seed=2026,
+                 docs=(((0, 2, 4, 6, 8, 10, 12), 512), ((2, 6, 10), 512), ((6, 10), 256), ((1, 13), 300)),
+                 kv_dtype="fp8", k_scale=0.25, v_scale=0.125),
+        # every request in a group, interleaved halves
+        Workload("tree_all_grouped", 8, 256, (1, 20), (1, 1), 8, 2, 128, seed=2027,
+                 docs=(((0, 2, 4, 6), 512), ((1, 3, 5, 7), 512), ((2, 6), 256), ((1, 5), 512))),
     ]
 }
 
@@ -74,8 +88,8 @@ def test_small_full_parity(name, mode):
     out, lse, info = run(DeviceBatch(b), mode=mode)
     log(f"  plan: cascade={info['use_cascade']} P_c={info['common_prefix_len']} "
         f"psplit={info['prefix_splits']} groups={info['num_level1_groups']}x{info['level1_splits']} "
-        f"schunks={info['suffix_chunks']}")
-    if mode == "on" and SMALL[name].groups:
+        f"levels={info['shared_levels']} schunks={info['suffix_chunks']}")
+    if mode == "on" and (SMALL[name].groups or SMALL[name].docs):
         assert info["num_level1_groups"] > 0
     assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}")
 
@@ -358,3 +372,22 @@ def test_long_prefill_chunks(mode):
         f"row tile={info['prefix_row_tile']} schunks={info['suffix_chunks']}")
     assert info["use_cascade"] == (1 if mode == "on" else 0)
     assert_close(out, lse, ref_o, ref_l, what=f"long_prefill/{mode}")
+
+
+TREE_LEVELS = {"tree_decode": 4, "tree_prefill": 3, "tree_d64": 3, "tree_fp8": 4, "tree_all_grouped": 3}
+
+
+@pytest.mark.parametrize("separate", [0, 1])
+@pytest.mark.parametrize("name", list(TREE_LEVELS))
+def test_tree_levels_every_depth(name, separate):
+    """The same batch with 1 to 4 shared levels allowed (fewer levels: a
+    request's positions past its innermost kept group are its own), one
+    launch or one launch per role: every row against the oracle."""
+    b = workloads.make_batch(SMALL[name])
+    ref_o, ref_l = oracle_ref(b)
+    db = DeviceBatch(b)
+    for levels in (1, 2, 3, 4):
+        log(f"[tree] {name} max_levels={levels} separate={separate}")
+        out, lse, info = run(db, mode="on", max_levels=levels, separate_phases=separate)
+        assert info["shared_levels"] == min(levels, TREE_LEVELS[name])
+        assert_close(out, lse, ref_o, ref_l, what=f"{name}/levels{levels}/sep{separate}")
