@@ -128,8 +128,8 @@ def attention_full(q, k_cache, v_cache, block_table, query_start_loc, seq_lens,
 
     This is the plain definition the cascade path must reproduce ([p2]
     section 1: equivalent to standard attention; section 8 Step 4: the
-    standard path is one varlen attention over the full block tables; [p1]:
-    the option "does not change the mathematical correctness").
+    standard path is one varlen attention over the full block tables; [p1]
+    states that the option leaves results mathematically unchanged).
 
     q [T, Hq, d]; k_cache, v_cache [num_pages, page_size, Hkv, d];
     block_table [N, stride]; query_start_loc [N+1]; seq_lens [N].
