@@ -500,9 +500,10 @@ __device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const ItemEnd
 // WIN: the item may apply a sliding window and attention sinks (the
 // stand-alone kernel; the cascade launch has neither).
 // PM: the role (prefix_mode) when fixed at compile time, -1: a.prefix_mode.
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN, int PM = -1>
+// smem: the work-group's LDS array (its size is checked against the shape's).
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN, int PM = -1, size_t NB = 0>
 __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const ReqOrder& ro, const int bid,
-                                          uint8_t* smem, ItemEnd& end) {
+                                          uint8_t (&smem)[NB], ItemEnd& end) {
   end.wrote = 0;
   const int pmode = PM >= 0 ? PM : a.prefix_mode;
   constexpr int W = RW * KG;              // waves per work-group
@@ -529,6 +530,7 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   constexpr int ROWB = D * ESZ;           // LDS bytes per key row
   constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
   using SM = TileSmem<D, NS, SK, ESZ>;
+  static_assert(NB >= (size_t)SM::BYTES, "LDS array smaller than the shape's layout");
   // The key-group states are combined in the stage buffer just consumed
   // (bf16); fp8 stages are too small for that, so fp8 items run one head
   // and combine at the item's end, when no DMA is in flight, from LDS 0.
