@@ -198,9 +198,39 @@ def summarize_pmc(fetch_dir, write_dir, workload, steps):
 
 # Batch shapes of the decision sweep: decode batches (one query token) over
 # request counts, shared-prefix lengths and suffix lengths around the gates
-# (256 tokens, 8 requests) and far from them, plus chunked-prefill batches.
+# (256 tokens, 8 requests) and far from them, plus chunked-prefill batches
+# (32 / 8 heads, head_dim 128, bf16); then decode batches with 64 / 8 heads,
+# with head_dim 64, with fp8 e4m3 caches, and with two interleaved documents
+# shared by the even and the odd requests after the prefix.
 SWEEP_DECODE = [(n, p, s) for n in (2, 4, 8, 16, 64, 256) for p in (256, 1024, 4096, 16384) for s in (16, 512)]
 SWEEP_PREFILL = [(n, p) for n in (8, 32, 128) for p in (256, 2048)]
+SWEEP_WIDE = ([("h64", n, p, s) for n in (4, 16, 64, 256) for p in (1024, 8192) for s in (16, 512)] +
+              [("d64", n, p, s) for n in (4, 16, 64) for p in (256, 4096) for s in (16, 512)] +
+              [("fp8", n, p, s) for n in (4, 16, 64) for p in (1024, 4096) for s in (16, 512)] +
+              [("docs", n, p, s) for n in (8, 32) for p in (256, 1024) for s in (16, 256)])
+
+
+def sweep_workloads():
+    """The decision sweep's batch shapes, as workloads (seed 7)."""
+    import workloads
+    W = workloads.Workload
+    cases = [W(name=f"decode_n{n}_p{p}_s{sl}", num_reqs=n, prefix=p, suffix=(sl, sl), q_len=(1, 1),
+               num_q_heads=32, num_kv_heads=8, head_dim=128, seed=7) for n, p, sl in SWEEP_DECODE]
+    cases += [W(name=f"prefill_n{n}_p{p}", num_reqs=n, prefix=p, suffix=(64, 512), q_len=(1, 64),
+                num_q_heads=32, num_kv_heads=8, head_dim=128, seed=7) for n, p in SWEEP_PREFILL]
+    for fam, n, p, sl in SWEEP_WIDE:
+        kw = dict(num_reqs=n, prefix=p, suffix=(sl, sl), q_len=(1, 1), num_q_heads=32, num_kv_heads=8,
+                  head_dim=128, seed=7)
+        if fam == "h64":
+            kw["num_q_heads"] = 64
+        elif fam == "d64":
+            kw["head_dim"] = 64
+        elif fam == "fp8":
+            kw.update(kv_dtype="fp8", k_scale=0.125, v_scale=0.0625)
+        else:
+            kw["docs"] = ((tuple(range(0, n, 2)), 1024), (tuple(range(1, n, 2)), 2048))
+        cases.append(W(name=f"{fam}_n{n}_p{p}_s{sl}", **kw))
+    return cases
 
 
 def decision_sweep(steps, warmup):
@@ -214,16 +244,10 @@ def decision_sweep(steps, warmup):
     import shared_prefix_attention_amd as spa
 
     dev = torch.device("cuda:0")
-    cases = [workloads.Workload(name=f"decode_n{n}_p{p}_s{sl}", num_reqs=n, prefix=p, suffix=(sl, sl), q_len=(1, 1),
-                                num_q_heads=32, num_kv_heads=8, head_dim=128, seed=7)
-             for n, p, sl in SWEEP_DECODE]
-    cases += [workloads.Workload(name=f"prefill_n{n}_p{p}", num_reqs=n, prefix=p, suffix=(64, 512), q_len=(1, 64),
-                                 num_q_heads=32, num_kv_heads=8, head_dim=128, seed=7)
-              for n, p in SWEEP_PREFILL]
     recs = []
-    for w in cases:
+    for w in sweep_workloads():
         b = workloads.make_batch(w)
-        touched = (b.k_cache.numel() + b.v_cache.numel() + b.q.numel()) * 2
+        touched = b.k_cache.numel() * b.k_cache.element_size() * 2 + b.q.numel() * 2
         rotate = int(min(32, max(2, math.ceil((1 << 30) / max(touched, 1)))))
         copies = [(b.q.to(dev), b.k_cache.to(dev), b.v_cache.to(dev)) for _ in range(rotate)]
         bt, qsl, sl = b.block_table.to(dev), b.query_start_loc.to(dev), b.seq_lens.to(dev)
@@ -233,7 +257,8 @@ def decision_sweep(steps, warmup):
         for mode in ("auto", "on", "off"):
             pl = spa.plan_batch(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                                 k_cache=b.k_cache, block_table=b.block_table, query_start_loc=b.query_start_loc,
-                                seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode)
+                                seq_lens=b.seq_lens, num_computed_tokens=b.num_computed, mode=mode,
+                                kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
             ws = torch.zeros(max(pl.workspace_bytes, 256), dtype=torch.uint8, device=dev)
 
             def f(i, pl=pl, ws=ws):
@@ -252,7 +277,10 @@ def decision_sweep(steps, warmup):
         best = min(times["on"], times["off"])
         chosen = times["on"] if casc else times["off"]
         rec = {"case": w.name, "num_reqs": w.num_reqs, "prefix": w.prefix, "suffix": list(w.suffix),
-               "q_len": list(w.q_len), "gates_pass": infos["auto"]["gates_pass"], "auto_cascade": int(casc),
+               "q_len": list(w.q_len), "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+               "head_dim": w.head_dim, "kv_dtype": w.kv_dtype, "docs": len(w.docs),
+               "levels": infos["on"]["shared_levels"],
+               "gates_pass": infos["auto"]["gates_pass"], "auto_cascade": int(casc),
                "cascade_us": round(times["on"], 2), "noncascade_us": round(times["off"], 2),
                "auto_us": round(times["auto"], 2), "chosen_over_best": round(chosen / best, 3),
                "faster": "cascade" if times["on"] < times["off"] else "non-cascade",

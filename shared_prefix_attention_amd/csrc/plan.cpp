@@ -564,6 +564,17 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
   const CostModel cm;
   const double bpt = 2.0 * pl->kv_bytes() * pl->hkv * pl->d;
 
+  // The prefix tree below the batch-wide prefix (requests of a batch larger
+  // than the tree-order table get none): the nested levels of the cascade
+  // path, and positions the non-cascade path reads several times.
+  std::vector<TreeCand> all_groups;
+  if (plen > 0 && n <= kOrderCapacity) {
+    std::vector<int32_t> all(n);
+    for (int32_t r = 0; r < n; ++r) all[r] = r;
+    tree_visit(bt, stride, seq_lens, qsl, ps, all, (int32_t)plen, 0, -1, kMaxShared, all_groups);
+  }
+  pl->cand_groups = (int32_t)all_groups.size();   // part of the shape, whether used or not
+
   // Non-cascade estimate: every request streams its whole sequence; the
   // shared pages are fetched from HBM once and re-read from cache by the
   // other requests when they fit in it.
@@ -598,9 +609,18 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
       const double m_us = nc_merge(nc, &il);
       if (items_us(direct) <= items_us(nc) + m_us - cm.merge_floor_us + cm.merge_trip_us) nc = direct;
     }
-    const double shared_bytes = bpt * plen;
-    const double reread = shared_bytes * (n - 1);
-    int64_t hbm_tokens = pl->kv_tokens_cascade;
+    // positions shared by several requests (the prefix, the nested groups'
+    // documents): one copy of each comes from HBM, the rest are re-reads.
+    // The re-reads go at a rate of elements (the items' per-element work
+    // bounds it), so fp8 caches count as bf16 there.
+    int64_t shared_tokens = plen, reread_tokens = plen * (int64_t)(n - 1);
+    for (const TreeCand& g : all_groups) {
+      shared_tokens += g.len - g.parent_len;
+      reread_tokens += (int64_t)(g.members.size() - 1) * (g.len - g.parent_len);
+    }
+    const double shared_bytes = bpt * shared_tokens;
+    const double reread = (double)(2 * 2 * pl->hkv * pl->d) * reread_tokens;
+    int64_t hbm_tokens = sum_seq - reread_tokens;
     double extra = 0.0;
     if (shared_bytes <= cm.mall_bytes) extra = reread;
     else hbm_tokens = sum_seq;
@@ -635,16 +655,10 @@ extern "C" ca_status_t cascade_attn_plan(const ca_params_t* prm, const int32_t* 
       pre.splits = (int32_t)cdiv(ntiles, tiles_per);
       pre.split_tokens = (int32_t)(tiles_per * kTileKeys);
     }
-    // nested levels: the prefix tree below the batch-wide prefix (requests
-    // of a batch larger than the tree-order table run without them)
+    // nested levels kept by the plan: at most max_levels - 1 below the
+    // batch-wide prefix, at most kMaxTreeGroups groups
     const int32_t max_levels = p.max_levels == 0 ? kMaxShared : p.max_levels;
-    std::vector<TreeCand> groups;
-    if (n <= kOrderCapacity) {
-      std::vector<int32_t> all(n);
-      for (int32_t r = 0; r < n; ++r) all[r] = r;
-      tree_visit(bt, stride, seq_lens, qsl, ps, all, (int32_t)plen, 0, -1, kMaxShared, groups);
-    }
-    pl->cand_groups = (int32_t)groups.size();   // part of the shape, whether used or not
+    std::vector<TreeCand> groups = all_groups;
     if (max_levels < kMaxShared) {   // keep the shallower levels (children follow their parents)
       std::vector<TreeCand> kept;
       std::vector<int32_t> remap(groups.size(), -1);

@@ -336,9 +336,10 @@ def test_auto_takes_the_measured_faster_path():
         assert _plan(b, mode="auto").info["use_cascade"] == casc, name
 
 
-# Shapes of the device decision sweep (32 / 8 heads, head_dim 128, seed 7)
-# where one path measured clearly faster (by 15 % or more; µs per step,
-# cascade / non-cascade): (name, N, P, suffix range, query range, cascade?)
+# Shapes of the device decision sweep (seed 7; decode shapes one query
+# token) where one path measured clearly faster (by 15 % or more; µs per
+# step, cascade / non-cascade): (name, N, P, suffix range, query range,
+# cascade?). 32 / 8 heads, head_dim 128, bf16:
 SWEEP_CLEAR = [
     ("decode_n2_p256_s16", 2, 256, (16, 16), (1, 1), 0),          # 16.9 / 11.3
     ("decode_n2_p4096_s16", 2, 4096, (16, 16), (1, 1), 1),        # 14.8 / 20.4
@@ -355,6 +356,26 @@ SWEEP_CLEAR = [
     ("prefill_n128_p256", 128, 256, (64, 512), (1, 64), 0),       # 166.6 / 140.5
 ]
 
+# The wider families (decode, one query token): 64 / 8 heads; head_dim 64;
+# fp8 e4m3 caches; two interleaved documents (1024 tokens for the even
+# requests, 2048 for the odd ones) after the prefix. (name, family, N, P, S,
+# cascade?)
+SWEEP_CLEAR_WIDE = [
+    ("h64_n4_p1024_s512", "h64", 4, 1024, 512, 1),       # 15.1 / 21.6
+    ("h64_n16_p8192_s16", "h64", 16, 8192, 16, 1),       # 22.6 / 44.4
+    ("h64_n64_p1024_s16", "h64", 64, 1024, 16, 1),       # 20.6 / 24.3
+    ("h64_n256_p8192_s512", "h64", 256, 8192, 512, 1),   # 155.1 / 523.4
+    ("d64_n4_p4096_s512", "d64", 4, 4096, 512, 1),       # 13.8 / 17.2
+    ("d64_n16_p4096_s16", "d64", 16, 4096, 16, 1),       # 13.6 / 22.6
+    ("d64_n64_p4096_s512", "d64", 64, 4096, 512, 1),     # 26.6 / 60.2
+    ("fp8_n4_p4096_s16", "fp8", 4, 4096, 16, 1),         # 13.8 / 17.9
+    ("fp8_n16_p4096_s512", "fp8", 16, 4096, 512, 1),     # 21.1 / 28.0
+    ("fp8_n64_p1024_s16", "fp8", 64, 1024, 16, 1),       # 18.4 / 21.9
+    ("fp8_n64_p4096_s16", "fp8", 64, 4096, 16, 1),       # 23.1 / 59.2
+    ("docs_n32_p256_s16", "docs", 32, 256, 16, 1),       # 22.2 / 30.3
+    ("docs_n32_p1024_s256", "docs", 32, 1024, 256, 1),   # 26.8 / 38.4
+]
+
 
 @pytest.mark.parametrize("name,n,p,s,q,casc", SWEEP_CLEAR, ids=[c[0] for c in SWEEP_CLEAR])
 def test_auto_matches_the_decision_sweep(name, n, p, s, q, casc):
@@ -367,6 +388,26 @@ def test_auto_matches_the_decision_sweep(name, n, p, s, q, casc):
     info = _plan(workloads.make_batch(w), mode="auto").info
     assert info["gates_pass"] == int(n >= 8)
     assert info["use_cascade"] == casc, (info["est_us_cascade"], info["est_us_noncascade"])
+
+
+@pytest.mark.parametrize("name,fam,n,p,s,casc", SWEEP_CLEAR_WIDE, ids=[c[0] for c in SWEEP_CLEAR_WIDE])
+def test_auto_matches_the_wider_decision_sweep(name, fam, n, p, s, casc):
+    kw = dict(num_reqs=n, prefix=p, suffix=(s, s), q_len=(1, 1), num_q_heads=32, num_kv_heads=8, head_dim=128,
+              seed=7)
+    if fam == "h64":
+        kw["num_q_heads"] = 64
+    elif fam == "d64":
+        kw["head_dim"] = 64
+    elif fam == "fp8":
+        kw.update(kv_dtype="fp8", k_scale=0.125, v_scale=0.0625)
+    else:
+        kw["docs"] = ((tuple(range(0, n, 2)), 1024), (tuple(range(1, n, 2)), 2048))
+    w = workloads.Workload(name=name, **kw)
+    b = workloads.make_batch(w)
+    info = _plan(b, mode="auto").info
+    assert info["use_cascade"] == casc, (info["est_us_cascade"], info["est_us_noncascade"])
+    if fam == "docs":
+        assert info["shared_levels"] == 2 and info["num_level1_groups"] == 2
 
 
 def _tree_of(pl):
