@@ -310,6 +310,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-noncascade", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm-cache (no rotation) loop")
     ap.add_argument("--max-levels", type=int, default=0, help="shared levels of the cascade plan (0 = default)")
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--probe-separate", action="store_true")
@@ -426,7 +427,7 @@ def main():
             "traffic": None if traffic is None else round(traffic)}
 
     # warm-cache number (no rotation) and the GPU non-cascade path
-    ms_warm = time_steps(step, args.steps, 1)
+    ms_warm = None if args.no_warm else time_steps(step, args.steps, 1)
     extra = {}
     if not args.no_noncascade and casc:
         plan_off = make_plan("off")
@@ -512,7 +513,7 @@ def main():
         "roofline": roof,
         "kernels": kern,
         "us_per_step_with_kernel_events": round(ms_events * 1e3, 3),
-        "warm_us_per_step": round(ms_warm * 1e3, 3),
+        "warm_us_per_step": None if ms_warm is None else round(ms_warm * 1e3, 3),
         "plan": {k: info[k] for k in ("prefix_splits", "prefix_row_tile", "num_level1_groups", "level1_splits",
                                        "suffix_chunks", "suffix_chunk_tokens", "suffix_kernel", "num_partial_slots",
                                        "workspace_bytes")},
