@@ -68,6 +68,16 @@ def check_resource_usage(remarks: str) -> list:
     if bad:
         raise RuntimeError("kernels use scratch memory or spill VGPRs (the inline-asm LDS reads rely on "
                            "neither): " + "; ".join(f"{k['name']}: {k}" for k in bad))
+    # The attention work-groups are 4 waves; the single cascade launch holds
+    # two per CU (an MFMA-bound prefix item beside a bandwidth-bound suffix
+    # item), so every attention kernel whose LDS leaves room for two must fit
+    # two in registers as well (2 waves per SIMD).
+    low = [k for k in kernels if ("attn_tile_kernel" in k["name"] or "cascade_phases_kernel" in k["name"])
+           and int(k.get("LDS Size [bytes/block]", "0")) <= 80 * 1024
+           and int(k.get("Occupancy [waves/SIMD]", "0")) < 2]
+    if low:
+        raise RuntimeError("attention kernels below two work-groups per CU: " +
+                           "; ".join(f"{k['name']}: {k}" for k in low))
     return kernels
 
 

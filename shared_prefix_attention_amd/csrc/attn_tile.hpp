@@ -51,6 +51,8 @@
 // need no mask skip it.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "merge.hpp"
 
@@ -160,6 +162,13 @@ struct GroupTable {
   int32_t pos_cum[kMaxTreeOrder + 1];
   uint8_t deepest[kMaxTreeOrder];          // [request]: innermost group, 0xff: none
 };
+
+// Kernels of plans without nested levels take an empty struct in place of
+// the group table: every launch copies its argument block, so a smaller one
+// costs less host time per launch.
+struct NoGroupTable {};
+template <bool TREE>
+using GroupTableArg = std::conditional_t<TREE, GroupTable, NoGroupTable>;
 
 // Query token of group-local token t of group j (its members' tokens in tree
 // order): the position p holding it, then the token within p's request.
@@ -501,9 +510,12 @@ __device__ __forceinline__ void merge_tail(const MergeTailArgs& a, const ItemEnd
 // stand-alone kernel; the cascade launch has neither).
 // PM: the role (prefix_mode) when fixed at compile time, -1: a.prefix_mode.
 // smem: the work-group's LDS array (its size is checked against the shape's).
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN, int PM = -1, size_t NB = 0>
-__device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& gt, const ReqOrder& ro, const int bid,
+// GT: GroupTable, or NoGroupTable for plans without nested levels.
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool WIN, int PM = -1, size_t NB = 0,
+          typename GT = GroupTable>
+__device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const ReqOrder& ro, const int bid,
                                           uint8_t (&smem)[NB], ItemEnd& end) {
+  constexpr bool TREE = std::is_same<GT, GroupTable>::value;
   end.wrote = 0;
   const int pmode = PM >= 0 ? PM : a.prefix_mode;
   constexpr int W = RW * KG;              // waves per work-group
@@ -563,20 +575,22 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   if (pmode) {
     int local = bid, splits = a.splits;
     key_begin = a.key_start;
-    if (pmode == 2) {
-      // nested level: find the group whose items contain bid
-      int lo = 0, hi = gt.n - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (gt.item_begin[mid] <= bid) lo = mid;
-        else hi = mid - 1;
+    if constexpr (TREE) {
+      if (pmode == 2) {
+        // nested level: find the group whose items contain bid
+        int lo = 0, hi = gt.n - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (gt.item_begin[mid] <= bid) lo = mid;
+          else hi = mid - 1;
+        }
+        grp = lo;
+        local = bid - gt.item_begin[grp];
+        split_tokens = gt.split_tokens[grp];
+        splits = gt.level_splits[gt.level[grp]];
+        req = gt.first_req[grp];
+        key_begin = gt.key_begin[grp];
       }
-      grp = lo;
-      local = bid - gt.item_begin[grp];
-      split_tokens = gt.split_tokens[grp];
-      splits = gt.level_splits[gt.level[grp]];
-      req = gt.first_req[grp];
-      key_begin = gt.key_begin[grp];
     }
     const int kv_items = a.hkv * splits;
     mt = local / kv_items;
@@ -595,8 +609,12 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     g0 = (rest % groups) * H;
     req = ro.n > 0 ? ro.req[rest / groups] : rest / groups;
     // a request in a group starts after its innermost group's shared positions
-    grp = (gt.n > 0 && gt.deepest[req] != 0xff) ? gt.deepest[req] : -1;
-    key_begin = (grp >= 0 ? gt.key_end[grp] : a.key_start) + c * split_tokens;
+    key_begin = a.key_start;
+    if constexpr (TREE) {
+      grp = (gt.n > 0 && gt.deepest[req] != 0xff) ? gt.deepest[req] : -1;
+      if (grp >= 0) key_begin = gt.key_end[grp];
+    }
+    key_begin += c * split_tokens;
     causal = true;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
   }
@@ -610,14 +628,19 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     pg_reg[k] = i < item_pages ? bt_row[min(first_page + i, a.bt_stride - 1)] : 0;
   }
   row_begin = mt * ROWS;
-  slot = (pmode == 2 ? gt.level_slot_base[gt.level[grp]] : a.slot_base) + c;
+  slot = a.slot_base + c;
   if (pmode == 1) {
     row_end = min(row_begin + ROWS, a.total_rows);
     key_end = min(key_begin + split_tokens, a.prefix_len);
   } else if (pmode == 2) {
-    row_end = min(row_begin + ROWS, gt.rows[grp]);
-    if (row_begin >= row_end) return;   // uniform across the work-group
-    key_end = max(key_begin, min(key_begin + split_tokens, gt.key_end[grp]));
+    if constexpr (TREE) {
+      slot = gt.level_slot_base[gt.level[grp]] + c;
+      row_end = min(row_begin + ROWS, gt.rows[grp]);
+      if (row_begin >= row_end) return;   // uniform across the work-group
+      key_end = max(key_begin, min(key_begin + split_tokens, gt.key_end[grp]));
+    } else {
+      return;   // no nested levels in this launch
+    }
   } else {
     const int q0 = a.qsl[req];
     const int q_len = a.qsl[req + 1] - q0;
@@ -639,10 +662,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     // levels deeper than the request's innermost group hold no state for
     // its rows: mark those partial slots (contiguous, the last levels')
     // empty, weight 0 in the merge
-    const int lv = grp >= 0 ? gt.level[grp] + 1 : 1;
-    const int e_lo = lv < gt.levels ? gt.level_slot_base[lv] : 0;
-    const int n_empty =
-        lv < gt.levels ? gt.level_slot_base[gt.levels - 1] + gt.level_splits[gt.levels - 1] - e_lo : 0;
+    int e_lo = 0, n_empty = 0;
+    if constexpr (TREE) {
+      const int lv = grp >= 0 ? gt.level[grp] + 1 : 1;
+      if (lv < gt.levels) {
+        e_lo = gt.level_slot_base[lv];
+        n_empty = gt.level_slot_base[gt.levels - 1] + gt.level_splits[gt.levels - 1] - e_lo;
+      }
+    }
     if (c == 0 && n_empty > 0) {
       const int nrows = row_end - row_begin;
       for (int e = tid; e < nrows * H * n_empty; e += NT) {
@@ -681,8 +708,10 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
     row_ok[rb] = m < row_end;
     const int t_in = m / a.group;
     row_j[rb] = m - t_in * a.group;
+    row_tok[rb] = tok_base + t_in;
     // nested level: packed rows are the group members' tokens in tree order
-    row_tok[rb] = pmode == 2 ? (row_ok[rb] ? group_token(gt, grp, t_in) : 0) : tok_base + t_in;
+    if constexpr (TREE)
+      if (pmode == 2) row_tok[rb] = row_ok[rb] ? group_token(gt, grp, t_in) : 0;
     row_qpos[rb] = q_pos_base + t_in;
   }
   auto load_q = [&](int g, u32x4_t (&q)[RB][KC]) {
@@ -1226,9 +1255,13 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GroupTable& g
   }
 }
 
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8>
-__global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs a, const GroupTable gt,
-                                                                  const ReqOrder ro, const MergeTailArgs mt) {
+// 128-row items ask for two work-groups per CU explicitly: left alone, the
+// compiler gives them a few more registers than two allow.
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool TREE>
+__global__ __launch_bounds__(64 * RW * KG, RB == 2 ? 2 : 1) void attn_tile_kernel(const TileArgs a,
+                                                                                  const GroupTableArg<TREE> gt,
+                                                                                  const ReqOrder ro,
+                                                                                  const MergeTailArgs mt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
   ItemEnd end;
   attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, ro, blockIdx.x, smem, end);
@@ -1241,10 +1274,11 @@ __global__ __launch_bounds__(64 * RW * KG) void attn_tile_kernel(const TileArgs 
 // bandwidth-heavy suffix share the CUs. All write partial states. Each role
 // has its own pipeline shape (stages x keys per stage) inside one LDS
 // allocation, sized so that two work-groups fit on a CU.
-template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK, bool F8>
+template <int D, int PRB, int PRW, int PKG, int PNS, int PSK, int SRB, int SRW, int SKG, int SNS, int SSK, bool F8,
+          bool TREE>
 __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, const TileArgs ga, const TileArgs sa,
                                                              const int n_prefix, const int n_group,
-                                                             const GroupTable gt, const ReqOrder ro,
+                                                             const GroupTableArg<TREE> gt, const ReqOrder ro,
                                                              const MergeTailArgs mt) {
   static_assert(PRW * PKG == 4 && SRW * SKG == 4, "both roles use 4 waves");
   constexpr int ESZ = F8 ? 1 : 2;
@@ -1253,7 +1287,7 @@ __global__ __launch_bounds__(256) void cascade_phases_kernel(const TileArgs pa, 
   const int bid = blockIdx.x;
   ItemEnd end;
   if (bid < n_prefix) attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false, 1>(pa, gt, ro, bid, smem, end);
-  else if (bid < n_prefix + n_group)
+  else if (TREE && bid < n_prefix + n_group)
     attn_item<D, PRB, PRW, PKG, PNS, PSK, false, F8, false, 2>(ga, gt, ro, bid - n_prefix, smem, end);
   else
     attn_item<D, SRB, SRW, SKG, SNS, SSK, (SKG > 1) && !F8, F8, false, 0>(sa, gt, ro, bid - n_prefix - n_group,

@@ -88,8 +88,13 @@ ca_status_t check_launch(const char* what) {
 template <int D, int RB, int RW, int KG, int NS, bool F8>
 void launch_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt, int grid,
                  hipStream_t s, int kind) {
-  launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, (KG > 1) && !F8, F8>, dim3(grid), dim3(64 * RW * KG), s, args,
-         gt, ro, mt);
+  constexpr bool MH = (KG > 1) && !F8;
+  if (gt.n > 0)
+    launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, MH, F8, true>, dim3(grid), dim3(64 * RW * KG), s, args, gt,
+           ro, mt);
+  else
+    launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, MH, F8, false>, dim3(grid), dim3(64 * RW * KG), s, args,
+           NoGroupTable{}, ro, mt);
 }
 
 // bf16 caches: 2 or 4 stages of 64 keys; fp8 caches (head_dim 128 only):
@@ -142,8 +147,12 @@ void launch_phases(const TileArgs& pa, const TileArgs& ga, const TileArgs& sa, i
   constexpr int PRB = P == 1 ? 2 : 1;
   constexpr int SRW = S == 2 ? 1 : 4, SKG = S == 2 ? 4 : 1;
   constexpr int NS = F8 ? 4 : 2;
-  launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, NS, 64, 1, SRW, SKG, NS, 64, F8>, dim3(grid), dim3(256), s,
-         pa, ga, sa, n_prefix, n_group, gt, ro, mt);
+  if (gt.n > 0)
+    launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, NS, 64, 1, SRW, SKG, NS, 64, F8, true>, dim3(grid),
+           dim3(256), s, pa, ga, sa, n_prefix, n_group, gt, ro, mt);
+  else
+    launch(K_PHASES, cascade_phases_kernel<D, PRB, 4, 1, NS, 64, 1, SRW, SKG, NS, 64, F8, false>, dim3(grid),
+           dim3(256), s, pa, ga, sa, n_prefix, 0, NoGroupTable{}, ro, mt);
 }
 
 template <int D, bool F8>

@@ -14,10 +14,12 @@ from shared_prefix_attention_amd import lds_wait_check as L
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _remarks(scratch="0", vspill="0", sspill="0"):
+def _remarks(scratch="0", vspill="0", sspill="0", name="kern_a", occupancy="2", lds="67584"):
     return "\n".join([
-        "x.hpp:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        f"x.hpp:1:1: remark: Function Name: {name} [-Rpass-analysis=kernel-resource-usage]",
         "x.hpp:1:1: remark:     VGPRs: 100 [-Rpass-analysis=kernel-resource-usage]",
+        f"x.hpp:1:1: remark:     Occupancy [waves/SIMD]: {occupancy} [-Rpass-analysis=kernel-resource-usage]",
+        f"x.hpp:1:1: remark:     LDS Size [bytes/block]: {lds} [-Rpass-analysis=kernel-resource-usage]",
         f"x.hpp:1:1: remark:     ScratchSize [bytes/lane]: {scratch} [-Rpass-analysis=kernel-resource-usage]",
         f"x.hpp:1:1: remark:     SGPRs Spill: {sspill} [-Rpass-analysis=kernel-resource-usage]",
         f"x.hpp:1:1: remark:     VGPRs Spill: {vspill} [-Rpass-analysis=kernel-resource-usage]",
@@ -34,6 +36,18 @@ def test_resource_gate():
         B.check_resource_usage(_remarks(vspill="4"))
     with pytest.raises(RuntimeError):
         B.check_resource_usage("no remarks at all")
+
+
+def test_attention_kernels_keep_two_work_groups_per_cu():
+    """An attention kernel whose LDS leaves room for two work-groups per CU
+    must fit two in registers too; other kernels, and attention kernels
+    whose LDS holds one, are not held to it."""
+    att = "_ZN2ca21cascade_phases_kernelILi128E"
+    assert B.check_resource_usage(_remarks(name=att, occupancy="2"))
+    with pytest.raises(RuntimeError):
+        B.check_resource_usage(_remarks(name=att, occupancy="1"))
+    assert B.check_resource_usage(_remarks(name=att, occupancy="1", lds="133120"))
+    assert B.check_resource_usage(_remarks(name="kern_a", occupancy="1"))
 
 
 def _asm(body):
