@@ -170,6 +170,20 @@ struct NoGroupTable {};
 template <bool TREE>
 using GroupTableArg = std::conditional_t<TREE, GroupTable, NoGroupTable>;
 
+// Group-table fields used by the per-request and nested-level items; the
+// empty table of plans without nested levels answers as a table with no
+// groups (its values are never used).
+__device__ __forceinline__ int gt_deepest(const GroupTable& gt, int r) {
+  return (gt.n > 0 && gt.deepest[r] != 0xff) ? gt.deepest[r] : -1;
+}
+__device__ __forceinline__ int gt_deepest(const NoGroupTable&, int) { return -1; }
+__device__ __forceinline__ int gt_key_end(const GroupTable& gt, int j) { return gt.key_end[j]; }
+__device__ __forceinline__ int gt_key_end(const NoGroupTable&, int) { return 0; }
+__device__ __forceinline__ int gt_rows(const GroupTable& gt, int j) { return gt.rows[j]; }
+__device__ __forceinline__ int gt_rows(const NoGroupTable&, int) { return 0; }
+__device__ __forceinline__ int gt_slot_base(const GroupTable& gt, int j) { return gt.level_slot_base[gt.level[j]]; }
+__device__ __forceinline__ int gt_slot_base(const NoGroupTable&, int) { return 0; }
+
 // Query token of group-local token t of group j (its members' tokens in tree
 // order): the position p holding it, then the token within p's request.
 __device__ __forceinline__ int group_token(const GroupTable& gt, int j, int t) {
@@ -609,12 +623,8 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
     g0 = (rest % groups) * H;
     req = ro.n > 0 ? ro.req[rest / groups] : rest / groups;
     // a request in a group starts after its innermost group's shared positions
-    key_begin = a.key_start;
-    if constexpr (TREE) {
-      grp = (gt.n > 0 && gt.deepest[req] != 0xff) ? gt.deepest[req] : -1;
-      if (grp >= 0) key_begin = gt.key_end[grp];
-    }
-    key_begin += c * split_tokens;
+    grp = gt_deepest(gt, req);
+    key_begin = (grp >= 0 ? gt_key_end(gt, grp) : a.key_start) + c * split_tokens;
     causal = true;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
   }
@@ -628,19 +638,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
     pg_reg[k] = i < item_pages ? bt_row[min(first_page + i, a.bt_stride - 1)] : 0;
   }
   row_begin = mt * ROWS;
-  slot = a.slot_base + c;
+  slot = (pmode == 2 ? gt_slot_base(gt, grp) : a.slot_base) + c;
   if (pmode == 1) {
     row_end = min(row_begin + ROWS, a.total_rows);
     key_end = min(key_begin + split_tokens, a.prefix_len);
-  } else if (pmode == 2) {
-    if constexpr (TREE) {
-      slot = gt.level_slot_base[gt.level[grp]] + c;
-      row_end = min(row_begin + ROWS, gt.rows[grp]);
-      if (row_begin >= row_end) return;   // uniform across the work-group
-      key_end = max(key_begin, min(key_begin + split_tokens, gt.key_end[grp]));
-    } else {
-      return;   // no nested levels in this launch
-    }
+  } else if (pmode == 2) {   // (only with a group table)
+    row_end = min(row_begin + ROWS, gt_rows(gt, grp));
+    if (row_begin >= row_end) return;   // uniform across the work-group
+    key_end = max(key_begin, min(key_begin + split_tokens, gt_key_end(gt, grp)));
   } else {
     const int q0 = a.qsl[req];
     const int q_len = a.qsl[req + 1] - q0;
@@ -883,6 +888,12 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
   const int U = H * n_tiles;
   const int pro = min(NS, U);
   for (int p = 0; p < pro; ++p) issue_next();
+  // Q was requested before these stages, so it lands before the first of
+  // them. Passing it through an asm operand here makes the compiler put its
+  // wait for Q at this point: left to itself, it waits for Q at the products
+  // inside the stage loop, i.e. for every DMA in flight, at every stage.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) reg_fence(qf[rb]);
 
   // ------------------------------------------------- end of one KV head
   // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). Waves
@@ -1008,8 +1019,12 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
     return;
   }
 
-  int h = 0, t = 0;   // head and tile of stage u
-  for (int u = 0; u < U; ++u) {
+  // Stage u of the item is tile t of head h (u = h * n_tiles + t): an inner
+  // loop over a head's tiles, and each head's end (the key-group combine,
+  // the next head's Q) outside it.
+  int u = 0;
+  for (int h = 0; h < H; ++h) {
+  for (int t = 0; t < n_tiles; ++t, ++u) {
     // Shared buffers: the prologue filled NS buffers and iteration i >= 1
     // issued stage i + NS - 1, so stage u is followed by min(NS - 2, ...)
     // issued stages here (NS - 1 at u = 0).
@@ -1229,29 +1244,32 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
         }
       }
     }
-    if (t == n_tiles - 1) {
-      // last tile of head g0 + h: the next head's Q is requested first so
-      // that its latency overlaps the combine
-      u32x4_t qn[RB][KC];
-      const bool more = MH && h + 1 < H;
-      if (more) load_q(g0 + h + 1, qn);
-      finish_head(g0 + h, u % NS);
-      if (refill) {
-        block_barrier();   // every wave is past the combine in this buffer
-        issue_next();
-      }
-      if (more) {
+  }
+  // end of head g0 + h, whose last tile was stage u - 1: the next head's Q
+  // is requested first so that its latency overlaps the combine
+  {
+    const int ul = u - 1;
+    const bool refill = PRIV && ul + NS < U;
+    u32x4_t qn[RB][KC];
+    const bool more = MH && h + 1 < H;
+    if (more) load_q(g0 + h + 1, qn);
+    finish_head(g0 + h, ul % NS);
+    if (more) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) qf[rb][kc] = qn[rb][kc];
-        reset_state();
-      }
-      ++h;
-      t = 0;
-    } else {
-      ++t;
+        for (int kc = 0; kc < KC; ++kc) qf[rb][kc] = qn[rb][kc];
+      reset_state();
+      // the next head's Q has landed here (its wait is placed here, not in
+      // the stage loop)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) reg_fence(qf[rb]);
     }
+    if (refill) {
+      block_barrier();   // every wave is past the combine in this buffer
+      issue_next();
+    }
+  }
   }
 }
 

@@ -44,8 +44,12 @@ def test_run_twice_is_bitwise_identical(name):
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("name", ["worked_decode", "mixed_prefill"])
+@pytest.mark.parametrize("name", ["worked_decode", "mixed_prefill", "multi_doc", "multi_doc_prefill"])
 def test_request_permutation_is_bitwise_invariant(name):
+    """Shuffled requests give every request bitwise the same rows. For the
+    batches with documents the shuffle scatters each document's requests
+    over the batch, so the permuted plan's nested groups have members that
+    are not adjacent (the prefix tree puts them in its own order)."""
     log(f"[invariance] permutation {name}")
     b = workloads.make_batch(workloads.get(name))
     n = b.workload.num_reqs

@@ -114,7 +114,8 @@ def test_grouped_heads(name, heads, mode):
     assert_close(out, lse, ref_o, ref_l, what=f"{name}/{mode}/h{heads}")
 
 
-@pytest.mark.parametrize("name", ["decode_ragged", "prefill_mix", "d64_gqa", "fp8_decode", "fp8_prefill"])
+@pytest.mark.parametrize("name", ["decode_ragged", "prefill_mix", "d64_gqa", "fp8_decode", "fp8_prefill",
+                                  "tree_prefill", "tree_fp8"])
 def test_small_hnd_layout(name):
     log(f"[parity] {name} HND")
     b = workloads.make_batch(SMALL[name])

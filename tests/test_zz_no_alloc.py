@@ -45,6 +45,7 @@ SEQUENCES = [
     (("worked_decode", "on"), ("tiny_decode", "on")),
     (("mixed_prefill_capped", "on"), ("decode_ragged", "on")),
     (("long_doc", "auto"), ("decode_ragged", "off")),
+    (("multi_doc", "on"), ("decode_ragged", "on")),   # nested levels, then none
 ]
 
 SMALL = {
