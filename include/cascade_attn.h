@@ -328,7 +328,8 @@ ca_status_t cascade_attn_run_noalloc(ca_plan_t plan, const void* q, const void* 
  * non-cascade path and, when a prefix is shared and no window binds, the
  * cascade path with the planner's prefix split count, half and twice it,
  * one, two or the planner's KV heads per decode item, and (if the batch has
- * groups) one or two shared levels. Each candidate runs twice untimed and
+ * nested groups) every shared level the detector finds, the batch-wide prefix
+ * only, and two levels when it finds more. Each candidate runs twice untimed and
  * `iters` times between two HIP events on `stream`; candidates needing more
  * than workspace_bytes are skipped. Returns the fastest plan in *out_plan
  * (the caller destroys it) and its mean time per run in *out_us (may be
@@ -336,8 +337,8 @@ ca_status_t cascade_attn_run_noalloc(ca_plan_t plan, const void* q, const void* 
  * params->use_tuned = 1, no explicit overrides (prefix_splits,
  * heads_per_item, max_levels all 0) and the same shape apply it. A shape is (num_reqs, head counts, head_dim,
  * kv_dtype, window, and the power-of-two buckets of the shared prefix, total
- * queries, longest query, mean remaining length and second-level group
- * count). Synchronises the stream; not for graph capture. out, lse_out and
+ * queries, longest query, mean remaining length and nested-group count).
+ * Synchronises the stream; not for graph capture. out, lse_out and
  * workspace are overwritten (out / lse_out hold this batch's result).
  * Errors: as cascade_attn_plan and cascade_attn_run; CA_EINVAL for iters
  * outside [1, 1000]; CA_EWORKSPACE if no candidate fits the workspace.

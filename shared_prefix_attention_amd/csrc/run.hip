@@ -562,7 +562,7 @@ extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const in
   if (base->prefix_len > 0 && base->window == 0) {
     ca_params_t pp = base_p;
     pp.mode = CA_MODE_FORCE_ON;
-    pp.max_levels = 1;   // any explicit setting bypasses the table
+    pp.max_levels = 4;   // every nested level; any explicit setting bypasses the table
     ca_plan_t on = nullptr;
     st = cascade_attn_plan(&pp, block_table_h, query_start_loc_h, seq_lens_h, num_computed_tokens_h, &on);
     if (st != CA_OK) {
@@ -571,6 +571,7 @@ extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const in
     }
     const int32_t s0 = on->prefix.splits;
     const int32_t h0 = on->suffix.heads_per_item;
+    const int32_t lv0 = on->tree.n > 0 ? on->tree.levels : 1;
     // two heads per decode item is a candidate whenever the plan's items are
     // decode-shaped bf16 ones (fp8 plans run one head per item)
     const bool two_heads = on->suffix.kernel == 1 && !on->kv_fp8 && on->hkv % 2 == 0 && h0 != 2;
@@ -581,8 +582,11 @@ extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const in
     std::vector<int32_t> heads{0};
     if (h0 > 1) heads.push_back(1);
     if (two_heads) heads.push_back(2);
+    // shared levels: all the detector finds, the batch-wide prefix only,
+    // and two when it finds more
     std::vector<int32_t> levels{0};
-    if (base->cand_groups > 0) levels.push_back(1);
+    if (lv0 > 1) levels.push_back(1);
+    if (lv0 > 2) levels.push_back(2);
     for (int32_t sp : splits)
       for (int32_t hd : heads)
         for (int32_t lv : levels) cands.push_back({CA_MODE_FORCE_ON, sp, hd, lv});
@@ -603,7 +607,7 @@ extern "C" ca_status_t cascade_attn_autotune(const ca_params_t* params, const in
     cp.prefix_splits = c.prefix_splits;
     cp.heads_per_item = c.heads_per_item;
     // an explicit level count keeps the table out of the candidate's plan
-    cp.max_levels = c.max_levels > 0 ? c.max_levels : 2;
+    cp.max_levels = c.max_levels > 0 ? c.max_levels : 4;
     ca_plan_t cand = nullptr;
     if (cascade_attn_plan(&cp, block_table_h, query_start_loc_h, seq_lens_h, num_computed_tokens_h, &cand) != CA_OK)
       continue;
