@@ -2,7 +2,7 @@
 scratch, no spills) and the static check that every inline-asm LDS read of
 the attention kernels is waited for before its registers are touched. Each
 check is run on small hand-written inputs, with and without a planted
-mistake, and on this build's own output when it is there."""
+mistake, and on the compiled library's own assembly and resource report when they are there."""
 
 import os
 
