@@ -554,14 +554,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
   constexpr bool PRIV = RW == 1;
   static_assert(!PRIV || (KG == W && NKB == 1 && SK / W == 16), "per-wave pipelines need one 16-key block per wave");
   constexpr int ROWB = D * ESZ;           // LDS bytes per key row
-  constexpr int XS_ROW = D + 4;           // floats per row of a published wave state
   using SM = TileSmem<D, NS, SK, ESZ>;
   static_assert(NB >= (size_t)SM::BYTES, "LDS array smaller than the shape's layout");
   // The key-group states are combined in the stage buffer just consumed
   // (bf16); fp8 stages are too small for that, so fp8 items run one head
   // and combine at the item's end, when no DMA is in flight, from LDS 0.
   static_assert(!F8 || (D == 128 && !MH), "fp8 caches: head_dim 128, one head per item");
-  static_assert(KG == 1 || (KG - 1) * RW * 16 * RB * XS_ROW * 4 <= (F8 ? NS : 1) * SM::STAGE_BYTES, "merge scratch");
+  static_assert(KG == 1 || (DB % KG == 0 && KG * RW * 16 * RB * ((KG - 1) * (DB / KG) * 16 + 4) * 4 <=
+                                           (F8 ? NS : 1) * SM::STAGE_BYTES), "key-group combine scratch");
   int32_t* s_pages = reinterpret_cast<int32_t*>(smem + NS * SM::STAGE_BYTES);
 
   const int tid = threadIdx.x;
@@ -896,117 +896,157 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
   for (int rb = 0; rb < RB; ++rb) reg_fence(qf[rb]);
 
   // ------------------------------------------------- end of one KV head
-  // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). Waves
-  // kg > 0 publish theirs in the stage buffer every wave has just finished
-  // with (the DMA in flight targets the other buffers); wave kg = 0 of each
-  // row block folds them in and writes the head's rows.
+  // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). With
+  // key groups (KG > 1) every wave publishes, in the stage buffer all waves
+  // have just finished with (the DMA in flight targets the other buffers),
+  // its m, l and the o blocks outside its own share of d; then each wave folds
+  // its share of d (DB / KG blocks) of the KG states, in key-group order, and
+  // writes it: the fold and the stores are spread over the waves.
   auto finish_head = [&](int g, int buf) {
+    constexpr int QD = DB / KG;                  // d blocks a wave folds and writes
+    constexpr int XP = (KG - 1) * QD * 16 + 4;   // floats per published row: other shares, m, l
+    constexpr int SLOT_F = 16 * RB * XP;         // floats per published wave state
+    // position of share q among the shares wave w publishes (all but its own)
+    auto share_pos = [](int q, int w) { return q < w ? q : q - 1; };
+    float* xs = reinterpret_cast<float*>(smem + (F8 ? 0 : buf * SM::STAGE_BYTES));
     if constexpr (KG > 1) {
-      constexpr int SLOT_F = 16 * RB * XS_ROW;   // floats per published wave state
-      float* xs = reinterpret_cast<float*>(smem + (F8 ? 0 : buf * SM::STAGE_BYTES));
       block_barrier();                           // every wave is done with this buffer
-      if (kg > 0 && wave_active) {
-        float* my = xs + ((kg - 1) * RW + rw) * SLOT_F;
+      if (wave_active) {
+        float* my = xs + (kg * RW + rw) * SLOT_F;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          float* r = my + (rb * 16 + lr) * XS_ROW;
+          float* r = my + (rb * 16 + lr) * XP;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t*>(r + db * 16 + lq * 4) = o[db][rb];
+          for (int db = 0; db < DB; ++db) {
+            const int q = db / QD;
+            if (q != kg)
+              *reinterpret_cast<f32x4_t*>(r + (share_pos(q, kg) * QD + db % QD) * 16 + lq * 4) = o[db][rb];
+          }
           const float l_tot = wave_sum_across_quads(l_run[rb]);
           if (lq == 0) {
-            r[D] = m_run[rb];
-            r[D + 1] = l_tot;
+            r[XP - 4] = m_run[rb];
+            r[XP - 3] = l_tot;
           }
         }
       }
       block_barrier();                           // states published
-      if (kg == 0 && wave_active) {
+    }
+    if (!wave_active) return;
+    // The rest with this wave's share Q known at compile time, so that every
+    // o block is named by a constant index (a register array indexed at run
+    // time would be placed in scratch memory).
+    auto fold_and_write = [&](auto share_c) {
+      constexpr int Q = decltype(share_c)::value;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float l_tot = wave_sum_across_quads(l_run[rb]);
-          float m = m_run[rb];
+      for (int rb = 0; rb < RB; ++rb) {
+        float m_fin = m_run[rb];
+        float l_tot;
+        if constexpr (KG > 1) {
+          // key group 0's state first, then groups 1 .. KG - 1 folded in order
+          const float* r0 = xs + (0 * RW + rw) * SLOT_F + (rb * 16 + lr) * XP;
+          float m = r0[XP - 4], l = r0[XP - 3];
+          f32x4_t acc[QD];
+#pragma unroll
+          for (int i = 0; i < QD; ++i)
+            acc[i] = Q == 0 ? o[i][rb]
+                            : *reinterpret_cast<const f32x4_t*>(r0 + (share_pos(Q, 0) * QD + i) * 16 + lq * 4);
 #pragma unroll
           for (int k2 = 1; k2 < KG; ++k2) {
-            const float* r = xs + ((k2 - 1) * RW + rw) * SLOT_F + (rb * 16 + lr) * XS_ROW;
-            const float m2 = r[D], l2 = r[D + 1];
+            const float* r = xs + (k2 * RW + rw) * SLOT_F + (rb * 16 + lr) * XP;
+            const float m2 = r[XP - 4], l2 = r[XP - 3];
             const float mn = vmax(m, m2);
             const float mu = (mn == -INFINITY) ? 0.f : mn;
             const float a1 = __builtin_amdgcn_exp2f(m - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-              o[db][rb] = o[db][rb] * a1 + *reinterpret_cast<const f32x4_t*>(r + db * 16 + lq * 4) * a2;
-            l_tot = l_tot * a1 + l2 * a2;
+            for (int i = 0; i < QD; ++i) {
+              const f32x4_t o2 =
+                  k2 == Q ? o[Q * QD + i][rb]
+                          : *reinterpret_cast<const f32x4_t*>(r + (share_pos(Q, k2) * QD + i) * 16 + lq * 4);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(o2[j], a2, acc[i][j] * a1);
+            }
+            l = __builtin_fmaf(l2, a2, l * a1);
             m = mn;
           }
-          m_run[rb] = m;
-          // the combined sum sits in lane group 0 so the epilogue's quad sum
-          // reproduces it
-          l_run[rb] = (lq == 0) ? l_tot : 0.f;
+#pragma unroll
+          for (int i = 0; i < QD; ++i) o[Q * QD + i][rb] = acc[i];
+          m_fin = m;
+          l_tot = l;
+        } else {
+          l_tot = wave_sum_across_quads(l_run[rb]);
         }
-      }
-    }
-    if (!wave_active || (KG > 1 && kg > 0)) return;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float l_tot = wave_sum_across_quads(l_run[rb]);
-      float m_fin = m_run[rb];
-      float o_fac = 1.f;
-      if (WIN && a.direct && a.sinks && row_ok[rb]) {
-        // attention sink: one more term exp(z) of the normaliser, no value
-        const float z = a.sinks[g * a.group + row_j[rb]] * kLog2e;
-        const float mn = vmax(m_fin, z);
-        if (mn != -INFINITY) {
-          o_fac = (m_fin == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_fin - mn);
-          l_tot = l_tot * o_fac + __builtin_amdgcn_exp2f(z - mn);
-          m_fin = mn;
+        float o_fac = 1.f;
+        if (WIN && a.direct && a.sinks && row_ok[rb]) {
+          // attention sink: one more term exp(z) of the normaliser, no value
+          const float z = a.sinks[g * a.group + row_j[rb]] * kLog2e;
+          const float mn = vmax(m_fin, z);
+          if (mn != -INFINITY) {
+            o_fac = (m_fin == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_fin - mn);
+            l_tot = l_tot * o_fac + __builtin_amdgcn_exp2f(z - mn);
+            m_fin = mn;
+          }
         }
-      }
-      const bool live = l_tot > 0.f;
-      const float inv = live ? a.v_scale * o_fac / l_tot : 0.f;
-      const float lse = live ? (m_fin + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-      if (!row_ok[rb]) continue;
-      const int64_t row = (int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb];
-      if (a.direct) {
-        f32x4_t acc[DB];
+        const bool live = l_tot > 0.f;
+        const float inv = live ? a.v_scale * o_fac / l_tot : 0.f;
+        const float lse = live ? (m_fin + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+        if (!row_ok[rb]) continue;
+        const int64_t row = (int64_t)row_tok[rb] * a.hq + g * a.group + row_j[rb];
+        // one wave (share 0) writes each row's LSE
+        if (a.direct) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = o[db][rb] * inv;
+          for (int i = 0; i < QD; ++i) {
+            constexpr int db0 = Q * QD;
+            const f32x4_t acc = o[db0 + i][rb] * inv;
+            *reinterpret_cast<u32x2_t*>(a.out + row * D + (db0 + i) * 16 + lq * 4) =
+                u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+          }
+          if (Q == 0 && lq == 0 && a.lse_out) a.lse_out[row] = lse;
+        } else {
+          const int64_t e0 = (int64_t)slot * a.slot_elems + row * D;
+          if (a.part_fp32) {
+            float* dst = static_cast<float*>(a.part_o) + e0;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<u32x2_t*>(a.out + row * D + db * 16 + lq * 4) =
-              u32x2_t{pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
-        if (lq == 0 && a.lse_out) a.lse_out[row] = lse;
-      } else {
-        const int64_t e0 = (int64_t)slot * a.slot_elems + row * D;
-        if (a.part_fp32) {
-          float* dst = static_cast<float*>(a.part_o) + e0;
+            for (int i = 0; i < QD; ++i) {
+              constexpr int db0 = Q * QD;
+              const f32x4_t r = o[db0 + i][rb] * inv;
+              float* d = dst + (db0 + i) * 16 + lq * 4;
+              if (a.coherent) {
+                const u32x4_t w = __builtin_bit_cast(u32x4_t, r);
+                store_dev_u64(d, (uint64_t)w[0] | ((uint64_t)w[1] << 32));
+                store_dev_u64(d + 2, (uint64_t)w[2] | ((uint64_t)w[3] << 32));
+              } else {
+                *reinterpret_cast<f32x4_t*>(d) = r;
+              }
+            }
+          } else {
+            uint16_t* dst = static_cast<uint16_t*>(a.part_o) + e0;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const f32x4_t r = o[db][rb] * inv;
-            float* d = dst + db * 16 + lq * 4;
-            if (a.coherent) {
-              const u32x4_t w = __builtin_bit_cast(u32x4_t, r);
-              store_dev_u64(d, (uint64_t)w[0] | ((uint64_t)w[1] << 32));
-              store_dev_u64(d + 2, (uint64_t)w[2] | ((uint64_t)w[3] << 32));
-            } else {
-              *reinterpret_cast<f32x4_t*>(d) = r;
+            for (int i = 0; i < QD; ++i) {
+              constexpr int db0 = Q * QD;
+              const f32x4_t r = o[db0 + i][rb] * inv;
+              const uint32_t lo = pack_bf16x2(r[0], r[1]), hi = pack_bf16x2(r[2], r[3]);
+              uint16_t* d = dst + (db0 + i) * 16 + lq * 4;
+              if (a.coherent) store_dev_u64(d, (uint64_t)lo | ((uint64_t)hi << 32));
+              else *reinterpret_cast<u32x2_t*>(d) = u32x2_t{lo, hi};
             }
           }
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(a.part_o) + e0;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const f32x4_t r = o[db][rb] * inv;
-            const uint32_t lo = pack_bf16x2(r[0], r[1]), hi = pack_bf16x2(r[2], r[3]);
-            uint16_t* d = dst + db * 16 + lq * 4;
-            if (a.coherent) store_dev_u64(d, (uint64_t)lo | ((uint64_t)hi << 32));
-            else *reinterpret_cast<u32x2_t*>(d) = u32x2_t{lo, hi};
+          if (Q == 0 && lq == 0) {
+            float* lp = a.part_lse + (int64_t)slot * a.slot_rows + row;
+            if (a.coherent) store_dev_f32(lp, lse);
+            else *lp = lse;
           }
         }
-        if (lq == 0) {
-          float* lp = a.part_lse + (int64_t)slot * a.slot_rows + row;
-          if (a.coherent) store_dev_f32(lp, lse);
-          else *lp = lse;
-        }
+      }
+    };
+    if constexpr (KG == 1) {
+      fold_and_write(std::integral_constant<int, 0>{});
+    } else {
+      static_assert(KG == 4, "key-group shares: four waves");
+      switch (kg) {
+        case 0: fold_and_write(std::integral_constant<int, 0>{}); break;
+        case 1: fold_and_write(std::integral_constant<int, 1>{}); break;
+        case 2: fold_and_write(std::integral_constant<int, 2>{}); break;
+        default: fold_and_write(std::integral_constant<int, 3>{}); break;
       }
     }
   };
