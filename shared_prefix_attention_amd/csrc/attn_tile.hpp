@@ -225,7 +225,10 @@ struct TileSmem {
   static constexpr int TILE_BYTES = SK * D * ESZ;          // one of K or V, one stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int NS_STAGE_BYTES = NS * STAGE_BYTES;  // the page table follows
-  static constexpr int BYTES = NS_STAGE_BYTES + kMaxItemPages * 4;
+  // After the page table has been read into registers, the same bytes hold
+  // each wave's 16 rows of Q (bf16), requested by DMA (one-row-block shapes)
+  static constexpr int Q_BYTES = 4 * 16 * D * 2;
+  static constexpr int BYTES = NS_STAGE_BYTES + (kMaxItemPages * 4 > Q_BYTES ? kMaxItemPages * 4 : Q_BYTES);
 };
 
 // 16-byte chunk swizzles of a key row (rows are D*2 bytes apart), chosen
@@ -734,8 +737,16 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
         }
       }
   };
+  // One row block per wave: the first head's Q goes through LDS by DMA, like
+  // K and V, requested after the page table has been read (its bytes hold Q)
+  // and waited for by hand once the first stages are requested, so that the
+  // first stage is not held back: a register load would make the compiler
+  // wait for every LDS-DMA request issued after it (vmcnt 0) before Q's first
+  // use. Two row blocks: Q in registers.
+  constexpr bool QLDS = RB == 1;
+  static_assert(!QLDS || W == 4, "Q tiles: four waves");
   u32x4_t qf[RB][KC];
-  load_q(g0, qf);
+  if constexpr (!QLDS) load_q(g0, qf);
 
   f32x4_t o[DB][RB];
   float m_run[RB], l_run[RB];
@@ -887,13 +898,56 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
   // the stage loop).
   const int U = H * n_tiles;
   const int pro = min(NS, U);
-  for (int p = 0; p < pro; ++p) issue_next();
-  // Q was requested before these stages, so it lands before the first of
-  // them. Passing it through an asm operand here makes the compiler put its
-  // wait for Q at this point: left to itself, it waits for Q at the products
-  // inside the stage loop, i.e. for every DMA in flight, at every stage.
+  // Q tile of this wave: its 16 rows, row r at r * QROWB bytes, 16-byte chunk
+  // c at position c ^ swz(r) (the swizzle of the K tiles, read in the same
+  // pattern by the MFMA operand reads)
+  constexpr int QROWB = D * 2;
+  const uint32_t q_lds = smem_base + NS * SM::STAGE_BYTES + wave * 16 * QROWB;
+  if constexpr (QLDS) {
+    block_barrier();   // every wave has read the page table, whose bytes the Q tiles reuse
+    if (wave_active) {
+      constexpr int QCH = QROWB / 16;          // 16-byte chunks per row
+      constexpr int QRPB = 64 / QCH;           // rows per 1 KB DMA block
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) reg_fence(qf[rb]);
+      for (int i = 0; i < 16 / QRPB; ++i) {
+        const int r = i * QRPB + lane / QCH;   // row of the tile this lane's chunk belongs to
+        const int c = lane % QCH;              // its chunk position in LDS
+        // lane r holds row r's token and head-in-group; rows past the item's
+        // last take the wave's first row (never used)
+        const int src = wrow0 + r < row_end ? r : 0;
+        const int tok = __shfl(row_tok[0], src);
+        const int j = __shfl(row_j[0], src);
+        lds_dma16(a.q + ((int64_t)tok * a.hq + g0 * a.group + j) * D + (c ^ chunk_swz<D>(r)) * 8,
+                  q_lds + i * 1024);
+      }
+    }
+  }
+  for (int p = 0; p < pro; ++p) issue_next();
+  if constexpr (QLDS) {
+    if (wave_active) {
+      // Q's requests precede the stages': they are done once at most the
+      // stages' requests are outstanding
+      if (pro >= 4) wait_vmcnt<4 * OPS>();
+      else if (pro == 3) wait_vmcnt<3 * OPS>();
+      else if (pro == 2) wait_vmcnt<2 * OPS>();
+      else if (pro == 1) wait_vmcnt<OPS>();
+      else wait_vmcnt<0>();
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        // the k-slot order of load_q
+        const int ch = F8 ? 2 * (lq + 4 * (kc >> 1)) + (kc & 1) : kc * 4 + lq;
+        qf[0][kc] = lds_read_b128<0>(q_lds + lr * QROWB + ((ch ^ chunk_swz<D>(lr)) * 16));
+      }
+      lds_wait_regs(qf[0]);
+    }
+  } else {
+    // Q was requested before these stages, so it lands before the first of
+    // them. Passing it through an asm operand here makes the compiler put its
+    // wait for Q at this point: left to itself, it waits for Q at the products
+    // inside the stage loop, i.e. for every DMA in flight, at every stage.
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) reg_fence(qf[rb]);
+  }
 
   // ------------------------------------------------- end of one KV head
   // Per wave and row: m (scaled, log2 domain), l and o (unnormalised). With
