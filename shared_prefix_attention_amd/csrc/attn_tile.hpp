@@ -1369,14 +1369,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
 
 // 128-row items ask for two work-groups per CU explicitly: left alone, the
 // compiler gives them a few more registers than two allow.
-template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool TREE>
+template <int D, int RB, int RW, int KG, int NS, int SK, bool MH, bool F8, bool TREE, bool WIN = true, int PM = -1>
 __global__ __launch_bounds__(64 * RW * KG, RB == 2 ? 2 : 1) void attn_tile_kernel(const TileArgs a,
                                                                                   const GroupTableArg<TREE> gt,
                                                                                   const ReqOrder ro,
                                                                                   const MergeTailArgs mt) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TileSmem<D, NS, SK, F8 ? 1 : 2>::BYTES];
   ItemEnd end;
-  attn_item<D, RB, RW, KG, NS, SK, MH, F8, true>(a, gt, ro, blockIdx.x, smem, end);
+  attn_item<D, RB, RW, KG, NS, SK, MH, F8, WIN, PM>(a, gt, ro, blockIdx.x, smem, end);
   if (mt.counters) merge_tail<D, 64 * RW * KG>(mt, end, reinterpret_cast<int32_t*>(smem));
 }
 

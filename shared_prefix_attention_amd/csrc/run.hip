@@ -89,12 +89,19 @@ template <int D, int RB, int RW, int KG, int NS, bool F8>
 void launch_tile(const TileArgs& args, const GroupTable& gt, const ReqOrder& ro, const MergeTailArgs& mt, int grid,
                  hipStream_t s, int kind) {
   constexpr bool MH = (KG > 1) && !F8;
+  // Per-request launches with no sliding window and no attention sinks (the
+  // non-cascade path's usual case) take a variant without that code and
+  // with the role fixed, which holds fewer scalar registers through the
+  // stage loop.
   if (gt.n > 0)
     launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, MH, F8, true>, dim3(grid), dim3(64 * RW * KG), s, args, gt,
            ro, mt);
-  else
+  else if (args.window > 0 || args.sinks || args.prefix_mode != 0)
     launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, MH, F8, false>, dim3(grid), dim3(64 * RW * KG), s, args,
            NoGroupTable{}, ro, mt);
+  else
+    launch(kind, attn_tile_kernel<D, RB, RW, KG, NS, 64, MH, F8, false, false, 0>, dim3(grid), dim3(64 * RW * KG),
+           s, args, NoGroupTable{}, ro, mt);
 }
 
 // bf16 caches: 2 or 4 stages of 64 keys; fp8 caches (head_dim 128 only):
