@@ -609,11 +609,14 @@ __device__ __forceinline__ void attn_item(const TileArgs& a, const GT& gt, const
         key_begin = gt.key_begin[grp];
       }
     }
-    const int kv_items = a.hkv * splits;
-    mt = local / kv_items;
-    const int kvi = local - mt * kv_items;
-    g0 = kvi / splits;
-    c = kvi - g0 * splits;
+    // The KV head is the fastest-varying index: work-groups are dealt to the
+    // XCDs in turn, so with 8 KV heads all items of one head (every row tile
+    // and split: they share its K/V tiles and its Q rows) run on one XCD and
+    // meet in its L2.
+    g0 = local % a.hkv;
+    const int rest = local / a.hkv;
+    c = rest % splits;
+    mt = rest / splits;
     key_begin += c * split_tokens;
     causal = false;
     bt_row = a.bt + (int64_t)req * a.bt_stride;
