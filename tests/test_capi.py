@@ -342,19 +342,18 @@ def test_auto_takes_the_measured_faster_path():
 # (name, N, P, suffix range, query range, cascade?). 32 / 8 heads,
 # head_dim 128, bf16:
 SWEEP_CLEAR = [
-    ("decode_n2_p256_s16", 2, 256, (16, 16), (1, 1), 0),          # 11.9 / 10.8
-    ("decode_n2_p4096_s16", 2, 4096, (16, 16), (1, 1), 1),        # 14.2 / 18.5
-    ("decode_n4_p1024_s16", 4, 1024, (16, 16), (1, 1), 1),        # 15.0 / 15.7
-    ("decode_n4_p4096_s512", 4, 4096, (512, 512), (1, 1), 1),     # 15.6 / 23.6
-    ("decode_n8_p256_s16", 8, 256, (16, 16), (1, 1), 0),          # 12.2 / 10.0
-    ("decode_n8_p1024_s16", 8, 1024, (16, 16), (1, 1), 1),        # 12.0 / 17.2
-    ("decode_n16_p4096_s16", 16, 4096, (16, 16), (1, 1), 1),      # 16.0 / 27.4
-    ("decode_n64_p256_s16", 64, 256, (16, 16), (1, 1), 0),        # 14.6 / 12.5
-    ("decode_n64_p1024_s512", 64, 1024, (512, 512), (1, 1), 1),   # 36.8 / 41.8
-    ("decode_n256_p1024_s16", 256, 1024, (16, 16), (1, 1), 1),    # 30.9 / 72.1
-    ("prefill_n8_p2048", 8, 2048, (64, 512), (1, 64), 1),         # 32.4 / 43.9
-    ("prefill_n32_p256", 32, 256, (64, 512), (1, 64), 0),         # 45.9 / 41.3
-    ("prefill_n128_p256", 128, 256, (64, 512), (1, 64), 0),       # 153.7 / 135.9
+    ("decode_n2_p4096_s16", 2, 4096, (16, 16), (1, 1), 1),        # 14.4 / 18.5
+    ("decode_n4_p1024_s16", 4, 1024, (16, 16), (1, 1), 1),        # 15.0 / 15.8
+    ("decode_n4_p4096_s512", 4, 4096, (512, 512), (1, 1), 1),     # 15.4 / 23.6
+    ("decode_n8_p256_s16", 8, 256, (16, 16), (1, 1), 0),          # 12.2 / 10.5
+    ("decode_n8_p1024_s16", 8, 1024, (16, 16), (1, 1), 1),        # 15.2 / 17.2
+    ("decode_n16_p4096_s16", 16, 4096, (16, 16), (1, 1), 1),      # 15.5 / 27.6
+    ("decode_n64_p256_s16", 64, 256, (16, 16), (1, 1), 0),        # 15.2 / 15.0
+    ("decode_n64_p1024_s512", 64, 1024, (512, 512), (1, 1), 1),   # 37.4 / 41.8
+    ("decode_n256_p1024_s16", 256, 1024, (16, 16), (1, 1), 1),    # 31.0 / 71.3
+    ("prefill_n8_p2048", 8, 2048, (64, 512), (1, 64), 1),         # 32.1 / 43.5
+    ("prefill_n32_p256", 32, 256, (64, 512), (1, 64), 0),         # 45.9 / 41.2
+    ("prefill_n128_p256", 128, 256, (64, 512), (1, 64), 0),       # 152.7 / 135.7
 ]
 
 # The wider families (decode, one query token): 64 / 8 heads; head_dim 64;
@@ -362,17 +361,17 @@ SWEEP_CLEAR = [
 # requests, 2048 for the odd ones) after the prefix. (name, family, N, P, S,
 # cascade?)
 SWEEP_CLEAR_WIDE = [
-    ("h64_n4_p1024_s512", "h64", 4, 1024, 512, 1),       # 14.5 / 17.5
-    ("h64_n16_p8192_s16", "h64", 16, 8192, 16, 1),       # 21.6 / 43.5
-    ("h64_n64_p1024_s16", "h64", 64, 1024, 16, 1),       # 20.6 / 22.7
-    ("h64_n256_p8192_s512", "h64", 256, 8192, 512, 1),   # 157.1 / 482.6
-    ("d64_n16_p4096_s16", "d64", 16, 4096, 16, 1),       # 15.5 / 20.7
-    ("d64_n64_p4096_s512", "d64", 64, 4096, 512, 1),     # 25.9 / 55.1
-    ("fp8_n16_p4096_s512", "fp8", 16, 4096, 512, 1),     # 20.2 / 26.2
-    ("fp8_n64_p1024_s16", "fp8", 64, 1024, 16, 1),       # 18.1 / 19.7
-    ("fp8_n64_p4096_s16", "fp8", 64, 4096, 16, 1),       # 22.3 / 55.7
-    ("docs_n32_p256_s16", "docs", 32, 256, 16, 1),       # 21.6 / 28.8
-    ("docs_n32_p1024_s256", "docs", 32, 1024, 256, 1),   # 26.2 / 36.5
+    ("h64_n4_p1024_s512", "h64", 4, 1024, 512, 1),       # 15.0 / 17.3
+    ("h64_n16_p8192_s16", "h64", 16, 8192, 16, 1),       # 21.6 / 44.4
+    ("h64_n64_p1024_s16", "h64", 64, 1024, 16, 1),       # 20.3 / 22.7
+    ("h64_n256_p8192_s512", "h64", 256, 8192, 512, 1),   # 153.1 / 480.8
+    ("d64_n16_p4096_s16", "d64", 16, 4096, 16, 1),       # 15.4 / 20.4
+    ("d64_n64_p4096_s512", "d64", 64, 4096, 512, 1),     # 26.8 / 55.1
+    ("fp8_n16_p4096_s512", "fp8", 16, 4096, 512, 1),     # 19.9 / 26.5
+    ("fp8_n64_p1024_s16", "fp8", 64, 1024, 16, 1),       # 18.5 / 19.7
+    ("fp8_n64_p4096_s16", "fp8", 64, 4096, 16, 1),       # 22.0 / 56.1
+    ("docs_n32_p256_s16", "docs", 32, 256, 16, 1),       # 21.2 / 28.6
+    ("docs_n32_p1024_s256", "docs", 32, 1024, 256, 1),   # 25.8 / 36.6
 ]
 
 
