@@ -488,6 +488,10 @@ def main():
         cpu = cpu_baseline(b, kv_bytes)
 
     gbs = kv_bytes / (ms * 1e-3) / 1e9
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count, "memory_gib": round(props.total_memory / 2**30, 1),
+              "hip": torch.version.hip}
     line = {
         "metric": "cascade attn us/step + effective KV GB/s (N=64,P=4096,S=128), % of HBM roofline",
         "value": round(gbs, 2),
@@ -504,6 +508,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "device": device,
         "config": {"workload": args.workload, "num_reqs": w.num_reqs, "prefix": w.prefix,
                    "suffix": list(w.suffix), "q_len": list(w.q_len), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
