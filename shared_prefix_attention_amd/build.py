@@ -94,20 +94,28 @@ def build(verbose: bool = True) -> str:
     usage = []
     for src in HIP_SOURCES:
         obj = os.path.join(objdir, src + ".o")
+        # the compiler's own gfx950 assembly of the same source (compiled
+        # alongside the object): every inline-asm LDS read is waited for
+        # before any use of its registers
+        asm_path = os.path.join(objdir, src + ".s")
+        asm_cmd = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC,
+                   os.path.join(CSRC, src), "-o", asm_path]
+        print("+", " ".join(asm_cmd), flush=True)
+        asm_proc = subprocess.Popen(asm_cmd)
         cmd = [hipcc, *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         print("+", " ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True)
+        finally:
+            asm_rc = asm_proc.wait()
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
             raise subprocess.CalledProcessError(r.returncode, cmd)
+        if asm_rc != 0:
+            raise subprocess.CalledProcessError(asm_rc, asm_cmd)
         usage += check_resource_usage(r.stderr)
         objs.append(obj)
-        # the compiler's own gfx950 assembly of the same source: every
-        # inline-asm LDS read is waited for before any use of its registers
-        asm_path = os.path.join(objdir, src + ".s")
-        _run([hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC,
-              os.path.join(CSRC, src), "-o", asm_path])
         from shared_prefix_attention_amd import lds_wait_check
         nfun, nreads, problems = lds_wait_check.check(open(asm_path).read())
         if problems:
