@@ -176,8 +176,9 @@ def summarize_pmc(fetch_dir, write_dir, workload, steps):
             rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
         return rows
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "kernels": {},
-           "command": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -- python3 bench.py --traffic-probe "
-                      f"--workload {workload} --steps {steps}; same with WRITE_SIZE into {write_dir}"}
+           "command": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o p -- python3 -u bench.py --traffic-probe "
+                      f"--workload {workload} --steps {steps}; the same with WRITE_SIZE into {write_dir}; then "
+                      f"python3 bench.py --summarize-pmc {fetch_dir} {write_dir} --workload {workload} --steps {steps}"}
     for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         rows = read(d, counter)
         copy = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
